@@ -1,0 +1,167 @@
+/*
+ * pkv.h -- C ABI of the MI355X (gfx950) paged-KV split-KV decode attention
+ * library (libpkv.so).
+ *
+ * The operation (AstrAI commit d565d44, "csrc/kernels/attn_paged_decode.cu",
+ * commit notes on the scalar and MMA split-KV paged decode kernels and their
+ * bindings): for every sequence b, query token i < q_len and query head h,
+ *
+ *     out[b,i,h,:] = sum_j softmax_j(s_j) * V[b, j, g(h), :]
+ *     s_j          = scale * <q[b,i,h,:], K[b, j, g(h), :]> + mask[b,(i,)j]
+ *
+ * over the keys j the row may see: j < kv_lens[b], and j <= c + i when a
+ * causal offset c >= 0 applies ("unified causal_offset: -1 = off, >= 0 = first
+ * Q position").  K and V live in fixed-size physical pages; logical key j of
+ * sequence b is slot j % page_size of physical page block_table[b, j /
+ * page_size].  GQA: query head h reads kv head g(h) = h / (Hq / Hkv).  A row
+ * that sees no finite score gets 0.  The work is split along the keys
+ * ("split-KV"); each split leaves a normalised partial output and its
+ * (max, sum) pair, merged by one log-sum-exp combine kernel.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are caller-owned DEVICE memory of the current HIP
+ *    device, read or written asynchronously on `stream`.  The library keeps
+ *    no pointer after a call returns.
+ *  - No entry point allocates, frees, copies, sets memory or synchronises;
+ *    pkv_paged_decode and pkv_combine only launch kernels on `stream`, so
+ *    they may be captured into a hipGraph.  Kernel arguments depend only on
+ *    host values, so device data (kv_lens, block_table, q, K/V, mask) may
+ *    change between graph replays.
+ *  - Every host-side check runs before any HIP call; a failed check returns
+ *    its status with nothing enqueued.  There are no exceptions, aborts or
+ *    prints.  The library is stateless apart from a per-device cache of the
+ *    compute-unit count, and is thread-safe.
+ *  - Caller contract (not checkable without a device sync): block-table
+ *    entries for the pages that hold keys j < kv_lens[b] are in
+ *    [0, num_pages); 0 <= kv_lens[b] <= max_kv_len; causal_offsets[b] >= -1.
+ *    Entries past ceil(kv_lens[b] / page_size) are never read, nor are page
+ *    slots at or past kv_lens[b].
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (distinct per failure kind, in the spirit of the structured
+ * unsupported-feature errors in the ejkernel v0.0.55 release notes and the
+ * binding validation in the AstrAI commit notes). */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, max_kv_len too big, bad stride */
+  PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS */
+  PKV_ERR_WORKSPACE = 4,   /* o_part / ml_part missing or smaller than pkv_workspace_bytes */
+  PKV_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
+  PKV_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_DEVICE = 7       /* querying the current device failed */
+};
+
+#define PKV_MAX_SPLITS 256
+
+/* Problem description (host memory; read during the call only).
+ * Sizes follow the statement of the paged decode problem: q[B, q_len, Hq, D],
+ * k_cache / v_cache[num_pages, page_size, Hkv, D], block_table[B,
+ * max_pages_per_seq], kv_lens[B]; the split count follows ejkernel's
+ * PageAttentionConfig (operations.configs docs: num_splits, 0 = auto). */
+typedef struct pkv_problem {
+  int32_t batch;             /* B >= 0 (0: nothing to do) */
+  int32_t q_len;             /* query tokens per sequence, >= 1 */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;          /* D in {32, 64, 128, 256} */
+  int32_t page_size;         /* power of two in [1, 4096] */
+  int32_t num_pages;         /* physical pages in the pool, >= 0 */
+  int32_t max_pages_per_seq; /* block_table row stride, >= 1 */
+  int32_t max_kv_len;        /* host-known bound on kv_lens; 0 => max_pages_per_seq * page_size */
+  float scale;               /* finite score scale, usually 1/sqrt(D) */
+  int32_t causal_offset;     /* -1 off; >= 0 position of query token 0 (all sequences) */
+  int32_t num_splits;        /* 0 heuristic; 1..PKV_MAX_SPLITS forced */
+  int64_t mask_stride_b;     /* mask element stride between sequences (>= 0) */
+  int64_t mask_stride_q;     /* mask element stride between query tokens; 0 => 2D [B, kv] mask */
+} pkv_problem;
+
+/* Number of splits pkv_paged_decode uses for this problem on a device with
+ * `num_cus` compute units (num_cus <= 0: the current device's count).  A
+ * forced p->num_splits is returned unchanged.  Pure host arithmetic once the
+ * CU count is known. */
+int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out);
+
+/* Workspace pkv_paged_decode needs with `splits` splits:
+ *   o_part : fp32 [B, q_len, Hq, splits, D]      (normalised partial outputs)
+ *   ml_part: fp32 [B, q_len, Hq, splits, 2]      (m, l) per partial,
+ * m = max scaled+masked score in natural-log units, l = sum exp(s - m).
+ * Both are 0 when splits == 1 (the split kernel then writes `out` itself). */
+int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
+                        size_t *ml_part_bytes);
+
+/* Paged decode attention.
+ *   q            bf16 [B, q_len, Hq, D], contiguous, 16-byte aligned
+ *   k_cache      bf16 [num_pages, page_size, Hkv, D], contiguous, 16-byte aligned
+ *   v_cache      bf16 [num_pages, page_size, Hkv, D], contiguous, 16-byte aligned
+ *   block_table  int32 [B, max_pages_per_seq]
+ *   kv_lens      int32 [B]
+ *   causal_offsets  NULL, or int32 [B]: per-sequence causal offset that
+ *                replaces p->causal_offset (-1 turns causality off for b)
+ *   mask         NULL, or fp32 additive mask; element (b, i, j) at
+ *                mask[b * mask_stride_b + i * mask_stride_q + j]; -inf removes
+ *                a key; entries at j >= kv_lens[b] are never read
+ *   o_part, ml_part  workspace of at least pkv_workspace_bytes for the split
+ *                count in use (16- and 8-byte aligned); may be NULL when that
+ *                count is 1.  Contents on return are the split partials.
+ *   out_bf16     bf16 [B, q_len, Hq, D], 16-byte aligned; round-to-nearest-even
+ *                of the fp32 result
+ *   out_f32      NULL, or fp32 [B, q_len, Hq, D] (the value before rounding)
+ * Returns PKV_OK after enqueueing one split kernel (plus the combine kernel
+ * when more than one split is used) on `stream`. */
+int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
+                     const void *v_cache, const int32_t *block_table,
+                     const int32_t *kv_lens, const int32_t *causal_offsets,
+                     const float *mask, float *o_part, size_t o_part_bytes,
+                     float *ml_part, size_t ml_part_bytes, void *out_bf16,
+                     float *out_f32, hipStream_t stream);
+
+/* The split step alone: the same split kernel as pkv_paged_decode, always
+ * writing the split partials and never launching the combine.  For callers
+ * that merge partials themselves, e.g. after gathering the partials of key
+ * shards held by several devices, with pkv_combine.  o_part (fp32 [B, q_len,
+ * Hq, splits, D], 16-byte aligned) and ml_part (fp32 [B, q_len, Hq, splits,
+ * 2], 8-byte aligned) are required for every split count, including 1: that
+ * is pkv_workspace_bytes for splits >= 2, and rows * D * 4 / rows * 8 bytes
+ * for one split.  Other arguments as for pkv_paged_decode. */
+int pkv_paged_decode_partials(const pkv_problem *p, const void *q,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table,
+                              const int32_t *kv_lens,
+                              const int32_t *causal_offsets, const float *mask,
+                              float *o_part, size_t o_part_bytes,
+                              float *ml_part, size_t ml_part_bytes,
+                              hipStream_t stream);
+
+/* The combine step alone: merges `splits` partials per row with the
+ * log-sum-exp rule  M = max_{l_s>0} m_s,  w_s = l_s exp(m_s - M),
+ * out = sum_s w_s o_s / sum_s w_s  (0 when no partial has l_s > 0).
+ *   o_part   fp32 [rows, splits, head_dim]   (16-byte aligned)
+ *   ml_part  fp32 [rows, splits, 2]          (m, l), 8-byte aligned
+ *   out_bf16 bf16 [rows, head_dim] (16-byte aligned), out_f32 NULL or fp32 [rows, head_dim]
+ * head_dim in {32, 64, 128, 256}; 1 <= splits <= PKV_MAX_SPLITS; rows >= 0. */
+int pkv_combine(int64_t rows, int splits, int head_dim, const float *o_part,
+                const float *ml_part, void *out_bf16, float *out_f32,
+                hipStream_t stream);
+
+/* Compute units of the current device (queried once per device, then cached). */
+int pkv_device_cus(int *num_cus);
+
+/* Static text for a status code. */
+const char *pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

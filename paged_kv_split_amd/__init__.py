@@ -1,0 +1,277 @@
+"""Python binding of libpkv.so, the MI355X paged-KV split-KV decode attention
+library.  Argument marshalling only: every step of the computation runs in
+the library's HIP kernels; PyTorch supplies device memory and streams.
+
+The C entry points are declared in include/pkv.h; the functions here carry
+the same names without the ``pkv_`` prefix.  Loading fails loudly when the
+library has not been built (``python -m paged_kv_split_amd.build``); there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_NULL = 1
+PKV_ERR_SHAPE = 2
+PKV_ERR_UNSUPPORTED = 3
+PKV_ERR_WORKSPACE = 4
+PKV_ERR_ALIGN = 5
+PKV_ERR_LAUNCH = 6
+PKV_ERR_DEVICE = 7
+PKV_MAX_SPLITS = 256
+
+EXPORTED = ("pkv_num_splits", "pkv_workspace_bytes", "pkv_paged_decode", "pkv_paged_decode_partials",
+            "pkv_combine", "pkv_device_cus", "pkv_status_string")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``pkv_problem`` (include/pkv.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("causal_offset", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("mask_stride_b", ctypes.c_int64),
+        ("mask_stride_q", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpkv.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_split_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(Problem)
+        L.pkv_num_splits.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.pkv_workspace_bytes.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.pkv_paged_decode.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                       ctypes.c_size_t, P, P, P]
+        L.pkv_paged_decode_partials.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                                ctypes.c_size_t, P]
+        L.pkv_combine.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+        L.pkv_device_cus.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        L.pkv_status_string.argtypes = [ctypes.c_int]
+        L.pkv_status_string.restype = ctypes.c_char_p
+        for name in ("pkv_num_splits", "pkv_workspace_bytes", "pkv_paged_decode",
+                     "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def make_problem(*, batch: int, q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 page_size: int, num_pages: int, max_pages_per_seq: int, max_kv_len: int = 0,
+                 scale: float = 1.0, causal_offset: int = -1, num_splits: int = 0,
+                 mask_stride_b: int = 0, mask_stride_q: int = 0) -> Problem:
+    return Problem(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                   max_pages_per_seq, max_kv_len, scale, causal_offset, num_splits,
+                   mask_stride_b, mask_stride_q)
+
+
+def device_cus() -> int:
+    n = ctypes.c_int(0)
+    _check(lib().pkv_device_cus(ctypes.byref(n)), "pkv_device_cus")
+    return n.value
+
+
+def num_splits(problem: Problem, num_cus: int = 0) -> int:
+    s = ctypes.c_int(0)
+    _check(lib().pkv_num_splits(ctypes.byref(problem), int(num_cus), ctypes.byref(s)), "pkv_num_splits")
+    return s.value
+
+
+def workspace_bytes(problem: Problem, splits: int) -> tuple[int, int]:
+    o = ctypes.c_size_t(0)
+    ml = ctypes.c_size_t(0)
+    _check(lib().pkv_workspace_bytes(ctypes.byref(problem), int(splits), ctypes.byref(o), ctypes.byref(ml)),
+           "pkv_workspace_bytes")
+    return o.value, ml.value
+
+
+def paged_decode_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block_table: int,
+                     kv_lens: int, causal_offsets: int, mask: int, o_part: int, o_part_bytes: int,
+                     ml_part: int, ml_part_bytes: int, out_bf16: int, out_f32: int, stream: int) -> int:
+    """pkv_paged_decode on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_paged_decode(ctypes.byref(problem), q or None, k_cache or None, v_cache or None,
+                                  block_table or None, kv_lens or None, causal_offsets or None,
+                                  mask or None, o_part or None, o_part_bytes, ml_part or None,
+                                  ml_part_bytes, out_bf16 or None, out_f32 or None, stream or None)
+
+
+def paged_decode_partials_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block_table: int,
+                              kv_lens: int, causal_offsets: int, mask: int, o_part: int,
+                              o_part_bytes: int, ml_part: int, ml_part_bytes: int, stream: int) -> int:
+    """pkv_paged_decode_partials on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_paged_decode_partials(ctypes.byref(problem), q or None, k_cache or None,
+                                           v_cache or None, block_table or None, kv_lens or None,
+                                           causal_offsets or None, mask or None, o_part or None,
+                                           o_part_bytes, ml_part or None, ml_part_bytes, stream or None)
+
+
+def combine_raw(rows: int, splits: int, head_dim: int, o_part: int, ml_part: int, out_bf16: int,
+                out_f32: int, stream: int) -> int:
+    """pkv_combine on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_combine(int(rows), int(splits), int(head_dim), o_part or None, ml_part or None,
+                             out_bf16 or None, out_f32 or None, stream or None)
+
+
+# ---- torch-facing helpers (device memory and streams only) ----------------
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _require(t, name, dtype, ndim=None):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def problem_for(q, k_cache, block_table, *, scale: float, causal_offset: int = -1, mask=None,
+                num_splits: int = 0, max_kv_len: int = 0) -> Problem:
+    B, q_len, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    msb = msq = 0
+    if mask is not None:
+        if mask.dim() == 2:
+            msb = mask.stride(0)
+        elif mask.dim() == 3:
+            msb, msq = mask.stride(0), mask.stride(1)
+        else:
+            raise ValueError("mask must be [B, kv] or [B, q_len, kv]")
+    return make_problem(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                        page_size=P, num_pages=num_pages, max_pages_per_seq=block_table.shape[1],
+                        max_kv_len=max_kv_len, scale=scale, causal_offset=causal_offset,
+                        num_splits=num_splits, mask_stride_b=msb, mask_stride_q=msq)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
+                 causal_offset: int = -1, causal_offsets=None, mask=None, num_splits: int = 0,
+                 max_kv_len: int = 0, out=None, out_f32=None, o_part=None, ml_part=None,
+                 stream=None, problem: Optional[Problem] = None):
+    """Paged decode on torch device tensors.  Returns ``out`` (bf16).
+
+    q bf16 [B, q_len, Hq, D]; k_cache, v_cache bf16 [num_pages, page_size,
+    Hkv, D]; block_table int32 [B, max_pages]; kv_lens int32 [B];
+    causal_offsets optional int32 [B]; mask optional fp32 [B, kv] or
+    [B, q_len, kv] (last dim contiguous).  ``out``/``out_f32``/``o_part``/
+    ``ml_part`` may be passed preallocated (required for graph capture);
+    missing ones are allocated here, outside the library call.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(kv_lens, "kv_lens", torch.int32, 1)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if causal_offsets is not None:
+        _require(causal_offsets, "causal_offsets", torch.int32, 1)
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_cuda or mask.stride(-1) != 1:
+            raise ValueError("mask must be a device float32 tensor with a contiguous last dim")
+    p = problem if problem is not None else problem_for(q, k_cache, block_table, scale=scale,
+                                                         causal_offset=causal_offset, mask=mask,
+                                                         num_splits=num_splits, max_kv_len=max_kv_len)
+    S = num_splits_for(p)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if S > 1 and (o_part is None or ml_part is None):
+        ob, mb = workspace_bytes(p, S)
+        o_part = torch.empty(ob // 4, dtype=torch.float32, device=q.device)
+        ml_part = torch.empty(mb // 4, dtype=torch.float32, device=q.device)
+    st = paged_decode_raw(p, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(kv_lens),
+                          _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
+                          0 if o_part is None else o_part.numel() * o_part.element_size(),
+                          _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
+                          _ptr(out), _ptr(out_f32), _stream_handle(stream))
+    _check(st, "pkv_paged_decode")
+    return out
+
+
+def paged_decode_partials(q, k_cache, v_cache, block_table, kv_lens, *, o_part, ml_part,
+                          problem: Problem, causal_offsets=None, mask=None, stream=None):
+    """Split step only: writes o_part [B, q_len, Hq, S, D] and ml_part
+    [B, q_len, Hq, S, 2] (fp32, preallocated) for the problem's split count."""
+    st = paged_decode_partials_raw(problem, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(kv_lens), _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
+                                   o_part.numel() * o_part.element_size(), _ptr(ml_part),
+                                   ml_part.numel() * ml_part.element_size(), _stream_handle(stream))
+    _check(st, "pkv_paged_decode_partials")
+
+
+def partials_bytes(problem: Problem, splits: int) -> tuple[int, int]:
+    """o_part / ml_part bytes pkv_paged_decode_partials needs (any split count)."""
+    rows = problem.batch * problem.q_len * problem.num_q_heads
+    return rows * splits * problem.head_dim * 4, rows * splits * 8
+
+
+def num_splits_for(problem: Problem) -> int:
+    """Split count the library will use (forced, or the heuristic on this device)."""
+    if problem.num_splits > 0:
+        return problem.num_splits
+    return num_splits(problem, 0)
+
+
+def combine(o_part, ml_part, *, rows: int, splits: int, head_dim: int, out=None, out_f32=None,
+            stream=None):
+    """pkv_combine on torch tensors: o_part fp32 [rows, S, D], ml_part fp32 [rows, S, 2]."""
+    import torch
+    _require(o_part, "o_part", torch.float32)
+    _require(ml_part, "ml_part", torch.float32)
+    if out is None:
+        out = torch.empty((rows, head_dim), dtype=torch.bfloat16, device=o_part.device)
+    _check(combine_raw(rows, splits, head_dim, _ptr(o_part), _ptr(ml_part), _ptr(out), _ptr(out_f32),
+                       _stream_handle(stream)), "pkv_combine")
+    return out

@@ -1,0 +1,318 @@
+// pkv_host.cpp -- host side of the C ABI: argument checks, split heuristic,
+// workspace sizing and launch of the split and combine kernels.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing; the HIP calls made are kernel launches on the caller's stream,
+// hipGetLastError after them, and (once per device, for the split heuristic)
+// a compute-unit query.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not queried yet
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks common to every entry point taking a pkv_problem.
+int check_problem(const pkv_problem *p) {
+  if (!p) return PKV_ERR_NULL;
+  if (p->batch < 0 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return PKV_ERR_SHAPE;
+  if (p->num_q_heads % p->num_kv_heads) return PKV_ERR_SHAPE;
+  if (!supported_dim(p->head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (!is_pow2(p->page_size) || p->page_size > 4096) return PKV_ERR_UNSUPPORTED;
+  if (p->num_pages < 0 || p->max_pages_per_seq < 1) return PKV_ERR_SHAPE;
+  if (p->max_kv_len < 0) return PKV_ERR_SHAPE;
+  const int64_t cap = (int64_t)p->max_pages_per_seq * p->page_size;
+  if (cap > INT32_MAX) return PKV_ERR_SHAPE;
+  if ((int64_t)p->max_kv_len > cap) return PKV_ERR_SHAPE;
+  if (!isfinite(p->scale)) return PKV_ERR_SHAPE;
+  if (p->causal_offset < -1) return PKV_ERR_SHAPE;
+  if (p->num_splits < 0) return PKV_ERR_SHAPE;
+  if (p->num_splits > PKV_MAX_SPLITS) return PKV_ERR_UNSUPPORTED;
+  if (p->mask_stride_b < 0 || p->mask_stride_q < 0) return PKV_ERR_SHAPE;
+  // rows * D and pool sizes must fit the 64-bit element arithmetic used on device
+  const int64_t rows = (int64_t)p->batch * p->q_len * p->num_q_heads;
+  if (rows > (int64_t)1 << 40) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+// Host-known bound on the keys of any sequence.
+int max_len_of(const pkv_problem *p) {
+  return p->max_kv_len > 0 ? p->max_kv_len : p->max_pages_per_seq * p->page_size;
+}
+
+int query_cus(int *out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PKV_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *out = c; return PKV_OK; }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return PKV_ERR_DEVICE;
+  if (dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+  *out = c;
+  return PKV_OK;
+}
+
+// Split heuristic (keys only along the sequence axis, in the spirit of the
+// pages' compute_num_splits and ejkernel's num_splits = 0 "auto"): use one
+// split when the (sequence, kv-head, row-block) units already give every CU
+// several workgroups; otherwise split each sequence so the grid reaches about
+// kTargetPerCu workgroups per CU, never below kMinTilesPerWave tiles per wave.
+constexpr int kTargetPerCu = 4;
+constexpr int kMinTilesPerWave = 2;
+
+int heuristic_splits(const pkv_problem *p, int cus) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  const int rp = pkv::rows_per_block(R);
+  const int64_t nrb = ceil_div(R, rp);
+  const int64_t units = (int64_t)p->batch * p->num_kv_heads * nrb;
+  if (units <= 0) return 1;
+  const int64_t target = (int64_t)cus * kTargetPerCu;
+  if (units >= target) return 1;
+  const int T = pkv::tile_keys(p->head_dim);
+  const int64_t min_keys = (int64_t)T * pkv::kWavesPerBlock * kMinTilesPerWave;
+  const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
+  int64_t s = ceil_div(target, units);
+  if (s > max_by_len) s = max_by_len;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid problem shape or stride";
+    case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, page_size or split count";
+    case PKV_ERR_WORKSPACE: return "split workspace missing or too small";
+    case PKV_ERR_ALIGN: return "pointer misaligned";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_DEVICE: return "device query failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_device_cus(int *num_cus) {
+  if (!num_cus) return PKV_ERR_NULL;
+  return query_cus(num_cus);
+}
+
+int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out) {
+  if (!splits_out) return PKV_ERR_NULL;
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->num_splits > 0) { *splits_out = p->num_splits; return PKV_OK; }
+  if (num_cus <= 0) {
+    rc = query_cus(&num_cus);
+    if (rc) return rc;
+  }
+  *splits_out = heuristic_splits(p, num_cus);
+  return PKV_OK;
+}
+
+int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
+                        size_t *ml_part_bytes) {
+  if (!o_part_bytes || !ml_part_bytes) return PKV_ERR_NULL;
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (splits < 1) return PKV_ERR_SHAPE;
+  if (splits > PKV_MAX_SPLITS) return PKV_ERR_UNSUPPORTED;
+  if (splits == 1) { *o_part_bytes = 0; *ml_part_bytes = 0; return PKV_OK; }
+  const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
+  *o_part_bytes = rows * (size_t)splits * (size_t)p->head_dim * sizeof(float);
+  *ml_part_bytes = rows * (size_t)splits * 2 * sizeof(float);
+  return PKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks and launch plan shared by pkv_paged_decode (partials_only = false)
+// and pkv_paged_decode_partials (true).  Returns a status; on PKV_OK `a`
+// holds the split-kernel arguments (a->S is the split count).
+int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_table, const int32_t *kv_lens, const int32_t *causal_offsets,
+                const float *mask, float *o_part, size_t o_part_bytes, float *ml_part,
+                size_t ml_part_bytes, void *out_bf16, float *out_f32, bool partials_only,
+                pkv::DecodeArgs *a) {
+  if (!q || !k_cache || !v_cache || !block_table || !kv_lens) return PKV_ERR_NULL;
+  if (!partials_only && !out_bf16) return PKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (out_bf16 && !aligned(out_bf16, 16)) || !aligned(block_table, 4) || !aligned(kv_lens, 4) ||
+      (causal_offsets && !aligned(causal_offsets, 4)) || (mask && !aligned(mask, 4)) ||
+      (out_f32 && !aligned(out_f32, 16)))
+    return PKV_ERR_ALIGN;
+
+  // split count: forced, or the heuristic (needs the device's CU count)
+  int S = p->num_splits;
+  if (S == 0) {
+    int cus = 0;
+    int rc = query_cus(&cus);
+    if (rc) return rc;
+    S = heuristic_splits(p, cus);
+  }
+  if (S > 1 || partials_only) {
+    const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
+    const size_t need_o = rows * (size_t)S * (size_t)p->head_dim * sizeof(float);
+    const size_t need_ml = rows * (size_t)S * 2 * sizeof(float);
+    if (!o_part || !ml_part || o_part_bytes < need_o || ml_part_bytes < need_ml) return PKV_ERR_WORKSPACE;
+    if (!aligned(o_part, 16) || !aligned(ml_part, 8)) return PKV_ERR_ALIGN;
+  }
+
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int R = G * p->q_len;
+  const int rp = pkv::rows_per_block(R);
+  const int T = pkv::tile_keys(p->head_dim);
+  const int64_t L = max_len_of(p);
+  int64_t chunk = ceil_div(ceil_div(L, S), T) * T;
+  if (chunk < T) chunk = T;
+  if (chunk > INT32_MAX) return PKV_ERR_SHAPE;
+
+  *a = pkv::DecodeArgs{};
+  a->q = static_cast<const uint16_t *>(q);
+  a->k = static_cast<const uint16_t *>(k_cache);
+  a->v = static_cast<const uint16_t *>(v_cache);
+  a->block_table = block_table;
+  a->kv_lens = kv_lens;
+  a->causal_offsets = causal_offsets;
+  a->mask = mask;
+  a->o_part = (S > 1 || partials_only) ? o_part : nullptr;
+  a->ml_part = (S > 1 || partials_only) ? ml_part : nullptr;
+  a->out = static_cast<uint16_t *>(out_bf16);
+  a->out_f32 = out_f32;
+  a->mask_sb = p->mask_stride_b;
+  a->mask_sq = p->mask_stride_q;
+  a->page_stride = (int64_t)p->page_size * p->num_kv_heads * p->head_dim;
+  a->row_stride = p->num_kv_heads * p->head_dim;
+  a->B = p->batch;
+  a->q_len = p->q_len;
+  a->Hq = p->num_q_heads;
+  a->Hkv = p->num_kv_heads;
+  a->G = G;
+  a->R = R;
+  a->page_shift = ilog2(p->page_size);
+  a->max_pages = p->max_pages_per_seq;
+  a->S = S;
+  a->chunk = (int32_t)chunk;
+  a->nrb = (R + rp - 1) / rp;
+  a->causal_offset = p->causal_offset;
+  a->scale_log2 = p->scale * 1.4426950408889634f;
+  const int64_t outer = (int64_t)p->batch * S;
+  const int64_t inner = (int64_t)p->num_kv_heads * a->nrb;
+  if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > INT32_MAX) return PKV_ERR_SHAPE;
+  a->outer = (int32_t)outer;
+  a->inner = (int32_t)inner;
+  a->partials = (S > 1 || partials_only) ? 1 : 0;
+  return PKV_OK;
+}
+
+int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stream) {
+  const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0;
+  (void)hipGetLastError();
+  int err = pkv::launch_split(a, p->head_dim, pkv::rows_per_block(a.R), causal, a.mask != nullptr, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
+                     const void *v_cache, const int32_t *block_table,
+                     const int32_t *kv_lens, const int32_t *causal_offsets,
+                     const float *mask, float *o_part, size_t o_part_bytes,
+                     float *ml_part, size_t ml_part_bytes, void *out_bf16,
+                     float *out_f32, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->batch == 0) return PKV_OK;
+  pkv::DecodeArgs a;
+  rc = plan_decode(p, q, k_cache, v_cache, block_table, kv_lens, causal_offsets, mask, o_part,
+                   o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
+  if (rc) return rc;
+  rc = launch_plan(a, p, stream);
+  if (rc) return rc;
+  if (a.S > 1) {
+    pkv::CombineArgs c = {};
+    c.o_part = o_part;
+    c.ml_part = ml_part;
+    c.out = static_cast<uint16_t *>(out_bf16);
+    c.out_f32 = out_f32;
+    c.rows = (int64_t)p->batch * p->q_len * p->num_q_heads;
+    c.S = a.S;
+    if (pkv::launch_combine(c, p->head_dim, stream) != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+int pkv_paged_decode_partials(const pkv_problem *p, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *kv_lens, const int32_t *causal_offsets,
+                              const float *mask, float *o_part, size_t o_part_bytes,
+                              float *ml_part, size_t ml_part_bytes, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->batch == 0) return PKV_OK;
+  pkv::DecodeArgs a;
+  rc = plan_decode(p, q, k_cache, v_cache, block_table, kv_lens, causal_offsets, mask, o_part,
+                   o_part_bytes, ml_part, ml_part_bytes, nullptr, nullptr, true, &a);
+  if (rc) return rc;
+  return launch_plan(a, p, stream);
+}
+
+int pkv_combine(int64_t rows, int splits, int head_dim, const float *o_part,
+                const float *ml_part, void *out_bf16, float *out_f32,
+                hipStream_t stream) {
+  if (rows < 0 || splits < 1) return PKV_ERR_SHAPE;
+  if (splits > PKV_MAX_SPLITS || !supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (rows == 0) return PKV_OK;
+  if (!o_part || !ml_part || !out_bf16) return PKV_ERR_NULL;
+  if (!aligned(o_part, 16) || !aligned(ml_part, 8) || !aligned(out_bf16, 16) ||
+      (out_f32 && !aligned(out_f32, 16)))
+    return PKV_ERR_ALIGN;
+  if (rows > (int64_t)1 << 40) return PKV_ERR_SHAPE;
+  pkv::CombineArgs c = {};
+  c.o_part = o_part;
+  c.ml_part = ml_part;
+  c.out = static_cast<uint16_t *>(out_bf16);
+  c.out_f32 = out_f32;
+  c.rows = rows;
+  c.S = splits;
+  (void)hipGetLastError();
+  int err = pkv::launch_combine(c, head_dim, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

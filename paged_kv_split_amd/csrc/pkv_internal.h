@@ -1,0 +1,60 @@
+// pkv_internal.h -- launch plan shared by the host entry points and the HIP
+// kernels of libpkv.so (not part of the public ABI).
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace pkv {
+
+// Everything a split-decode launch needs, fixed on the host from host values
+// only (so a captured graph stays valid when device data changes).
+struct DecodeArgs {
+  const uint16_t *q;
+  const uint16_t *k;
+  const uint16_t *v;
+  const int32_t *block_table;
+  const int32_t *kv_lens;
+  const int32_t *causal_offsets;  // nullable
+  const float *mask;              // nullable
+  float *o_part;                  // [rows, S, D]   (S > 1)
+  float *ml_part;                 // [rows, S, 2]   (S > 1)
+  uint16_t *out;                  // bf16 [rows, D] (S == 1)
+  float *out_f32;                 // nullable       (S == 1)
+  int64_t mask_sb, mask_sq;
+  int64_t page_stride;            // elements per physical page: P * Hkv * D
+  int32_t row_stride;             // elements per page slot: Hkv * D
+  int32_t B, q_len, Hq, Hkv, G, R;  // R = G * q_len rows per kv head
+  int32_t page_shift;             // log2(page_size)
+  int32_t max_pages;              // block_table row stride
+  int32_t S;                      // splits
+  int32_t chunk;                  // keys per split (multiple of the tile)
+  int32_t nrb;                    // row blocks per kv head
+  int32_t causal_offset;          // -1 off (overridden by causal_offsets)
+  float scale_log2;               // scale * log2(e)
+  int32_t outer;                  // B * S
+  int32_t inner;                  // Hkv * nrb
+  int32_t partials;               // 1: write o_part/ml_part even when S == 1
+};
+
+struct CombineArgs {
+  const float *o_part;
+  const float *ml_part;
+  uint16_t *out;
+  float *out_f32;
+  int64_t rows;
+  int32_t S;
+};
+
+// Which split kernel serves a problem: rows packed per workgroup and keys
+// per wave tile for a head dim.
+int rows_per_block(int R);         // padded rows RP in {1, 2, 4, 8}
+int tile_keys(int head_dim);       // keys per wave tile T
+constexpr int kWavesPerBlock = 4;  // waves per split workgroup
+
+// Launchers (return a hipError_t value).
+int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
+                 bool has_mask, hipStream_t stream);
+int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,177 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol that
+include/pkv.h declares, rejects bad arguments with the documented status
+before any HIP call, sizes workspace and splits by the documented
+arithmetic, and links no allocation, copy or synchronisation routine."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_split_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert declared_functions() == sorted(pkv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True, text=True).stdout
+    defined = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in defined, name
+
+
+def test_link_audit_no_alloc_copy_or_sync():
+    out = subprocess.run(["nm", "-D", "--undefined-only", pkv.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1].split("@")[0] for l in out.splitlines() if l.strip()}
+    banned = [s for s in syms if re.match(
+        r"^hip(Malloc|Free|HostMalloc|HostFree|MallocAsync|FreeAsync|Memcpy|Memset|StreamSynchronize|"
+        r"DeviceSynchronize|EventSynchronize|MallocManaged)", s) and not s.endswith("Async") or
+        s in ("hipMemcpy", "hipMemset", "hipMalloc", "hipFree")]
+    # async copies are banned too: the library only launches kernels
+    banned += [s for s in syms if s.startswith(("hipMemcpy", "hipMemset", "hipMalloc", "hipFree"))]
+    assert not banned, banned
+
+
+def base_problem(**kw):
+    args = dict(batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32, num_pages=8,
+                max_pages_per_seq=4, max_kv_len=100, scale=0.125)
+    args.update(kw)
+    return pkv.make_problem(**args)
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake addresses: never dereferenced, checks fail first
+
+
+def call(p, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, kl=FAKE, co=0, mask=0, o=0, ob=0, ml=0, mb=0, out=FAKE,
+             out32=0)
+    a.update(ptrs)
+    return pkv.paged_decode_raw(p, a["q"], a["k"], a["v"], a["bt"], a["kl"], a["co"], a["mask"], a["o"],
+                                a["ob"], a["ml"], a["mb"], a["out"], a["out32"], 0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q_len", 0, pkv.PKV_ERR_SHAPE),
+    ("num_q_heads", 0, pkv.PKV_ERR_SHAPE),
+    ("num_kv_heads", 3, pkv.PKV_ERR_SHAPE),           # 8 % 3 != 0
+    ("head_dim", 96, pkv.PKV_ERR_UNSUPPORTED),
+    ("head_dim", 512, pkv.PKV_ERR_UNSUPPORTED),
+    ("page_size", 48, pkv.PKV_ERR_UNSUPPORTED),
+    ("page_size", 8192, pkv.PKV_ERR_UNSUPPORTED),
+    ("page_size", 0, pkv.PKV_ERR_UNSUPPORTED),
+    ("max_pages_per_seq", 0, pkv.PKV_ERR_SHAPE),
+    ("max_kv_len", 129, pkv.PKV_ERR_SHAPE),           # > 4 pages * 32
+    ("max_kv_len", -1, pkv.PKV_ERR_SHAPE),
+    ("batch", -1, pkv.PKV_ERR_SHAPE),
+    ("causal_offset", -2, pkv.PKV_ERR_SHAPE),
+    ("num_splits", -1, pkv.PKV_ERR_SHAPE),
+    ("num_splits", 257, pkv.PKV_ERR_UNSUPPORTED),
+    ("scale", float("nan"), pkv.PKV_ERR_SHAPE),
+    ("scale", float("inf"), pkv.PKV_ERR_SHAPE),
+    ("mask_stride_b", -4, pkv.PKV_ERR_SHAPE),
+    ("num_pages", -1, pkv.PKV_ERR_SHAPE),
+])
+def test_shape_errors(field, value, status):
+    p = base_problem(**{field: value})
+    assert call(p) == status
+    s = ctypes.c_int(0)
+    assert pkv.lib().pkv_num_splits(ctypes.byref(p), 256, ctypes.byref(s)) == status
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "bt", "kl", "out"])
+def test_null_pointers(which):
+    assert call(base_problem(num_splits=1), **{which: 0}) == pkv.PKV_ERR_NULL
+
+
+@pytest.mark.parametrize("which,addr", [("q", FAKE + 8), ("k", FAKE + 2), ("v", FAKE + 4), ("out", FAKE + 2),
+                                        ("out32", FAKE + 4), ("bt", FAKE + 2), ("kl", FAKE + 1),
+                                        ("mask", FAKE + 2), ("co", FAKE + 3)])
+def test_misaligned_pointers(which, addr):
+    assert call(base_problem(num_splits=1), **{which: addr}) == pkv.PKV_ERR_ALIGN
+
+
+def test_workspace_checks():
+    p = base_problem(num_splits=4)
+    ob, mb = pkv.workspace_bytes(p, 4)
+    rows = 2 * 1 * 8
+    assert ob == rows * 4 * 64 * 4 and mb == rows * 4 * 2 * 4
+    assert call(p) == pkv.PKV_ERR_WORKSPACE
+    assert call(p, o=FAKE, ob=ob, ml=FAKE, mb=mb - 1) == pkv.PKV_ERR_WORKSPACE
+    assert call(p, o=FAKE, ob=ob - 4, ml=FAKE, mb=mb) == pkv.PKV_ERR_WORKSPACE
+    assert call(p, o=FAKE + 8, ob=ob, ml=FAKE, mb=mb) == pkv.PKV_ERR_ALIGN
+    assert call(p, o=FAKE, ob=ob, ml=FAKE + 4, mb=mb) == pkv.PKV_ERR_ALIGN
+    assert pkv.workspace_bytes(p, 1) == (0, 0)
+    with pytest.raises(pkv.PkvError):
+        pkv.workspace_bytes(p, 0)
+    with pytest.raises(pkv.PkvError):
+        pkv.workspace_bytes(p, 257)
+
+
+def test_batch_zero_is_a_noop_even_with_null_pointers():
+    assert call(base_problem(batch=0), q=0, k=0, v=0, bt=0, kl=0, out=0) == pkv.PKV_OK
+
+
+def test_forced_splits_are_returned_unchanged():
+    for s in (1, 3, 64, 256):
+        assert pkv.num_splits(base_problem(num_splits=s), 256) == s
+
+
+def test_split_heuristic_shapes():
+    """Heuristic: one split when units fill the chip, more for few long sequences,
+    bounded by the key count and 64."""
+    # B=256, Hkv=8, R=32 -> 4 row blocks: 8192 units >= 4*256 -> 1
+    big = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                       max_pages_per_seq=256, max_kv_len=8192, num_pages=13000)
+    assert pkv.num_splits(big, 256) == 1
+    # B=4, Hkv=8, G=4 -> 32 units, 32768 keys -> splits to reach 1024 workgroups
+    long = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+                        max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
+    s = pkv.num_splits(long, 256)
+    assert s == 32
+    # short sequences cap the split count
+    short = base_problem(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
+                         max_kv_len=100)
+    assert pkv.num_splits(short, 256) == 1
+    # more CUs never means fewer splits
+    assert pkv.num_splits(long, 512) >= pkv.num_splits(long, 256)
+    # the heuristic never exceeds 64
+    huge = base_problem(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=32, page_size=4096,
+                        max_pages_per_seq=500, max_kv_len=2_000_000)
+    assert pkv.num_splits(huge, 1024) == 64
+
+
+def test_combine_argument_checks():
+    lib = pkv
+    assert lib.combine_raw(4, 0, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_SHAPE
+    assert lib.combine_raw(-1, 2, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_SHAPE
+    assert lib.combine_raw(4, 2, 48, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.combine_raw(4, 300, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.combine_raw(4, 2, 64, 0, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_NULL
+    assert lib.combine_raw(4, 2, 64, FAKE + 4, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_ALIGN
+    assert lib.combine_raw(0, 2, 64, 0, 0, 0, 0, 0) == pkv.PKV_OK
+
+
+def test_status_strings_are_distinct():
+    msgs = {pkv.status_string(s) for s in range(8)}
+    assert len(msgs) == 8
+    assert pkv.status_string(99) == "unknown status"
+
+
+def test_problem_struct_layout():
+    assert ctypes.sizeof(pkv.Problem) == 64
+    assert pkv.Problem.mask_stride_b.offset == 48

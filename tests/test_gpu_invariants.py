@@ -1,0 +1,261 @@
+"""GPU invariants that need no oracle value: byte-identity under physical page
+reshuffles and buffer moves, exact closed forms, poisoned unused memory,
+agreement across split counts, graph capture, stream ordering and guard
+bands around every output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_split_amd as pkv
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check, dev_tensors, note, problem, run  # noqa: E402
+
+
+def permute_pages(w, seed):
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(w.num_pages)
+    k = np.empty_like(w.k_cache)
+    v = np.empty_like(w.v_cache)
+    k[perm] = w.k_cache
+    v[perm] = w.v_cache
+    bt = np.where(w.block_table >= 0, perm[np.clip(w.block_table, 0, None)], -1).astype(np.int32)
+    return w.replace(k_cache=k, v_cache=v, block_table=bt)
+
+
+CASES = [
+    lambda: workloads.tiny(),
+    lambda: workloads.build("reshuffle_gqa", B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                            kv_lens=[1000, 513, 64, 1], seed=3001, mask="2d", spare_pages=5),
+    lambda: workloads.build("reshuffle_causal", B=3, q_len=4, Hq=16, Hkv=2, D=64, page_size=16,
+                            kv_lens=[300, 45, 128], seed=3002, causal="last"),
+    lambda: workloads.build("reshuffle_d256", B=2, q_len=1, Hq=8, Hkv=8, D=256, page_size=64,
+                            kv_lens=[700, 250], seed=3003),
+    lambda: workloads.build("reshuffle_d32", B=2, q_len=1, Hq=64, Hkv=8, D=32, page_size=32,
+                            kv_lens=[900, 31], seed=3004, mask="2d"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+@pytest.mark.parametrize("splits", [1, 7])
+def test_page_reshuffle_is_byte_identical(i, splits):
+    w = CASES[i]()
+    note(f"reshuffle {w.name} splits={splits}")
+    a16, a32 = run(w, num_splits=splits)
+    for seed in (1, 2):
+        b16, b32 = run(permute_pages(w, seed), num_splits=splits)
+        assert np.array_equal(a16, b16)
+        assert np.array_equal(a32.view(np.uint32), b32.view(np.uint32))
+
+
+def test_kv_len_one_returns_v_row_exactly():
+    w = workloads.build("kv1", B=5, q_len=1, Hq=16, Hkv=4, D=128, page_size=32, kv_lens=[1] * 5,
+                        seed=3010, spare_pages=4)
+    for splits in (1, 4):
+        note(f"kv_len=1 splits={splits}")
+        out16, out32 = run(w, num_splits=splits)
+        G = w.Hq // w.Hkv
+        for b in range(w.B):
+            pg = w.block_table[b, 0]
+            for h in range(w.Hq):
+                assert np.array_equal(out16[b, 0, h], w.v_cache[pg, 0, h // G])
+
+
+def test_unused_block_table_entries_and_poison_never_read():
+    w = workloads.build("poison", B=3, q_len=1, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[33, 100, 2],
+                        seed=3020, spare_pages=6, max_pages_per_seq=8)
+    ref16, ref32 = run(w, num_splits=1)
+    bt = w.block_table.copy()
+    bt[bt < 0] = np.iinfo(np.int32).max                     # would fault if dereferenced
+    for splits in (1, 3):
+        out16, out32 = run(w.replace(block_table=bt), num_splits=splits)
+        assert np.isfinite(out32).all()
+        check(out16, out32, oracle.decode(w), "poison")
+    out16, out32 = run(w.replace(block_table=bt), num_splits=1)
+    assert np.array_equal(out16, ref16)
+
+
+def test_gqa_matches_mha_with_repeated_heads():
+    w = workloads.build("gqa", B=2, q_len=1, Hq=32, Hkv=4, D=128, page_size=32, kv_lens=[700, 300],
+                        seed=3030)
+    G = w.Hq // w.Hkv
+    mha = w.replace(Hkv=w.Hq, k_cache=np.repeat(w.k_cache, G, axis=2).copy(),
+                    v_cache=np.repeat(w.v_cache, G, axis=2).copy())
+    a16, a32 = run(w, num_splits=1)
+    b16, b32 = run(mha, num_splits=1)
+    assert np.abs(a32.astype(np.float64) - b32).max() <= 2e-3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_counts_agree(D):
+    w = workloads.build("splits", B=2, q_len=1, Hq=16, Hkv=4, D=D, page_size=64, kv_lens=[4000, 1500],
+                        seed=3040 + D, outlier_p=0.01)
+    ref = oracle.decode(w)
+    outs = {}
+    for s in (1, 0, 2, 64, 256):
+        note(f"splits {s}")
+        outs[s] = run(w, num_splits=s)
+        check(*outs[s], ref, f"S={s}")
+    for s in (0, 2, 64, 256):
+        assert np.abs(outs[s][1].astype(np.float64) - outs[1][1]).max() <= 2e-3
+
+
+def test_zero_mask_is_byte_identical_to_no_mask():
+    w = workloads.build("zmask", B=3, q_len=2, Hq=8, Hkv=2, D=128, page_size=32, kv_lens=[300, 77, 1],
+                        seed=3050, mask="2d", mask_p=0.0)
+    for s in (1, 3):
+        a = run(w, num_splits=s)
+        b = run(w.replace(mask=None), num_splits=s)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_causal_equals_truncated_single_token_calls():
+    w = workloads.build("causal", B=3, q_len=4, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[300, 45, 4],
+                        seed=3060, causal="last")
+    out16, out32 = run(w, num_splits=1)
+    for i in range(w.q_len):
+        lens = np.minimum(w.kv_lens, w.causal_offsets + i + 1).astype(np.int32)
+        wi = w.replace(q_len=1, q=w.q[:, i:i + 1].copy(), kv_lens=lens, causal_offsets=None)
+        b16, b32 = run(wi, num_splits=1)
+        assert np.abs(out32[:, i:i + 1].astype(np.float64) - b32).max() <= 2e-3
+
+
+def test_replicas_at_other_addresses_are_byte_identical():
+    w = workloads.build("replica", B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                        kv_lens=[2000, 100, 1, 900], seed=3070, mask="2d")
+    d1 = dev_tensors(w)
+    pad = torch.empty(12345 * 16, dtype=torch.uint8, device="cuda:0")   # shift later allocations
+    d2 = dev_tensors(w)
+    assert d1["k"].data_ptr() != d2["k"].data_ptr()
+    for s in (1, 5):
+        a = run(w, d1, num_splits=s)
+        b = run(w, d2, num_splits=s)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    del pad
+
+
+def test_repeated_calls_are_deterministic():
+    w = workloads.ragged(B=32, hi=2048)
+    d = dev_tensors(w)
+    a = run(w, d)
+    for _ in range(3):
+        b = run(w, d)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_graph_capture_replay_matches_eager():
+    """Capture one call into a hipGraph with preallocated buffers, then replay
+    after changing q and kv_lens in place; every replay must equal eager."""
+    w = workloads.build("graph", B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                        kv_lens=[1500, 900, 64, 1000], seed=3080, mask="2d")
+    d = dev_tensors(w)
+    p = problem(w, num_splits=4)
+    ob, mb = pkv.workspace_bytes(p, 4)
+    o_part = torch.empty(ob // 4, dtype=torch.float32, device="cuda:0")
+    ml_part = torch.empty(mb // 4, dtype=torch.float32, device="cuda:0")
+    out = torch.empty(tuple(d["q"].shape), dtype=torch.bfloat16, device="cuda:0")
+    out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
+
+    def call(stream=None):
+        pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale, mask=d["mask"],
+                         out=out, out_f32=out32, o_part=o_part, ml_part=ml_part, problem=p, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out32.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        if rep:
+            newq = torch.randn(d["q"].shape, generator=torch.Generator().manual_seed(rep)).to(torch.bfloat16)
+            d["q"].copy_(newq.to("cuda:0"))
+            lens = rng.integers(1, w.kv_lens + 1).astype(np.int32)   # stay within each sequence's pages
+            d["kl"].copy_(torch.from_numpy(lens).to("cuda:0"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replay = out32.clone()
+        replay16 = out.clone()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(replay.view(torch.int32), out32.view(torch.int32)), f"replay {rep}"
+        assert torch.equal(replay16.view(torch.int16), out.view(torch.int16)), f"replay {rep}"
+        if rep == 0:
+            assert torch.equal(replay.view(torch.int32), eager.view(torch.int32))
+
+
+def test_runs_on_the_given_stream_in_order():
+    """Inputs are written by work queued on a side stream just before the call;
+    a correct result shows the kernels ran on that stream after it."""
+    w = workloads.build("stream", B=8, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                        kv_lens=[2048] * 8, seed=3090)
+    ref16, ref32 = run(w, num_splits=0)
+    d = dev_tensors(w)
+    real_q = d["q"].clone()
+    d["q"].zero_()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    big = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0")
+    with torch.cuda.stream(s):
+        for _ in range(20):
+            big.mul_(1.0001)       # long-running work ahead of the copy
+        d["q"].copy_(real_q)
+    out16, out32 = run(w, d, num_splits=0, stream=s)
+    assert np.array_equal(out16, ref16)
+
+
+def test_guard_bands_untouched():
+    w = workloads.build("canary", B=3, q_len=2, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[500, 3, 200],
+                        seed=3100, mask="2d", causal="last")
+    d = dev_tensors(w)
+    S = 6
+    p = problem(w, num_splits=S)
+    ob, mb = pkv.workspace_bytes(p, S)
+    n = int(np.prod(d["q"].shape))
+    G = 4096  # guard elements on each side
+    sent32 = np.float32(-7.25)
+    buf16 = torch.full((n + 2 * G,), 0x5A5A, dtype=torch.int16, device="cuda:0")
+    buf32 = torch.full((n + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
+    bufo = torch.full((ob // 4 + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
+    bufm = torch.full((mb // 4 + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
+    out = buf16[G:G + n].view(torch.bfloat16).view(d["q"].shape)
+    out32 = buf32[G:G + n].view(d["q"].shape)
+    pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale, causal_offsets=d["co"],
+                     mask=d["mask"], out=out, out_f32=out32, o_part=bufo[G:G + ob // 4],
+                     ml_part=bufm[G:G + mb // 4], problem=p)
+    torch.cuda.synchronize()
+    for buf, val in ((buf16, 0x5A5A), (buf32, sent32), (bufo, sent32), (bufm, sent32)):
+        h = buf.cpu().numpy()
+        assert (h[:G] == val).all() and (h[-G:] == val).all()
+    check(out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), oracle.decode(w), "canary")
+
+
+def test_combine_entry_point_on_hand_made_partials():
+    rows, S, D = 37, 5, 128
+    rng = np.random.default_rng(7)
+    o = rng.standard_normal((rows, S, D)).astype(np.float32)
+    m = rng.standard_normal((rows, S)).astype(np.float32) * 3
+    l = rng.uniform(0.5, 40, (rows, S)).astype(np.float32)
+    l[3, :] = 0
+    m[3, :] = -np.inf
+    l[5, 2] = 0
+    m[5, 2] = -np.inf
+    ml = np.stack([m, l], axis=-1)
+    ref = oracle.combine(o.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
+    od = torch.from_numpy(o).cuda()
+    mld = torch.from_numpy(np.ascontiguousarray(ml)).cuda()
+    out32 = torch.empty((rows, D), dtype=torch.float32, device="cuda:0")
+    out = pkv.combine(od, mld, rows=rows, splits=S, head_dim=D, out_f32=out32)
+    torch.cuda.synchronize()
+    check(out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref, "combine")
+    assert not out32[3].any()

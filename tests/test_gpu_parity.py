@@ -1,0 +1,98 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Tolerances: max |out_f32 - ref| <= 2e-3, max |out_bf16 - ref| <= 1e-2 (half a
+bf16 ulp + 2e-3 where |ref| >= 4, since bf16 rounding alone exceeds 1e-2
+there), out_bf16 == RNE(out_f32) bit for bit.  Small cases are checked on every
+output; the full-size decode shapes on every output where the oracle is quick
+and on sampled sequences (all their rows) where it is not.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check, note, run, sub_batch  # noqa: E402
+
+
+def compare(w, num_splits=0, seqs=None):
+    note(f"case {w.name} B={w.B} q_len={w.q_len} Hq={w.Hq} Hkv={w.Hkv} D={w.D} P={w.page_size} "
+         f"maxL={w.max_kv_len} splits={num_splits} seed={w.seed}")
+    out16, out32 = run(w, num_splits=num_splits)
+    if seqs is None:
+        ref = oracle.decode(w)
+        return check(out16, out32, ref, w.name)
+    ref = oracle.decode(sub_batch(w, seqs))
+    return check(out16[seqs], out32[seqs], ref, w.name)
+
+
+# ---- the five decode shapes -------------------------------------------------
+
+def test_tiny():
+    compare(workloads.tiny())
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+def test_tiny_forced_splits(splits):
+    compare(workloads.tiny(), num_splits=splits)
+
+
+def test_decode_1b_full():
+    compare(workloads.decode_1b())
+
+
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+@pytest.mark.parametrize("Hq", [8, 32, 64])
+def test_sweep_full_size_sampled(D, Hq):
+    w = workloads.sweep(D, Hq)
+    compare(w, seqs=[0, 7, 15])
+
+
+@pytest.mark.parametrize("splits", [0, 1, 64])
+def test_long_ctx_full(splits):
+    compare(workloads.long_ctx(), num_splits=splits)
+
+
+def test_ragged_full_size_sampled():
+    w = workloads.ragged()
+    L = w.kv_lens
+    seqs = sorted({int(L.argmax()), int(L.argmin()), 0, 1, 100, 255})
+    compare(w, seqs=seqs)
+
+
+# ---- smaller cases that span several tiles and a ragged tail -----------------
+
+SMALL = [
+    dict(B=3, q_len=1, Hq=8, Hkv=8, D=32, page_size=32, kv_lens=[1, 300, 517]),
+    dict(B=3, q_len=1, Hq=32, Hkv=8, D=64, page_size=16, kv_lens=[65, 255, 0]),
+    dict(B=2, q_len=1, Hq=64, Hkv=8, D=128, page_size=64, kv_lens=[700, 33]),
+    dict(B=2, q_len=1, Hq=16, Hkv=2, D=256, page_size=32, kv_lens=[257, 130]),
+    dict(B=4, q_len=1, Hq=24, Hkv=4, D=64, page_size=32, kv_lens=[128, 129, 2047, 5]),   # G=6
+    dict(B=2, q_len=3, Hq=6, Hkv=2, D=128, page_size=8, kv_lens=[100, 41], causal="last"),  # R=9: 2 row blocks
+    dict(B=2, q_len=4, Hq=64, Hkv=8, D=128, page_size=32, kv_lens=[300, 64], causal="last"),  # R=32
+    dict(B=2, q_len=2, Hq=4, Hkv=1, D=32, page_size=1, kv_lens=[77, 5], causal=70),
+    dict(B=2, q_len=1, Hq=2, Hkv=2, D=64, page_size=256, kv_lens=[600, 1]),
+    dict(B=3, q_len=2, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[200, 90, 13], mask="3d"),
+    dict(B=3, q_len=1, Hq=16, Hkv=4, D=128, page_size=32, kv_lens=[400, 333, 1], mask="2d", mask_p=0.5),
+    dict(B=2, q_len=1, Hq=8, Hkv=1, D=256, page_size=64, kv_lens=[1000, 999], outlier_p=0.05),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_small_cases(i, splits):
+    kw = dict(SMALL[i])
+    w = workloads.build(f"small{i}", seed=2000 + i, spare_pages=3, **kw)
+    compare(w, num_splits=splits)
+
+
+def test_all_masked_and_empty_rows_are_zero():
+    w = workloads.build("masked", B=3, q_len=1, Hq=8, Hkv=2, D=64, page_size=32,
+                        kv_lens=[50, 0, 90], seed=2100, mask="2d", mask_p=0.0)
+    w.mask[2, :] = -np.inf
+    for s in (1, 4):
+        out16, out32 = run(w, num_splits=s)
+        assert not out32[1:].any() and not out16[1:].any()
+        check(out16, out32, oracle.decode(w), "masked")
