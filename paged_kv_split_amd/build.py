@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("pkv_host.cpp", "pkv_decode.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("pkv_host.cpp", "pkv_decode.hip", "pkv_decode_mfma.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -14,15 +14,20 @@
 //  * a workgroup is kWavesPerBlock wave64s; wave w takes tiles w, w+NW, ...
 //    of T keys and keeps its own (m, l, acc); waves merge once at the end
 //    through LDS, so the key loop has no workgroup barrier;
+//  * the split's slice of the page table is staged in LDS once (in windows of
+//    kBtCap pages), so a K/V address costs an LDS read, not an HBM round trip;
+//  * K/V tiles are double-buffered in registers: the loads of a wave's next
+//    tile are in flight while it computes the current one;
 //  * QK^T uses v_dot2_f32_bf16 on packed bf16 pairs (exact products, fp32
 //    accumulation) in a "key-major" lane layout: D/32 lanes per key, each
-//    holding 32 elements of q and k, reduced across those lanes;
+//    holding 32 elements of q and k, summed across those lanes with DPP;
 //  * PV uses fp32 FMAs in a "d-major" layout: D/8 lanes per key, each owning
 //    8 output columns; probabilities cross between the two layouts through a
 //    per-wave LDS slice (no barrier: LDS is in order within a wave);
-//  * K and V rows are fetched with 128-bit loads, one page-table lookup per
-//    key row, 64-bit element offsets; rows past the split end are never
-//    loaded (tails read as zero);
+//  * cross-lane max/sum use DPP (quad_perm, row mirrors, row_ror) and the
+//    gfx950 permlane16/32 swaps, no LDS traffic;
+//  * K and V rows are fetched with 128-bit loads; rows past the split end are
+//    never loaded (tails read as zero);
 //  * the workgroup index is decoded so that the Hkv x row-block siblings of a
 //    (b, s) unit land on the same XCD back to back (blocks are dealt to the 8
 //    XCDs round-robin), so they share that XCD's L2 for the interleaved kv
@@ -40,7 +45,8 @@ int rows_per_block(int R) {
   if (R <= 1) return 1;
   if (R <= 2) return 2;
   if (R <= 4) return 4;
-  return 8;
+  if (R <= 8) return 8;
+  return R <= 16 ? 16 : 32;
 }
 
 int tile_keys(int head_dim) { return 2 * (64 / (head_dim / 32)); }
@@ -51,6 +57,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBtCap = 1024;  // page-table entries staged in LDS per window
+constexpr int kMaxSplitsCombine = 256;  // = PKV_MAX_SPLITS
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -70,25 +78,80 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
-// max / sum over the lanes that differ in lane-id bits [LO, 6)
-template <int LO>
-__device__ __forceinline__ float wave_max_hi(float x) {
-#pragma unroll
-  for (int bit = LO; bit < 6; ++bit) x = fmaxf(x, __shfl_xor(x, 1 << bit, 64));
+// ---- cross-lane primitives (DPP / permlane; semantics checked on gfx950) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kRor4 = 0x124;       // lane i receives lane (i-4) mod 16
+constexpr int kRor8 = 0x128;       // lane i receives lane (i-8) mod 16 (= i xor 8)
+
+struct OpSum {
+  __device__ static float f(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+};
+
+template <class Op>
+__device__ __forceinline__ float xor16(float x) {  // combine lanes i and i^16
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x) {  // combine lanes i and i^32
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Reduce over lane bits [0, HI) (HI <= 3) of independent values.
+template <int HI, class Op>
+__device__ __forceinline__ float reduce_lo(float x) {
+  if constexpr (HI >= 1) x = Op::f(x, dpp<kXor1>(x));
+  if constexpr (HI >= 2) x = Op::f(x, dpp<kXor2>(x));
+  if constexpr (HI >= 3) x = Op::f(x, dpp<kHalfMirror>(x));  // quads already reduced
   return x;
 }
-template <int LO>
-__device__ __forceinline__ float wave_sum_hi(float x) {
-#pragma unroll
-  for (int bit = LO; bit < 6; ++bit) x += __shfl_xor(x, 1 << bit, 64);
+
+// Reduce over lane bits [LO, 6) when lanes that differ only in bits [0, LO)
+// already hold equal values (mirror pairings are then valid).
+template <int LO, class Op>
+__device__ __forceinline__ float reduce_hi_grouped(float x) {
+  if constexpr (LO <= 0) x = Op::f(x, dpp<kXor1>(x));
+  if constexpr (LO <= 1) x = Op::f(x, dpp<kXor2>(x));
+  if constexpr (LO <= 2) x = Op::f(x, dpp<kHalfMirror>(x));
+  if constexpr (LO <= 3) x = Op::f(x, dpp<kMirror>(x));
+  if constexpr (LO <= 4) x = xor16<Op>(x);
+  x = xor32<Op>(x);
   return x;
 }
-// sum over the lanes that differ in lane-id bits [0, HI)
-template <int HI>
-__device__ __forceinline__ float wave_sum_lo(float x) {
-#pragma unroll
-  for (int bit = 0; bit < HI; ++bit) x += __shfl_xor(x, 1 << bit, 64);
+
+// Reduce over lane bits [LO, 6) of independent values (true xor pairings).
+template <int LO, class Op>
+__device__ __forceinline__ float reduce_hi(float x) {
+  if constexpr (LO <= 0) x = Op::f(x, dpp<kXor1>(x));
+  if constexpr (LO <= 1) x = Op::f(x, dpp<kXor2>(x));
+  if constexpr (LO <= 2) {  // bits 2 and 3 together: lanes i, i-4, i+4, i+8 (mod 16)
+    x = Op::f(x, dpp<kRor4>(x));
+    x = Op::f(x, dpp<kRor8>(x));
+  } else if constexpr (LO <= 3) {
+    x = Op::f(x, dpp<kRor8>(x));
+  }
+  if constexpr (LO <= 4) x = xor16<Op>(x);
+  x = xor32<Op>(x);
   return x;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit streaming load (K/V are read once per unit: non-temporal hint)
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ uint32_t comp(const uint4 &v, int e) {
@@ -100,8 +163,9 @@ struct Layout {
   static constexpr int NW = kWavesPerBlock;
   static constexpr int LPK = D / 32;       // lanes per key, QK layout
   static constexpr int KPP = 64 / LPK;     // keys per QK pass
-  static constexpr int NPASS = 2;
+  static constexpr int NPASS = 1;
   static constexpr int T = KPP * NPASS;    // keys per wave tile
+  static constexpr bool QREG = RP <= 2;    // q in registers; else read from LDS (shared by the block)
   static constexpr int LPV = D / 8;        // lanes per key, PV layout
   static constexpr int KPV = 64 / LPV;     // keys per PV step
   static constexpr int NSTEP = T / KPV;    // PV steps per tile
@@ -109,14 +173,217 @@ struct Layout {
   static constexpr int LOG_LPV = ilog2c(LPV);
   static constexpr int PBUF = NW * T * RP;             // floats
   static constexpr int MERGE = NW * RP * D + NW * RP * 2;
-  static constexpr int SMEM = PBUF > MERGE ? PBUF : MERGE;
+  static constexpr int QLDS = QREG ? 0 : RP * D / 2;  // q rows as packed bf16 pairs (floats)
+  static constexpr int MAIN = kBtCap + 4 + QLDS + PBUF;  // page-table slice (+1 page when a window
+                                                         // starts mid-page), q, p slices
+  static constexpr int SMEM = MAIN > MERGE ? MAIN : MERGE;
 };
+
+// Per-wave context of the split kernel.
+template <int D, int RP>
+struct Ctx {
+  const uint16_t *kbase, *vbase;
+  const int *bt;         // LDS page-table slice
+  int p0;                // first page of the slice
+  int page_shift, pmask;
+  int64_t page_stride;
+  int row_stride;
+  int kb;                // first key of the split
+  int ke;                // end of the keys this block may see
+  int jq, qq, kg, ds;
+};
+
+template <int D, int RP>
+struct Tile {
+  uint4 k[Layout<D, RP>::NPASS][4];
+  uint4 v[Layout<D, RP>::NSTEP];
+};
+
+template <int D, int RP>
+__device__ __forceinline__ int64_t row_offset(const Ctx<D, RP> &c, int j) {
+  const int page = c.bt[(j >> c.page_shift) - c.p0];
+  return (int64_t)page * c.page_stride + (int64_t)(j & c.pmask) * c.row_stride;
+}
+
+// Issue the loads of tile `base` (keys base .. base+T-1) into registers.
+template <int D, int RP>
+__device__ __forceinline__ void load_tile(const Ctx<D, RP> &c, int base, Tile<D, RP> &t) {
+  using Lay = Layout<D, RP>;
+#pragma unroll
+  for (int pp = 0; pp < Lay::NPASS; ++pp) {
+    const int j = base + pp * Lay::KPP + c.jq;
+    if (j < c.ke) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(c.kbase + row_offset(c, j));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = load_stream(src + c.qq + Lay::LPK * c4);
+    } else {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < Lay::NSTEP; ++st) {
+    const int j = base + st * Lay::KPV + c.kg;
+    if (j < c.ke) {
+      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + row_offset(c, j)) + c.ds);
+    } else {
+      t.v[st] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// Online-softmax state of one wave.
+template <int RP>
+struct State {
+  float m[RP];        // running max (base-2 units), uniform across the wave
+  float l[RP];        // running sum of this lane's key group (QK layout)
+  float acc[RP][8];   // PV accumulator, this lane's 8 columns and key group
+};
+
+// q rows of a block: in registers (few rows) or read from the block's LDS copy
+template <int D, int RP, bool QREG>
+struct QRows;
+template <int D, int RP>
+struct QRows<D, RP, true> {
+  uint4 v[RP][4];  // this lane's chunks qq + LPK*c4 of every row
+  __device__ __forceinline__ uint4 get(int r, int c4, int) const { return v[r][c4]; }
+};
+template <int D, int RP>
+struct QRows<D, RP, false> {
+  const uint4 *lds;  // [RP][D/8] in LDS
+  __device__ __forceinline__ uint4 get(int r, int c4, int qq) const {
+    return lds[r * (D / 8) + qq + (D / 32) * c4];
+  }
+};
+
+template <int D, int RP, bool CAUSAL, bool MASK, class Q>
+__device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int base,
+                                             const Tile<D, RP> &t, const Q &qrows,
+                                             const int (&lim)[RP], int b, int r0, float *pbuf,
+                                             State<RP> &st) {
+  using Lay = Layout<D, RP>;
+  constexpr int NPASS = Lay::NPASS, KPP = Lay::KPP, LPK = Lay::LPK;
+  // scores, summed over the LPK lanes of each key
+  float sc[NPASS][RP];
+#pragma unroll
+  for (int pp = 0; pp < NPASS; ++pp) {
+    float d[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) d[r] = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const uint4 kk = t.k[pp][c4];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        const uint4 qv = qrows.get(r, c4, c.qq);
+        d[r] = dot2_bf16(kk.x, qv.x, d[r]);
+        d[r] = dot2_bf16(kk.y, qv.y, d[r]);
+        d[r] = dot2_bf16(kk.z, qv.z, d[r]);
+        d[r] = dot2_bf16(kk.w, qv.w, d[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) sc[pp][r] = reduce_lo<Lay::LOG_LPK, OpSum>(d[r]);
+  }
+  // scale, mask, visibility
+#pragma unroll
+  for (int pp = 0; pp < NPASS; ++pp) {
+    const int j = base + pp * KPP + c.jq;
+    const bool in = j < c.ke;
+    float mv[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) mv[r] = 0.f;
+    if (MASK && in) {
+      if (a.mask_sq == 0) {
+        const float m0 = a.mask[(int64_t)b * a.mask_sb + j] * kLog2e;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) mv[r] = m0;
+      } else {
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
+          mv[r] = a.mask[(int64_t)b * a.mask_sb + (int64_t)(rr / a.G) * a.mask_sq + j] * kLog2e;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const float v = fmaf(sc[pp][r], a.scale_log2, mv[r]);
+      const bool vis = CAUSAL ? (in && j < lim[r]) : (in && lim[r] > 0);
+      sc[pp][r] = vis ? v : -INFINITY;
+    }
+  }
+  // online softmax update (m uniform across the wave)
+  float alpha[RP], mu[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float mt = sc[0][r];
+#pragma unroll
+    for (int pp = 1; pp < NPASS; ++pp) mt = fmaxf(mt, sc[pp][r]);
+    mt = reduce_hi_grouped<Lay::LOG_LPK, OpMax>(mt);
+    const float mnew = fmaxf(st.m[r], mt);
+    const float use = mnew == -INFINITY ? 0.f : mnew;
+    alpha[r] = fast_exp2(st.m[r] - use);
+    st.m[r] = mnew;
+    mu[r] = use;
+  }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NPASS; ++pp) {
+      const float pv = fast_exp2(sc[pp][r] - mu[r]);
+      lsum += pv;
+      if ((r & (LPK - 1)) == c.qq) pbuf[(pp * KPP + c.jq) * RP + r] = pv;
+    }
+    st.l[r] = fmaf(st.l[r], alpha[r], lsum);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // PV
+#pragma unroll
+  for (int r = 0; r < RP; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[r][e] *= alpha[r];
+#pragma unroll
+  for (int s2 = 0; s2 < Lay::NSTEP; ++s2) {
+    const int key = s2 * Lay::KPV + c.kg;
+    float pr[RP];
+    if constexpr (RP >= 4) {
+#pragma unroll
+      for (int r4 = 0; r4 < RP / 4; ++r4) {
+        const float4 t4 = reinterpret_cast<const float4 *>(pbuf + key * RP)[r4];
+        pr[4 * r4 + 0] = t4.x;
+        pr[4 * r4 + 1] = t4.y;
+        pr[4 * r4 + 2] = t4.z;
+        pr[4 * r4 + 3] = t4.w;
+      }
+    } else if constexpr (RP == 2) {
+      const float2 t2 = reinterpret_cast<const float2 *>(pbuf + key * RP)[0];
+      pr[0] = t2.x;
+      pr[1] = t2.y;
+    } else {
+      pr[0] = pbuf[key];
+    }
+    float vf[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t u = comp(t.v[s2], e2);
+      vf[2 * e2] = bf16_lo(u);
+      vf[2 * e2 + 1] = bf16_hi(u);
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[r][e] = fmaf(pr[r], vf[e], st.acc[r][e]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
 
 template <int D, int RP, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const DecodeArgs a) {
   using Lay = Layout<D, RP>;
-  constexpr int NW = Lay::NW, LPK = Lay::LPK, KPP = Lay::KPP, NPASS = Lay::NPASS, T = Lay::T;
-  constexpr int LPV = Lay::LPV, KPV = Lay::KPV, NSTEP = Lay::NSTEP;
+  constexpr int NW = Lay::NW, LPK = Lay::LPK, T = Lay::T, LPV = Lay::LPV;
   __shared__ __attribute__((aligned(16))) float smem[Lay::SMEM];
 
   // ---- unit decode (XCD-aware): siblings (kv head, row block) of one
@@ -134,13 +401,11 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int jq = lane / LPK, qq = lane % LPK;   // QK layout
-  const int kg = lane / LPV, ds = lane % LPV;   // PV layout
 
   const int r0 = rb * RP;
   const int L = a.kv_lens[b];
-  int c = -1;
-  if (CAUSAL) c = a.causal_offsets ? a.causal_offsets[b] : a.causal_offset;
+  int cofs = -1;
+  if (CAUSAL) cofs = a.causal_offsets ? a.causal_offsets[b] : a.causal_offset;
 
   // per-row visible key limit and the block's key range
   int lim[RP];
@@ -151,220 +416,144 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     int lr = 0;
     if (rr < a.R) {
       lr = L;
-      if (CAUSAL && c >= 0) {
-        const int64_t cl = (int64_t)c + rr / a.G + 1;
+      if (CAUSAL && cofs >= 0) {
+        const int64_t cl = (int64_t)cofs + rr / a.G + 1;
         if (cl < lr) lr = (int)cl;
       }
     }
     lim[r] = lr;
     kmax = lr > kmax ? lr : kmax;
   }
-  const int kb = s * a.chunk;
-  int ke = kb + a.chunk;
-  if (ke > kmax) ke = kmax;
-  const int ntiles = kb < ke ? (ke - kb + T - 1) / T : 0;
 
-  // ---- q rows of this block in registers (QK layout: chunks qq + LPK*c4)
-  uint32_t qr[RP][16];
+  Ctx<D, RP> c;
+  c.kbase = a.k + g * D;
+  c.vbase = a.v + g * D;
+  c.bt = reinterpret_cast<const int *>(smem);
+  c.page_shift = a.page_shift;
+  c.pmask = (1 << a.page_shift) - 1;
+  c.page_stride = a.page_stride;
+  c.row_stride = a.row_stride;
+  c.kb = s * a.chunk;
+  int kend = c.kb + a.chunk;
+  if (kend > kmax) kend = kmax;
+  c.jq = lane / LPK;
+  c.qq = lane % LPK;
+  c.kg = lane / LPV;
+  c.ds = lane % LPV;
+
+  // ---- q rows of this block: registers (QK layout: chunks qq + LPK*c4) or
+  // the block's LDS copy [RP][D] (zero rows past R)
+  QRows<D, RP, Lay::QREG> qrows;
+  if constexpr (Lay::QREG) {
 #pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const int rr = r0 + r;
-    if (rr < a.R) {
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
+    for (int r = 0; r < RP; ++r) {
+      const int rr = r0 + r;
+      if (rr < a.R) {
+        const int i = rr / a.G;
+        const int h = g * a.G + (rr - i * a.G);
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const uint4 t = src[qq + LPK * c4];
-        qr[r][4 * c4 + 0] = t.x;
-        qr[r][4 * c4 + 1] = t.y;
-        qr[r][4 * c4 + 2] = t.z;
-        qr[r][4 * c4 + 3] = t.w;
+        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
+      } else {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) qr[r][e] = 0u;
     }
+  } else {
+    uint4 *qs = reinterpret_cast<uint4 *>(smem + kBtCap + 4);
+    for (int idx = threadIdx.x; idx < RP * (D / 8); idx += NW * 64) {
+      const int r = idx / (D / 8);
+      const int ch = idx - r * (D / 8);
+      const int rr = r0 + r;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (rr < a.R) {
+        const int i = rr / a.G;
+        const int h = g * a.G + (rr - i * a.G);
+        v = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D)[ch];
+      }
+      qs[idx] = v;
+    }
+    qrows.lds = qs;  // published by the barrier before the first tile
   }
 
+  float *pbuf = smem + kBtCap + 4 + Lay::QLDS + w * (T * RP);
+  int *bt_lds = reinterpret_cast<int *>(smem);
   const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
-  const uint16_t *kbase = a.k + g * D;
-  const uint16_t *vbase = a.v + g * D;
-  const int pmask = (1 << a.page_shift) - 1;
-  float *pbuf = smem + w * (T * RP);
 
-  float m_run[RP], l_part[RP], acc[RP][8];
+  State<RP> st;
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    m_run[r] = -INFINITY;
-    l_part[r] = 0.f;
+    st.m[r] = -INFINITY;
+    st.l[r] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+    for (int e = 0; e < 8; ++e) st.acc[r][e] = 0.f;
   }
 
-  for (int t = w; t < ntiles; t += NW) {
-    const int base = kb + t * T;
-    // K rows, QK layout
-    uint4 kr[NPASS][4];
-#pragma unroll
-    for (int pp = 0; pp < NPASS; ++pp) {
-      const int j = base + pp * KPP + jq;
-      if (j < ke) {
-        const int page = bt_row[j >> a.page_shift];
-        const int64_t off = (int64_t)page * a.page_stride + (int64_t)(j & pmask) * a.row_stride;
-        const uint4 *src = reinterpret_cast<const uint4 *>(kbase + off);
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) kr[pp][c4] = src[qq + LPK * c4];
-      } else {
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) kr[pp][c4] = make_uint4(0u, 0u, 0u, 0u);
-      }
+  // ---- key windows whose pages fit the LDS page-table slice (one window
+  // unless the split spans more than kBtCap pages).  The first window's slice
+  // does not depend on kv_lens, so its load is issued with the q load.
+  const int win_keys = (kBtCap << a.page_shift) >= NW * T ? ((kBtCap << a.page_shift) / (NW * T)) * (NW * T)
+                                                         : NW * T;
+  const int cap_keys = a.max_pages << a.page_shift;
+  auto load_bt = [&](int from) {
+    int to = from + win_keys;
+    if (to > c.kb + a.chunk) to = c.kb + a.chunk;
+    if (to > cap_keys) to = cap_keys;
+    const int p0 = from >> a.page_shift;
+    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
+  };
+  load_bt(c.kb);
+  __syncthreads();
+  for (int wb = c.kb; wb < kend; wb += win_keys) {
+    const int we = wb + win_keys < kend ? wb + win_keys : kend;
+    if (wb != c.kb) {
+      __syncthreads();
+      load_bt(wb);
+      __syncthreads();
     }
-    // V rows, PV layout
-    uint4 vr[NSTEP];
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int j = base + st * KPV + kg;
-      if (j < ke) {
-        const int page = bt_row[j >> a.page_shift];
-        const int64_t off = (int64_t)page * a.page_stride + (int64_t)(j & pmask) * a.row_stride;
-        vr[st] = reinterpret_cast<const uint4 *>(vbase + off)[ds];
-      } else {
-        vr[st] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+    c.p0 = wb >> a.page_shift;
+    c.ke = we;
+    const int ntiles = (we - wb + T - 1) / T;
 
-    // scores
-    float sc[NPASS][RP];
-#pragma unroll
-    for (int pp = 0; pp < NPASS; ++pp) {
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        float d = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d = dot2_bf16(comp(kr[pp][c4], e), qr[r][4 * c4 + e], d);
-        sc[pp][r] = wave_sum_lo<Lay::LOG_LPK>(d);
-      }
+    // double-buffered tile loop: the next tile's loads fly during this compute
+    Tile<D, RP> ta, tb;
+    int t = w;
+    if (t < ntiles) load_tile(c, wb + t * T, ta);
+    for (; t < ntiles; t += 2 * NW) {
+      if (t + NW < ntiles) load_tile(c, wb + (t + NW) * T, tb);
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, st);
+      if (t + NW >= ntiles) break;
+      if (t + 2 * NW < ntiles) load_tile(c, wb + (t + 2 * NW) * T, ta);
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, st);
     }
-#pragma unroll
-    for (int pp = 0; pp < NPASS; ++pp) {
-      const int j = base + pp * KPP + jq;
-      const bool in = j < ke;
-      float mv[RP];
-#pragma unroll
-      for (int r = 0; r < RP; ++r) mv[r] = 0.f;
-      if (MASK && in) {
-        if (a.mask_sq == 0) {
-          const float m0 = a.mask[(int64_t)b * a.mask_sb + j] * kLog2e;
-#pragma unroll
-          for (int r = 0; r < RP; ++r) mv[r] = m0;
-        } else {
-#pragma unroll
-          for (int r = 0; r < RP; ++r) {
-            const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
-            mv[r] = a.mask[(int64_t)b * a.mask_sb + (int64_t)(rr / a.G) * a.mask_sq + j] * kLog2e;
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        const float v = sc[pp][r] * a.scale_log2 + mv[r];
-        const bool vis = CAUSAL ? (j < lim[r] && in) : (in && r0 + r < a.R);
-        sc[pp][r] = vis ? v : -INFINITY;
-      }
-    }
-
-    // online softmax update
-    float alpha[RP], mu[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      float mt = sc[0][r];
-#pragma unroll
-      for (int pp = 1; pp < NPASS; ++pp) mt = fmaxf(mt, sc[pp][r]);
-      mt = wave_max_hi<Lay::LOG_LPK>(mt);
-      const float mnew = fmaxf(m_run[r], mt);
-      const float use = mnew == -INFINITY ? 0.f : mnew;
-      alpha[r] = fast_exp2(m_run[r] - use);
-      m_run[r] = mnew;
-      mu[r] = use;
-    }
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      float lsum = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < NPASS; ++pp) {
-        const float pv = fast_exp2(sc[pp][r] - mu[r]);
-        lsum += pv;
-        if ((r % LPK) == qq) pbuf[(pp * KPP + jq) * RP + r] = pv;
-      }
-      l_part[r] = l_part[r] * alpha[r] + lsum;
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // PV
-#pragma unroll
-    for (int r = 0; r < RP; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[r][e] *= alpha[r];
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int key = st * KPV + kg;
-      float pr[RP];
-      if constexpr (RP >= 4) {
-#pragma unroll
-        for (int r4 = 0; r4 < RP / 4; ++r4) {
-          const float4 t4 = reinterpret_cast<const float4 *>(pbuf + key * RP)[r4];
-          pr[4 * r4 + 0] = t4.x;
-          pr[4 * r4 + 1] = t4.y;
-          pr[4 * r4 + 2] = t4.z;
-          pr[4 * r4 + 3] = t4.w;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < RP; ++r) pr[r] = pbuf[key * RP + r];
-      }
-      float vf[8];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t u = comp(vr[st], e2);
-        vf[2 * e2] = bf16_lo(u);
-        vf[2 * e2 + 1] = bf16_hi(u);
-      }
-#pragma unroll
-      for (int r = 0; r < RP; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 
   // ---- wave totals: l over QK key groups, acc over PV key groups
   float l_tot[RP];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) l_tot[r] = wave_sum_hi<Lay::LOG_LPK>(l_part[r]);
+  for (int r = 0; r < RP; ++r) l_tot[r] = reduce_hi_grouped<Lay::LOG_LPK, OpSum>(st.l[r]);
 #pragma unroll
   for (int r = 0; r < RP; ++r)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = wave_sum_hi<Lay::LOG_LPV>(acc[r][e]);
+    for (int e = 0; e < 8; ++e) st.acc[r][e] = reduce_hi<Lay::LOG_LPV, OpSum>(st.acc[r][e]);
 
   // ---- merge the waves through LDS and write
   __syncthreads();
   float *ob = smem;                    // [NW][RP][D]
   float *mlb = smem + NW * RP * D;     // [NW][RP][2]
-  if (kg == 0) {
+  if (c.kg == 0) {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      float4 *dst = reinterpret_cast<float4 *>(ob + (w * RP + r) * D + ds * 8);
-      dst[0] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-      dst[1] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+      float4 *dst = reinterpret_cast<float4 *>(ob + (w * RP + r) * D + c.ds * 8);
+      dst[0] = make_float4(st.acc[r][0], st.acc[r][1], st.acc[r][2], st.acc[r][3]);
+      dst[1] = make_float4(st.acc[r][4], st.acc[r][5], st.acc[r][6], st.acc[r][7]);
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      mlb[(w * RP + r) * 2] = m_run[r];
+      mlb[(w * RP + r) * 2] = st.m[r];
       mlb[(w * RP + r) * 2 + 1] = l_tot[r];
     }
   }
@@ -407,31 +596,54 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   }
 }
 
+// Combine: one wave per output row.  The split weights w_s = l_s exp(m_s - M)
+// are computed lane-parallel over the splits (M, sum w by DPP reductions in a
+// fixed order), parked in LDS, then the partial rows are accumulated in
+// split order with many loads in flight; empty splits (l_s = 0) are skipped.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float wsh[4][kMaxSplitsCombine];
+  const int wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
   constexpr int PER = (D + 63) / 64;
-  const float *ml = a.ml_part + row * a.S * 2;
-  const float *op = a.o_part + row * a.S * D;
+  const int S = a.S;
+  const float2 *ml = reinterpret_cast<const float2 *>(a.ml_part) + row * S;
+  const float *op = a.o_part + row * S * D;
+  constexpr int SPL = kMaxSplitsCombine / 64;  // splits per lane
+  float2 v[SPL];
   float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s)
-    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const int sidx = lane + 64 * k;
+    v[k] = sidx < S ? ml[sidx] : make_float2(-INFINITY, 0.f);
+    if (v[k].y > 0.f) M = fmaxf(M, v[k].x);
+  }
+  M = reduce_hi<0, OpMax>(M);
+  float W = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const float wk = v[k].y > 0.f ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
+      if (lane + 64 * k < S) wsh[wv][lane + 64 * k] = wk;
+      W += wk;
+    }
+    W = reduce_hi<0, OpSum>(W);
+  }
+  __builtin_amdgcn_wave_barrier();
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  float W = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.S; ++s) {
-      const float l = ml[2 * s + 1];
-      if (!(l > 0.f)) continue;
-      const float f = l * fast_exp2((ml[2 * s] - M) * kLog2e);
-      W += f;
+  if (W > 0.f) {
+#pragma unroll 8
+    for (int sidx = 0; sidx < S; ++sidx) {
+      const float f = wsh[wv][sidx];
+      if (f == 0.f) continue;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) o[k] = fmaf(f, op[s * D + d], o[k]);
+        if (d < D) o[k] = fmaf(f, op[sidx * D + d], o[k]);
       }
     }
   }

@@ -1,0 +1,447 @@
+// pkv_decode_mfma.hip -- split-KV paged decode kernel for CDNA4 (gfx950),
+// matrix-core path, used when the rows that share a kv head (G query heads x
+// q_len tokens) fill a 16-row MFMA tile.
+//
+// Method as in pkv_decode.hip (AstrAI commit d565d44, "attn_paged_decode.cu"
+// commit notes: the MMA split-KV paged decode kernel packs the query heads of
+// one kv head into tensor-core tiles and resolves the page table once per key
+// tile).  gfx950 mapping:
+//  * a workgroup covers up to 32 rows (two 16-row blocks) of one kv head and
+//    one key split; its kWavesPerBlock waves take 16-key tiles in turn and
+//    merge their (m, l, O) once at the end through LDS;
+//  * K and V tiles are fetched with full-row 128-bit loads into registers
+//    (double-buffered, so the next tile's loads fly during this tile's math)
+//    and written to a per-wave LDS slice with an XOR chunk swizzle;
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the K operand is a
+//    ds_read_b128 per lane, Q stays in registers; the S^T accumulator leaves
+//    each lane one query row and four keys, so the online-softmax max, exp
+//    and rescale are in-lane apart from two permlane swaps;
+//  * O^T = V^T P^T with v_mfma_f32_16x16x16_bf16: V^T comes straight from
+//    the row-major V tile through ds_read_b64_tr_b16 (the gfx950 transposing
+//    LDS read), P^T is the S^T register layout itself; P is split into a bf16
+//    high part and a bf16 remainder (two MFMAs) so the probabilities keep
+//    about 16 significant bits, and the row sums l use the fp32 values;
+//  * exclusion (tail, causal, -inf mask) is a select; scores are in base 2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBtCap = 1024;
+constexpr int KT = 16;  // keys per wave tile
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float xor16_max(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int D>
+struct MLay {
+  static constexpr int NW = kWavesPerBlock;
+  static constexpr int NCH = D / 8;          // 16-byte chunks per row
+  static constexpr int LPR = D / 8;          // lanes per row in a coalesced load
+  static constexpr int RPI = 64 / LPR;       // rows per load instruction
+  static constexpr int NLD = KT / RPI;       // load instructions per 16-key tile (K or V)
+  static constexpr int TILE_ELEMS = KT * D;  // bf16 per K (or V) tile
+  static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
+  static constexpr int BT_BYTES = (kBtCap + 4) * 4;
+  static constexpr int MERGE_BYTES = NW * 16 * D * 4 + NW * 32 * 2 * 4;
+  static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
+  static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+  // swizzles (16-byte chunk index within a row)
+  __device__ static int swk(int ch, int row) { return ch ^ (row & (NCH - 1)); }
+  __device__ static int swv(int ch, int row) { return ch ^ ((2 * row) & (NCH - 2)); }
+};
+
+template <int D>
+struct MTile {
+  uint4 k[MLay<D>::NLD];
+  uint4 v[MLay<D>::NLD];
+};
+
+struct MCtx {
+  const uint16_t *kbase, *vbase;
+  const int *bt;
+  int p0, page_shift, pmask;
+  int64_t page_stride;
+  int row_stride;
+  int ke;
+};
+
+template <int D>
+__device__ __forceinline__ void mload(const MCtx &c, int base, int lane, MTile<D> &t) {
+  using L = MLay<D>;
+  const int ch = lane % L::LPR;
+#pragma unroll
+  for (int ii = 0; ii < L::NLD; ++ii) {
+    const int j = base + ii * L::RPI + lane / L::LPR;
+    if (j < c.ke) {
+      const int page = c.bt[(j >> c.page_shift) - c.p0];
+      const int64_t off = (int64_t)page * c.page_stride + (int64_t)(j & c.pmask) * c.row_stride;
+      t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(c.kbase + off) + ch);
+      t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + off) + ch);
+    } else {
+      t.k[ii] = make_uint4(0u, 0u, 0u, 0u);
+      t.v[ii] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+template <int D, int NRB>
+struct MState {
+  float m[NRB];           // running max of this lane's row (base 2), equal across its 4 lanes
+  float l[NRB];           // this lane's share of the row sum
+  f32x4_t o[NRB][D / 16]; // O^T: d = 16*nb + 4q + i, row c
+};
+
+template <int D, int NRB, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int base, const MTile<D> &t,
+                                         const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB], int b,
+                                         int r0, uint16_t *kt, uint16_t *vt, int lane, MState<D, NRB> &st) {
+  using L = MLay<D>;
+  const int cc = lane & 15;
+  const int q = lane >> 4;
+  // tile -> LDS (swizzled rows)
+#pragma unroll
+  for (int ii = 0; ii < L::NLD; ++ii) {
+    const int row = ii * L::RPI + lane / L::LPR;
+    const int ch = lane % L::LPR;
+    reinterpret_cast<uint4 *>(kt + row * D)[L::swk(ch, row)] = t.k[ii];
+    reinterpret_cast<uint4 *>(vt + row * D)[L::swv(ch, row)] = t.v[ii];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // S^T[key][row] = K Q^T : A = K[key cc][d 32s+8q..], B = Q^T
+  f32x4_t s4[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) s4[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int stp = 0; stp < D / 32; ++stp) {
+    const uint4 kv = reinterpret_cast<const uint4 *>(kt + cc * D)[L::swk(4 * stp + q, cc)];
+    const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kv);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      s4[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, __builtin_bit_cast(bf16x8_t, qb[rb][stp]), s4[rb], 0, 0, 0);
+  }
+
+  // scale, mask, visibility; lane holds keys base+4q+i of row r0+cc+16rb
+  float mk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = base + 4 * q + i;
+    if (MASK && j < c.ke && a.mask_sq == 0) mk[i] = a.mask[(int64_t)b * a.mask_sb + j] * kLog2e;
+  }
+  float alpha[NRB];
+  bf16x4_t ph[NRB], pl[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float sv[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = base + 4 * q + i;
+      float mv = mk[i];
+      if (MASK && a.mask_sq != 0 && j < c.ke) {
+        const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
+        mv = a.mask[(int64_t)b * a.mask_sb + (int64_t)(rr / a.G) * a.mask_sq + j] * kLog2e;
+      }
+      const float v = fmaf(s4[rb][i], a.scale_log2, mv);
+      const bool vis = j < c.ke && j < lim[rb];
+      sv[i] = vis ? v : -INFINITY;
+      mt = fmaxf(mt, sv[i]);
+    }
+    mt = xor32_max(xor16_max(mt));
+    const float mnew = fmaxf(st.m[rb], mt);
+    const float use = mnew == -INFINITY ? 0.f : mnew;
+    alpha[rb] = fast_exp2(st.m[rb] - use);
+    st.m[rb] = mnew;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(sv[i] - use);
+      lsum += p;
+      const uint16_t hb = f32_to_bf16_rne(p);
+      const float rem = p - bf16_bits_to_f32(hb);
+      ph[rb][i] = __builtin_bit_cast(__bf16, hb);
+      pl[rb][i] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(rem));
+    }
+    st.l[rb] = fmaf(st.l[rb], alpha[rb], lsum);
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] *= alpha[rb];
+  }
+
+  // O^T[d][row] += V^T P^T : A = V^T via the transposing LDS read
+  const int srow = 4 * q + (cc >> 2);      // V row this lane addresses for the transposing read
+  const int sd = 4 * (cc & 3);             // its d offset within the 16-column block
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    const int d0 = 16 * nb + sd;
+    const int ch = d0 >> 3;
+    const int half = (d0 >> 2) & 1;
+    // vt points into LDS: the C cast is an address-space cast to the LDS offset
+    lds_i16x4_t *src = (lds_i16x4_t *)(reinterpret_cast<char *>(vt) + srow * D * 2 + L::swv(ch, srow) * 16 +
+                                       half * 8);
+    const i16x4_t vraw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);
+    const bf16x4_t va = __builtin_bit_cast(bf16x4_t, vraw);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      st.o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[rb], st.o[rb][nb], 0, 0, 0);
+      st.o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[rb], st.o[rb][nb], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int NRB, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_mfma(const DecodeArgs a) {
+  using L = MLay<D>;
+  constexpr int NW = L::NW;
+  constexpr int RW = 16 * NRB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[L::SMEM_BYTES];
+
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int slot = x >> 3;
+  const int inner_idx = slot % a.inner;
+  const int outer_idx = (slot / a.inner) * 8 + xcd;
+  if (outer_idx >= a.outer) return;
+  const int b = outer_idx / a.S;
+  const int s = outer_idx - b * a.S;
+  const int g = inner_idx / a.nrb;
+  const int rg = inner_idx - g * a.nrb;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int cc = lane & 15;
+  const int q = lane >> 4;
+  const int r0 = rg * RW;
+
+  const int kvlen = a.kv_lens[b];
+  int cofs = -1;
+  if (CAUSAL) cofs = a.causal_offsets ? a.causal_offsets[b] : a.causal_offset;
+  auto row_limit = [&](int rr) -> int {
+    if (rr >= a.R) return 0;
+    int lr = kvlen;
+    if (CAUSAL && cofs >= 0) {
+      const int64_t cl = (int64_t)cofs + rr / a.G + 1;
+      if (cl < lr) lr = (int)cl;
+    }
+    return lr;
+  };
+  int lim[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) lim[rb] = row_limit(r0 + cc + 16 * rb);
+  const int rlast = (r0 + RW < a.R ? r0 + RW : a.R) - 1;
+  const int kmax = row_limit(rlast);   // the last row sees the most keys
+
+  int *bt_lds = reinterpret_cast<int *>(smem_raw);
+  uint16_t *kt = reinterpret_cast<uint16_t *>(smem_raw + L::BT_BYTES + w * L::WAVE_LDS);
+  uint16_t *vt = kt + L::TILE_ELEMS;
+
+  MCtx c;
+  c.kbase = a.k + g * D;
+  c.vbase = a.v + g * D;
+  c.bt = bt_lds;
+  c.page_shift = a.page_shift;
+  c.pmask = (1 << a.page_shift) - 1;
+  c.page_stride = a.page_stride;
+  c.row_stride = a.row_stride;
+  const int kb = s * a.chunk;
+  int kend = kb + a.chunk;
+  if (kend > kmax) kend = kmax;
+
+  // q operand: lane supplies Q[row cc+16rb][d 32*stp + 8q .. +8]
+  uint4 qb[NRB][D / 32];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int rr = r0 + cc + 16 * rb;
+    if (rr < a.R) {
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
+#pragma unroll
+      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
+    } else {
+#pragma unroll
+      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
+  const int win_keys = ((kBtCap << a.page_shift) / (NW * KT)) * (NW * KT);
+  const int cap_keys = a.max_pages << a.page_shift;
+  auto load_bt = [&](int from) {
+    int to = from + win_keys;
+    if (to > kb + a.chunk) to = kb + a.chunk;
+    if (to > cap_keys) to = cap_keys;
+    const int p0 = from >> a.page_shift;
+    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
+  };
+
+  MState<D, NRB> st;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    st.m[rb] = -INFINITY;
+    st.l[rb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  load_bt(kb);
+  __syncthreads();
+  for (int wb = kb; wb < kend; wb += win_keys) {
+    const int we = wb + win_keys < kend ? wb + win_keys : kend;
+    if (wb != kb) {
+      __syncthreads();
+      load_bt(wb);
+      __syncthreads();
+    }
+    c.p0 = wb >> a.page_shift;
+    c.ke = we;
+    const int ntiles = (we - wb + KT - 1) / KT;
+    MTile<D> ta, tb;
+    int t = w;
+    if (t < ntiles) mload<D>(c, wb + t * KT, lane, ta);
+    for (; t < ntiles; t += 2 * NW) {
+      if (t + NW < ntiles) mload<D>(c, wb + (t + NW) * KT, lane, tb);
+      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + t * KT, ta, qb, lim, b, r0, kt, vt, lane, st);
+      if (t + NW >= ntiles) break;
+      if (t + 2 * NW < ntiles) mload<D>(c, wb + (t + 2 * NW) * KT, lane, ta);
+      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + (t + NW) * KT, tb, qb, lim, b, r0, kt, vt, lane, st);
+    }
+  }
+
+  // row sums over the four lanes of each row
+  float ltot[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) ltot[rb] = xor32_sum(xor16_sum(st.l[rb]));
+
+  // merge the waves, one 16-row block at a time
+  float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][D]
+  float *mlb = ob + NW * 16 * D;                          // [NW][32][2]
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      // lane holds O^T[d = 16nb + 4q + i][row cc]
+      float4 *dst = reinterpret_cast<float4 *>(ob + (w * 16 + cc) * D + 16 * nb + 4 * q);
+      dst[0] = make_float4(st.o[rb][nb][0], st.o[rb][nb][1], st.o[rb][nb][2], st.o[rb][nb][3]);
+    }
+    if (q == 0) {
+      mlb[(w * 32 + cc + 16 * rb) * 2] = st.m[rb];
+      mlb[(w * 32 + cc + 16 * rb) * 2 + 1] = ltot[rb];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D; idx += NW * 64) {
+      const int r = idx / D;
+      const int d = idx - r * D;
+      const int rr = r0 + 16 * rb + r;
+      if (rr >= a.R) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww)
+        if (mlb[(ww * 32 + 16 * rb + r) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(ww * 32 + 16 * rb + r) * 2]);
+      float W = 0.f, o = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float lw = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
+          if (lw > 0.f) {
+            const float f = fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M);
+            W = fmaf(f, lw, W);
+            o = fmaf(f, ob[(ww * 16 + r) * D + d], o);
+          }
+        }
+      }
+      const float res = W > 0.f ? o / W : 0.f;
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      const int64_t row = ((int64_t)b * a.q_len + i) * a.Hq + h;
+      if (!a.partials) {
+        a.out[row * D + d] = f32_to_bf16_rne(res);
+        if (a.out_f32) a.out_f32[row * D + d] = res;
+      } else {
+        a.o_part[(row * a.S + s) * D + d] = res;
+        if (d == 0) {
+          a.ml_part[(row * a.S + s) * 2] = W > 0.f ? M * kLn2 : -INFINITY;
+          a.ml_part[(row * a.S + s) * 2 + 1] = W;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int NRB, bool C, bool M>
+hipError_t mlaunch_t(const DecodeArgs &a, hipStream_t stream) {
+  const int64_t outer_pad = ((int64_t)a.outer + 7) / 8 * 8;
+  const int64_t grid = outer_pad * a.inner;
+  hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int NRB>
+hipError_t mlaunch_nrb(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
+  if (causal) return mask ? mlaunch_t<D, NRB, true, true>(a, s) : mlaunch_t<D, NRB, true, false>(a, s);
+  return mask ? mlaunch_t<D, NRB, false, true>(a, s) : mlaunch_t<D, NRB, false, false>(a, s);
+}
+
+template <int D>
+hipError_t mlaunch_d(const DecodeArgs &a, int nrb16, bool causal, bool mask, hipStream_t s) {
+  return nrb16 == 1 ? mlaunch_nrb<D, 1>(a, causal, mask, s) : mlaunch_nrb<D, 2>(a, causal, mask, s);
+}
+
+}  // namespace
+
+int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
+                      hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return mlaunch_d<32>(a, nrb16, causal, has_mask, stream);
+    case 64: return mlaunch_d<64>(a, nrb16, causal, has_mask, stream);
+    case 128: return mlaunch_d<128>(a, nrb16, causal, has_mask, stream);
+    default: return mlaunch_d<256>(a, nrb16, causal, has_mask, stream);
+  }
+}
+
+}  // namespace pkv

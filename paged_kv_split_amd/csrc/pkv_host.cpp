@@ -241,7 +241,10 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
 int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stream) {
   const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0;
   (void)hipGetLastError();
-  int err = pkv::launch_split(a, p->head_dim, pkv::rows_per_block(a.R), causal, a.mask != nullptr, stream);
+  const int rows = pkv::rows_per_block(a.R);
+  int err = pkv::use_mfma(a.R)
+                ? pkv::launch_split_mfma(a, p->head_dim, rows / 16, causal, a.mask != nullptr, stream)
+                : pkv::launch_split(a, p->head_dim, rows, causal, a.mask != nullptr, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

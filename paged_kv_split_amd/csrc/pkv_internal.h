@@ -46,15 +46,19 @@ struct CombineArgs {
   int32_t S;
 };
 
-// Which split kernel serves a problem: rows packed per workgroup and keys
-// per wave tile for a head dim.
-int rows_per_block(int R);         // padded rows RP in {1, 2, 4, 8}
-int tile_keys(int head_dim);       // keys per wave tile T
+// Which split kernel serves a problem.  R = G * q_len rows share a kv head:
+// R <= 8 runs on the VALU kernel with R padded to RP in {1, 2, 4, 8}; larger
+// R fills 16-row matrix-core tiles (one or two per workgroup).
+inline bool use_mfma(int R) { return R > 8; }
+int rows_per_block(int R);         // rows per workgroup: RP (VALU) or 16/32 (MFMA)
+int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
 
 // Launchers (return a hipError_t value).
 int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
                  bool has_mask, hipStream_t stream);
+int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
+                      hipStream_t stream);
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

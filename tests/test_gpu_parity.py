@@ -70,13 +70,20 @@ SMALL = [
     dict(B=2, q_len=1, Hq=64, Hkv=8, D=128, page_size=64, kv_lens=[700, 33]),
     dict(B=2, q_len=1, Hq=16, Hkv=2, D=256, page_size=32, kv_lens=[257, 130]),
     dict(B=4, q_len=1, Hq=24, Hkv=4, D=64, page_size=32, kv_lens=[128, 129, 2047, 5]),   # G=6
-    dict(B=2, q_len=3, Hq=6, Hkv=2, D=128, page_size=8, kv_lens=[100, 41], causal="last"),  # R=9: 2 row blocks
+    dict(B=2, q_len=3, Hq=6, Hkv=2, D=128, page_size=8, kv_lens=[100, 41], causal="last"),  # R=9: one 16-row MFMA block
     dict(B=2, q_len=4, Hq=64, Hkv=8, D=128, page_size=32, kv_lens=[300, 64], causal="last"),  # R=32
     dict(B=2, q_len=2, Hq=4, Hkv=1, D=32, page_size=1, kv_lens=[77, 5], causal=70),
     dict(B=2, q_len=1, Hq=2, Hkv=2, D=64, page_size=256, kv_lens=[600, 1]),
     dict(B=3, q_len=2, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[200, 90, 13], mask="3d"),
     dict(B=3, q_len=1, Hq=16, Hkv=4, D=128, page_size=32, kv_lens=[400, 333, 1], mask="2d", mask_p=0.5),
     dict(B=2, q_len=1, Hq=8, Hkv=1, D=256, page_size=64, kv_lens=[1000, 999], outlier_p=0.05),
+    # rows that fill matrix-core tiles (R = G * q_len > 8)
+    dict(B=2, q_len=2, Hq=8, Hkv=1, D=64, page_size=16, kv_lens=[300, 17]),                   # R=16
+    dict(B=2, q_len=3, Hq=16, Hkv=1, D=128, page_size=32, kv_lens=[333, 70], causal="last"),  # R=48
+    dict(B=2, q_len=1, Hq=32, Hkv=2, D=256, page_size=32, kv_lens=[500, 64]),                 # R=16, D=256
+    dict(B=2, q_len=4, Hq=16, Hkv=4, D=32, page_size=8, kv_lens=[200, 5], mask="3d", causal="last"),
+    dict(B=1, q_len=2, Hq=64, Hkv=4, D=128, page_size=64, kv_lens=[777], mask="2d", mask_p=0.3),  # R=32
+    dict(B=3, q_len=1, Hq=24, Hkv=2, D=64, page_size=32, kv_lens=[90, 1, 0], outlier_p=0.05),  # R=12
 ]
 
 
