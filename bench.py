@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--runs", type=int, default=5, help="timed repetitions (median reported)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +114,15 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}), flush=True)
+        return
     w = make_workload(args.workload)
     print(f"bench: workload {w.name} built on host", file=sys.stderr, flush=True)
 
@@ -212,7 +224,7 @@ def main():
         comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if S > 1 else 0.0
         return total, split_ms, comb_ms
 
-    runs = [timed(True) for _ in range(5)]
+    runs = [timed(True) for _ in range(max(1, args.runs))]
     total_ms = statistics.median(r[0] for r in runs)
     split_ms = statistics.median(r[1] for r in runs)
     comb_ms = statistics.median(r[2] for r in runs)

@@ -59,6 +59,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBtCap = 1024;  // page-table entries staged in LDS per window
 constexpr int kMaxSplitsCombine = 256;  // = PKV_MAX_SPLITS
+constexpr float kRescaleLog2 = 8.f;     // lazy-rescale threshold (base-2 score units)
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -81,7 +82,7 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 // ---- cross-lane primitives (DPP / permlane; semantics checked on gfx950) ----
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
@@ -193,10 +194,11 @@ struct Ctx {
   int jq, qq, kg, ds;
 };
 
-template <int D, int RP>
+template <int D, int RP, bool MASK>
 struct Tile {
   uint4 k[Layout<D, RP>::NPASS][4];
   uint4 v[Layout<D, RP>::NSTEP];
+  float mk[MASK ? Layout<D, RP>::NPASS : 1][MASK ? RP : 1];  // additive mask (log2 units) of this lane's key
 };
 
 template <int D, int RP>
@@ -206,28 +208,67 @@ __device__ __forceinline__ int64_t row_offset(const Ctx<D, RP> &c, int j) {
 }
 
 // Issue the loads of tile `base` (keys base .. base+T-1) into registers.
-template <int D, int RP>
-__device__ __forceinline__ void load_tile(const Ctx<D, RP> &c, int base, Tile<D, RP> &t) {
+// Rows past the end are clamped to the last valid key: they load finite
+// data that the score mask gives zero weight, so no lane branches and no
+// register is zero-filled.  When a page holds at least one tile, the tile's
+// page is wave-uniform and resolved once, in scalar registers.
+template <int D, int RP, bool MASK>
+__device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int base,
+                                          Tile<D, RP, MASK> &t) {
   using Lay = Layout<D, RP>;
+  const int jlast = c.ke - 1;
+  if constexpr (MASK) {
 #pragma unroll
-  for (int pp = 0; pp < Lay::NPASS; ++pp) {
-    const int j = base + pp * Lay::KPP + c.jq;
-    if (j < c.ke) {
+    for (int pp = 0; pp < Lay::NPASS; ++pp) {
+      int j = base + pp * Lay::KPP + c.jq;
+      j = j < jlast ? j : jlast;
+      const float *mrow = a.mask + (int64_t)b * a.mask_sb + j;
+      if (a.mask_sq == 0) {
+        const float m0 = *mrow;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) t.mk[pp][r] = m0;
+      } else {
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
+          t.mk[pp][r] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
+        }
+      }
+    }
+  }
+  if (c.page_shift >= ilog2c(Lay::T)) {
+    const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
+    const int64_t pofs = (int64_t)page * c.page_stride;
+    const uint16_t *kp = c.kbase + pofs;
+    const uint16_t *vp = c.vbase + pofs;
+#pragma unroll
+    for (int pp = 0; pp < Lay::NPASS; ++pp) {
+      int j = base + pp * Lay::KPP + c.jq;
+      j = j < jlast ? j : jlast;
+      const uint4 *src = reinterpret_cast<const uint4 *>(kp + (uint32_t)((j & c.pmask) * c.row_stride));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = load_stream(src + c.qq + Lay::LPK * c4);
+    }
+#pragma unroll
+    for (int st = 0; st < Lay::NSTEP; ++st) {
+      int j = base + st * Lay::KPV + c.kg;
+      j = j < jlast ? j : jlast;
+      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + (uint32_t)((j & c.pmask) * c.row_stride)) + c.ds);
+    }
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < Lay::NPASS; ++pp) {
+      int j = base + pp * Lay::KPP + c.jq;
+      j = j < jlast ? j : jlast;
       const uint4 *src = reinterpret_cast<const uint4 *>(c.kbase + row_offset(c, j));
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = load_stream(src + c.qq + Lay::LPK * c4);
-    } else {
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = make_uint4(0u, 0u, 0u, 0u);
     }
-  }
 #pragma unroll
-  for (int st = 0; st < Lay::NSTEP; ++st) {
-    const int j = base + st * Lay::KPV + c.kg;
-    if (j < c.ke) {
+    for (int st = 0; st < Lay::NSTEP; ++st) {
+      int j = base + st * Lay::KPV + c.kg;
+      j = j < jlast ? j : jlast;
       t.v[st] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + row_offset(c, j)) + c.ds);
-    } else {
-      t.v[st] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
@@ -258,7 +299,7 @@ struct QRows<D, RP, false> {
 
 template <int D, int RP, bool CAUSAL, bool MASK, class Q>
 __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int base,
-                                             const Tile<D, RP> &t, const Q &qrows,
+                                             const Tile<D, RP, MASK> &t, const Q &qrows,
                                              const int (&lim)[RP], int b, int r0, float *pbuf,
                                              State<RP> &st) {
   using Lay = Layout<D, RP>;
@@ -290,61 +331,53 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
   for (int pp = 0; pp < NPASS; ++pp) {
     const int j = base + pp * KPP + c.jq;
     const bool in = j < c.ke;
-    float mv[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) mv[r] = 0.f;
-    if (MASK && in) {
-      if (a.mask_sq == 0) {
-        const float m0 = a.mask[(int64_t)b * a.mask_sb + j] * kLog2e;
-#pragma unroll
-        for (int r = 0; r < RP; ++r) mv[r] = m0;
-      } else {
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-          const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
-          mv[r] = a.mask[(int64_t)b * a.mask_sb + (int64_t)(rr / a.G) * a.mask_sq + j] * kLog2e;
-        }
-      }
-    }
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      const float v = fmaf(sc[pp][r], a.scale_log2, mv[r]);
+      const float v = MASK ? fmaf(sc[pp][r], a.scale_log2, t.mk[pp][r] * kLog2e) : sc[pp][r] * a.scale_log2;
       const bool vis = CAUSAL ? (in && j < lim[r]) : (in && lim[r] > 0);
       sc[pp][r] = vis ? v : -INFINITY;
     }
   }
-  // online softmax update (m uniform across the wave)
-  float alpha[RP], mu[RP];
+  // online softmax with a lazy reference: the running reference m only moves
+  // (and the accumulators are rescaled) when a score exceeds it by more than
+  // kRescaleLog2; otherwise p = 2^(s - m) <= 2^kRescaleLog2, which fp32 holds
+  // with room to spare.  m is uniform across the wave, so the branch is too.
+  float dmax = -INFINITY;   // NaN (-inf - -inf) is ignored by fmaxf
 #pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    float mt = sc[0][r];
+  for (int r = 0; r < RP; ++r)
 #pragma unroll
-    for (int pp = 1; pp < NPASS; ++pp) mt = fmaxf(mt, sc[pp][r]);
-    mt = reduce_hi_grouped<Lay::LOG_LPK, OpMax>(mt);
-    const float mnew = fmaxf(st.m[r], mt);
-    const float use = mnew == -INFINITY ? 0.f : mnew;
-    alpha[r] = fast_exp2(st.m[r] - use);
-    st.m[r] = mnew;
-    mu[r] = use;
+    for (int pp = 0; pp < NPASS; ++pp) dmax = fmaxf(dmax, sc[pp][r] - st.m[r]);
+  const bool above = dmax > kRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(above) != 0) {
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      float mt = sc[0][r];
+#pragma unroll
+      for (int pp = 1; pp < NPASS; ++pp) mt = fmaxf(mt, sc[pp][r]);
+      mt = reduce_hi_grouped<Lay::LOG_LPK, OpMax>(mt);
+      const float mnew = fmaxf(st.m[r], mt);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(st.m[r] - mnew);
+      st.m[r] = mnew;
+      st.l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[r][e] *= alpha;
+    }
   }
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
+    const float use = st.m[r] == -INFINITY ? 0.f : st.m[r];
     float lsum = 0.f;
 #pragma unroll
     for (int pp = 0; pp < NPASS; ++pp) {
-      const float pv = fast_exp2(sc[pp][r] - mu[r]);
+      const float pv = fast_exp2(sc[pp][r] - use);
       lsum += pv;
-      if ((r & (LPK - 1)) == c.qq) pbuf[(pp * KPP + c.jq) * RP + r] = pv;
+      pbuf[(pp * KPP + c.jq) * RP + r] = pv;   // the LPK lanes of a key store the same value
     }
-    st.l[r] = fmaf(st.l[r], alpha[r], lsum);
+    st.l[r] += lsum;
   }
   __builtin_amdgcn_wave_barrier();
 
   // PV
-#pragma unroll
-  for (int r = 0; r < RP; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[r][e] *= alpha[r];
 #pragma unroll
   for (int s2 = 0; s2 < Lay::NSTEP; ++s2) {
     const int key = s2 * Lay::KPV + c.kg;
@@ -517,14 +550,14 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     const int ntiles = (we - wb + T - 1) / T;
 
     // double-buffered tile loop: the next tile's loads fly during this compute
-    Tile<D, RP> ta, tb;
+    Tile<D, RP, MASK> ta, tb;
     int t = w;
-    if (t < ntiles) load_tile(c, wb + t * T, ta);
+    if (t < ntiles) load_tile(a, c, b, r0, wb + t * T, ta);
     for (; t < ntiles; t += 2 * NW) {
-      if (t + NW < ntiles) load_tile(c, wb + (t + NW) * T, tb);
+      if (t + NW < ntiles) load_tile(a, c, b, r0, wb + (t + NW) * T, tb);
       compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, st);
       if (t + NW >= ntiles) break;
-      if (t + 2 * NW < ntiles) load_tile(c, wb + (t + 2 * NW) * T, ta);
+      if (t + 2 * NW < ntiles) load_tile(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
       compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, st);
     }
   }

@@ -40,6 +40,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBtCap = 1024;
 constexpr int KT = 16;  // keys per wave tile
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (base-2 score units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -92,10 +93,11 @@ struct MLay {
   __device__ static int swv(int ch, int row) { return ch ^ ((2 * row) & (NCH - 2)); }
 };
 
-template <int D>
+template <int D, int NRB, bool MASK>
 struct MTile {
   uint4 k[MLay<D>::NLD];
   uint4 v[MLay<D>::NLD];
+  float mk[MASK ? NRB : 1][4];  // additive mask of this lane's 4 keys (per row block for 3D masks)
 };
 
 struct MCtx {
@@ -107,21 +109,58 @@ struct MCtx {
   int ke;
 };
 
-template <int D>
-__device__ __forceinline__ void mload(const MCtx &c, int base, int lane, MTile<D> &t) {
+// Loads of one 16-key tile: full K/V rows, 128 bits per lane.  Rows past the
+// end are clamped to the last valid key (finite data, zero weight); when a
+// page holds the whole tile its page is resolved once, in scalar registers.
+template <int D, int NRB, bool MASK>
+__device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b, int r0, int base, int lane,
+                                      MTile<D, NRB, MASK> &t) {
   using L = MLay<D>;
   const int ch = lane % L::LPR;
+  const int jlast = c.ke - 1;
+  if (c.page_shift >= 4) {
+    const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
+    const int64_t pofs = (int64_t)page * c.page_stride;
+    const uint16_t *kp = c.kbase + pofs;
+    const uint16_t *vp = c.vbase + pofs;
 #pragma unroll
-  for (int ii = 0; ii < L::NLD; ++ii) {
-    const int j = base + ii * L::RPI + lane / L::LPR;
-    if (j < c.ke) {
+    for (int ii = 0; ii < L::NLD; ++ii) {
+      int j = base + ii * L::RPI + lane / L::LPR;
+      j = j < jlast ? j : jlast;
+      const uint32_t off = (uint32_t)((j & c.pmask) * c.row_stride);
+      t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + ch);
+      t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + ch);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < L::NLD; ++ii) {
+      int j = base + ii * L::RPI + lane / L::LPR;
+      j = j < jlast ? j : jlast;
       const int page = c.bt[(j >> c.page_shift) - c.p0];
       const int64_t off = (int64_t)page * c.page_stride + (int64_t)(j & c.pmask) * c.row_stride;
       t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(c.kbase + off) + ch);
       t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + off) + ch);
-    } else {
-      t.k[ii] = make_uint4(0u, 0u, 0u, 0u);
-      t.v[ii] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if constexpr (MASK) {
+    const int q = lane >> 4;
+    const int cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int j = base + 4 * q + i;
+      j = j < jlast ? j : jlast;
+      const float *mrow = a.mask + (int64_t)b * a.mask_sb + j;
+      if (a.mask_sq == 0) {
+        const float m0 = *mrow;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) t.mk[rb][i] = m0;
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
+          t.mk[rb][i] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
+        }
+      }
     }
   }
 }
@@ -133,14 +172,10 @@ struct MState {
   f32x4_t o[NRB][D / 16]; // O^T: d = 16*nb + 4q + i, row c
 };
 
-template <int D, int NRB, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int base, const MTile<D> &t,
-                                         const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB], int b,
-                                         int r0, uint16_t *kt, uint16_t *vt, int lane, MState<D, NRB> &st) {
+// Registers of one tile -> the wave's LDS slice (rows XOR-swizzled by chunk).
+template <int D, int NRB, bool MASK>
+__device__ __forceinline__ void mstore(const MTile<D, NRB, MASK> &t, uint16_t *kt, uint16_t *vt, int lane) {
   using L = MLay<D>;
-  const int cc = lane & 15;
-  const int q = lane >> 4;
-  // tile -> LDS (swizzled rows)
 #pragma unroll
   for (int ii = 0; ii < L::NLD; ++ii) {
     const int row = ii * L::RPI + lane / L::LPR;
@@ -149,7 +184,17 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
     reinterpret_cast<uint4 *>(vt + row * D)[L::swv(ch, row)] = t.v[ii];
   }
   __builtin_amdgcn_wave_barrier();
+}
 
+template <int D, int NRB, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int base,
+                                         const float (&mk)[MASK ? NRB : 1][4],
+                                         const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB], int b,
+                                         int r0, const uint16_t *kt, const uint16_t *vt, int lane,
+                                         MState<D, NRB> &st) {
+  using L = MLay<D>;
+  const int cc = lane & 15;
+  const int q = lane >> 4;
   // S^T[key][row] = K Q^T : A = K[key cc][d 32s+8q..], B = Q^T
   f32x4_t s4[NRB];
 #pragma unroll
@@ -164,49 +209,47 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
   }
 
   // scale, mask, visibility; lane holds keys base+4q+i of row r0+cc+16rb
-  float mk[4] = {0.f, 0.f, 0.f, 0.f};
+  float sv[NRB][4];
+  float dmax = -INFINITY;   // NaN (-inf - -inf) is ignored by fmaxf
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = base + 4 * q + i;
-    if (MASK && j < c.ke && a.mask_sq == 0) mk[i] = a.mask[(int64_t)b * a.mask_sb + j] * kLog2e;
-  }
-  float alpha[NRB];
-  bf16x4_t ph[NRB], pl[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    float sv[4];
-    float mt = -INFINITY;
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = base + 4 * q + i;
-      float mv = mk[i];
-      if (MASK && a.mask_sq != 0 && j < c.ke) {
-        const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
-        mv = a.mask[(int64_t)b * a.mask_sb + (int64_t)(rr / a.G) * a.mask_sq + j] * kLog2e;
-      }
-      const float v = fmaf(s4[rb][i], a.scale_log2, mv);
-      const bool vis = j < c.ke && j < lim[rb];
-      sv[i] = vis ? v : -INFINITY;
-      mt = fmaxf(mt, sv[i]);
+      const float v = MASK ? fmaf(s4[rb][i], a.scale_log2, mk[rb][i] * kLog2e) : s4[rb][i] * a.scale_log2;
+      sv[rb][i] = (j < c.ke && j < lim[rb]) ? v : -INFINITY;
+      dmax = fmaxf(dmax, sv[rb][i] - st.m[rb]);
     }
-    mt = xor32_max(xor16_max(mt));
-    const float mnew = fmaxf(st.m[rb], mt);
-    const float use = mnew == -INFINITY ? 0.f : mnew;
-    alpha[rb] = fast_exp2(st.m[rb] - use);
-    st.m[rb] = mnew;
+  // lazy reference max: move it (and rescale O, l) only when a score exceeds
+  // it by more than kRescaleLog2; the branch is wave-uniform
+  if (__builtin_amdgcn_ballot_w64(dmax > kRescaleLog2) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float mt = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
+      mt = xor32_max(xor16_max(mt));
+      const float mnew = fmaxf(st.m[rb], mt);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(st.m[rb] - mnew);
+      st.m[rb] = mnew;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] *= alpha;
+    }
+  }
+  bf16x4_t ph[NRB], pl[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float use = st.m[rb] == -INFINITY ? 0.f : st.m[rb];
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(sv[i] - use);
+      const float p = fast_exp2(sv[rb][i] - use);
       lsum += p;
       const uint16_t hb = f32_to_bf16_rne(p);
       const float rem = p - bf16_bits_to_f32(hb);
       ph[rb][i] = __builtin_bit_cast(__bf16, hb);
       pl[rb][i] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(rem));
     }
-    st.l[rb] = fmaf(st.l[rb], alpha[rb], lsum);
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] *= alpha[rb];
+    st.l[rb] += lsum;
   }
 
   // O^T[d][row] += V^T P^T : A = V^T via the transposing LDS read
@@ -218,7 +261,7 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
     const int ch = d0 >> 3;
     const int half = (d0 >> 2) & 1;
     // vt points into LDS: the C cast is an address-space cast to the LDS offset
-    lds_i16x4_t *src = (lds_i16x4_t *)(reinterpret_cast<char *>(vt) + srow * D * 2 + L::swv(ch, srow) * 16 +
+    lds_i16x4_t *src = (lds_i16x4_t *)(reinterpret_cast<const char *>(vt) + srow * D * 2 + L::swv(ch, srow) * 16 +
                                        half * 8);
     const i16x4_t vraw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);
     const bf16x4_t va = __builtin_bit_cast(bf16x4_t, vraw);
@@ -231,8 +274,13 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
   __builtin_amdgcn_wave_barrier();
 }
 
+// Two resident workgroups per CU (2 waves per SIMD) where the registers allow.
+template <int D, int NRB>
+constexpr int mfma_min_blocks() { return (D >= 256 && NRB == 2) ? 1 : 2; }
+
 template <int D, int NRB, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_mfma(const DecodeArgs a) {
+__global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) void split_decode_mfma(
+    const DecodeArgs a) {
   using L = MLay<D>;
   constexpr int NW = L::NW;
   constexpr int RW = 16 * NRB;
@@ -339,15 +387,20 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_mfma(const D
     c.p0 = wb >> a.page_shift;
     c.ke = we;
     const int ntiles = (we - wb + KT - 1) / KT;
-    MTile<D> ta, tb;
+    // one register tile: this tile goes to LDS, then the next tile's loads
+    // are issued into the freed registers and fly while this tile computes
+    MTile<D, NRB, MASK> tr;
     int t = w;
-    if (t < ntiles) mload<D>(c, wb + t * KT, lane, ta);
-    for (; t < ntiles; t += 2 * NW) {
-      if (t + NW < ntiles) mload<D>(c, wb + (t + NW) * KT, lane, tb);
-      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + t * KT, ta, qb, lim, b, r0, kt, vt, lane, st);
-      if (t + NW >= ntiles) break;
-      if (t + 2 * NW < ntiles) mload<D>(c, wb + (t + 2 * NW) * KT, lane, ta);
-      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + (t + NW) * KT, tb, qb, lim, b, r0, kt, vt, lane, st);
+    if (t < ntiles) mload<D, NRB, MASK>(a, c, b, r0, wb + t * KT, lane, tr);
+    for (; t < ntiles; t += NW) {
+      mstore<D, NRB, MASK>(tr, kt, vt, lane);
+      float mk[MASK ? NRB : 1][4];
+#pragma unroll
+      for (int rb = 0; rb < (MASK ? NRB : 1); ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mk[rb][i] = MASK ? tr.mk[rb][i] : 0.f;
+      if (t + NW < ntiles) mload<D, NRB, MASK>(a, c, b, r0, wb + (t + NW) * KT, lane, tr);
+      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + t * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
     }
   }
 
