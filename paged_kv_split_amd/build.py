@@ -20,10 +20,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source of the library into paged_kv_split_amd/libpkv.so."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -32,7 +29,27 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source of the library (in parallel) and link
+    paged_kv_split_amd/libpkv.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = "%d" % os.getpid()
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(CSRC, os.path.basename(s) + ".%s.o" % tag) for s in SOURCES]
+    cflags = [f for f in FLAGS if f != "-shared"]
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda so: _run([HIPCC, *cflags, *inc, "-c", so[0], "-o", so[1]], verbose),
+                        zip(SOURCES, objs)))
+        tmp = LIB + ".tmp" + tag
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -45,11 +45,15 @@ int rows_per_block(int R) {
   if (R <= 1) return 1;
   if (R <= 2) return 2;
   if (R <= 4) return 4;
-  if (R <= 8) return 8;
   return R <= 16 ? 16 : 32;
 }
 
-int tile_keys(int head_dim) { return 2 * (64 / (head_dim / 32)); }
+// Keys per VALU wave tile (one QK pass: 64 / (D/32)), never below the
+// 16-key tile of the matrix-core kernel, so split boundaries suit both.
+int tile_keys(int head_dim) {
+  const int t = 64 / (head_dim / 32);
+  return t < 16 ? 16 : t;
+}
 
 namespace {
 
@@ -173,9 +177,16 @@ struct Layout {
   static constexpr int LOG_LPK = ilog2c(LPK);
   static constexpr int LOG_LPV = ilog2c(LPV);
   static constexpr int PBUF = NW * T * RP;             // floats
+  static constexpr int KBUF = NW * T * D / 2;          // per-wave K tile (bf16 pairs, as floats)
+  // XOR swizzle of a K row's 16-byte chunks in the per-wave K tile, so the
+  // key-major reads (lane = key jq, part qq) hit distinct LDS banks
+  static constexpr int SW_MUL = LPK;
+  static constexpr int SW_SHIFT = LPK >= 4 ? 0 : (LPK == 2 ? 1 : 2);
+  static constexpr int SW_MASK = LPK >= 8 ? 1 : 3;
+  __device__ static int kslot(int ch, int row) { return ch ^ (SW_MUL * ((row >> SW_SHIFT) & SW_MASK)); }
   static constexpr int MERGE = NW * RP * D + NW * RP * 2;
   static constexpr int QLDS = QREG ? 0 : RP * D / 2;  // q rows as packed bf16 pairs (floats)
-  static constexpr int MAIN = kBtCap + 4 + QLDS + PBUF;  // page-table slice (+1 page when a window
+  static constexpr int MAIN = kBtCap + 4 + QLDS + PBUF + KBUF;  // page-table slice (+1 page when a window
                                                          // starts mid-page), q, p slices
   static constexpr int SMEM = MAIN > MERGE ? MAIN : MERGE;
 };
@@ -196,7 +207,7 @@ struct Ctx {
 
 template <int D, int RP, bool MASK>
 struct Tile {
-  uint4 k[Layout<D, RP>::NPASS][4];
+  uint4 k[Layout<D, RP>::NSTEP];   // K rows in the row layout (same rows/chunks as v)
   uint4 v[Layout<D, RP>::NSTEP];
   float mk[MASK ? Layout<D, RP>::NPASS : 1][MASK ? RP : 1];  // additive mask (log2 units) of this lane's key
 };
@@ -208,11 +219,14 @@ __device__ __forceinline__ int64_t row_offset(const Ctx<D, RP> &c, int j) {
 }
 
 // Issue the loads of tile `base` (keys base .. base+T-1) into registers.
-// Rows past the end are clamped to the last valid key: they load finite
-// data that the score mask gives zero weight, so no lane branches and no
-// register is zero-filled.  When a page holds at least one tile, the tile's
-// page is wave-uniform and resolved once, in scalar registers.
-template <int D, int RP, bool MASK>
+// K and V use the same row layout: lane (kg, ds) fetches 16 bytes (chunk ds)
+// of rows base + st*KPV + kg, so each wave instruction reads whole rows and
+// one page lookup serves both caches.  Rows past the end are clamped to the
+// last valid key: they load finite data that the score mask gives zero
+// weight, so no lane branches and no register is zero-filled.  With UPAGE (a
+// page holds at least one tile) the tile's page is wave-uniform and resolved
+// once, in scalar registers.
+template <int D, int RP, bool MASK, bool UPAGE>
 __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int base,
                                           Tile<D, RP, MASK> &t) {
   using Lay = Layout<D, RP>;
@@ -236,39 +250,27 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
       }
     }
   }
-  if (c.page_shift >= ilog2c(Lay::T)) {
+  if constexpr (UPAGE) {
     const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
     const int64_t pofs = (int64_t)page * c.page_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
 #pragma unroll
-    for (int pp = 0; pp < Lay::NPASS; ++pp) {
-      int j = base + pp * Lay::KPP + c.jq;
-      j = j < jlast ? j : jlast;
-      const uint4 *src = reinterpret_cast<const uint4 *>(kp + (uint32_t)((j & c.pmask) * c.row_stride));
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = load_stream(src + c.qq + Lay::LPK * c4);
-    }
-#pragma unroll
     for (int st = 0; st < Lay::NSTEP; ++st) {
       int j = base + st * Lay::KPV + c.kg;
       j = j < jlast ? j : jlast;
-      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + (uint32_t)((j & c.pmask) * c.row_stride)) + c.ds);
+      const uint32_t off = (uint32_t)((j & c.pmask) * c.row_stride);
+      t.k[st] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + c.ds);
+      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + c.ds);
     }
   } else {
 #pragma unroll
-    for (int pp = 0; pp < Lay::NPASS; ++pp) {
-      int j = base + pp * Lay::KPP + c.jq;
-      j = j < jlast ? j : jlast;
-      const uint4 *src = reinterpret_cast<const uint4 *>(c.kbase + row_offset(c, j));
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) t.k[pp][c4] = load_stream(src + c.qq + Lay::LPK * c4);
-    }
-#pragma unroll
     for (int st = 0; st < Lay::NSTEP; ++st) {
       int j = base + st * Lay::KPV + c.kg;
       j = j < jlast ? j : jlast;
-      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + row_offset(c, j)) + c.ds);
+      const int64_t off = row_offset(c, j);
+      t.k[st] = load_stream(reinterpret_cast<const uint4 *>(c.kbase + off) + c.ds);
+      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + off) + c.ds);
     }
   }
 }
@@ -300,10 +302,20 @@ struct QRows<D, RP, false> {
 template <int D, int RP, bool CAUSAL, bool MASK, class Q>
 __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int base,
                                              const Tile<D, RP, MASK> &t, const Q &qrows,
-                                             const int (&lim)[RP], int b, int r0, float *pbuf,
+                                             const int (&lim)[RP], int b, int r0, float *pbuf, float *kbuf,
                                              State<RP> &st) {
   using Lay = Layout<D, RP>;
   constexpr int NPASS = Lay::NPASS, KPP = Lay::KPP, LPK = Lay::LPK;
+  // K tile: row layout (registers) -> per-wave LDS slice -> key-major layout
+  {
+    uint4 *kw = reinterpret_cast<uint4 *>(kbuf);
+#pragma unroll
+    for (int st = 0; st < Lay::NSTEP; ++st) {
+      const int row = st * Lay::KPV + c.kg;
+      kw[row * (D / 8) + Lay::kslot(c.ds, row)] = t.k[st];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
   // scores, summed over the LPK lanes of each key
   float sc[NPASS][RP];
 #pragma unroll
@@ -311,9 +323,11 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
     float d[RP];
 #pragma unroll
     for (int r = 0; r < RP; ++r) d[r] = 0.f;
+    const int krow = pp * KPP + c.jq;
+    const uint4 *kr = reinterpret_cast<const uint4 *>(kbuf) + krow * (D / 8);
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
-      const uint4 kk = t.k[pp][c4];
+      const uint4 kk = kr[Lay::kslot(c.qq + LPK * c4, krow)];
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
         const uint4 qv = qrows.get(r, c4, c.qq);
@@ -413,7 +427,27 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int RP, bool CAUSAL, bool MASK>
+// The key-tile loop of one wave, double-buffered in registers: the next
+// tile's loads fly during this tile's compute.
+template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q>
+__device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int wb,
+                                          int t0, int ntiles, const Q &qrows, const int (&lim)[RP], float *pbuf,
+                                          float *kbuf, State<RP> &st) {
+  using Lay = Layout<D, RP>;
+  constexpr int NW = Lay::NW, T = Lay::T;
+  Tile<D, RP, MASK> ta, tb;
+  int t = t0;
+  if (t < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + t * T, ta);
+  for (; t < ntiles; t += 2 * NW) {
+    if (t + NW < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + NW) * T, tb);
+    compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, kbuf, st);
+    if (t + NW >= ntiles) break;
+    if (t + 2 * NW < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
+    compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, kbuf, st);
+  }
+}
+
+template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const DecodeArgs a) {
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, LPK = Lay::LPK, T = Lay::T, LPV = Lay::LPV;
@@ -510,6 +544,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   }
 
   float *pbuf = smem + kBtCap + 4 + Lay::QLDS + w * (T * RP);
+  float *kbuf = smem + kBtCap + 4 + Lay::QLDS + Lay::PBUF + w * (T * D / 2);
   int *bt_lds = reinterpret_cast<int *>(smem);
   const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
 
@@ -549,17 +584,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     c.ke = we;
     const int ntiles = (we - wb + T - 1) / T;
 
-    // double-buffered tile loop: the next tile's loads fly during this compute
-    Tile<D, RP, MASK> ta, tb;
-    int t = w;
-    if (t < ntiles) load_tile(a, c, b, r0, wb + t * T, ta);
-    for (; t < ntiles; t += 2 * NW) {
-      if (t + NW < ntiles) load_tile(a, c, b, r0, wb + (t + NW) * T, tb);
-      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, st);
-      if (t + NW >= ntiles) break;
-      if (t + 2 * NW < ntiles) load_tile(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
-      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, st);
-    }
+    tile_loop<D, RP, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, w, ntiles, qrows, lim, pbuf, kbuf, st);
   }
 
   // ---- wave totals: l over QK key groups, acc over PV key groups
@@ -633,6 +658,13 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 // are computed lane-parallel over the splits (M, sum w by DPP reductions in a
 // fixed order), parked in LDS, then the partial rows are accumulated in
 // split order with many loads in flight; empty splits (l_s = 0) are skipped.
+// Combine: one wave per output row.  The split weights w_s = l_s exp(m_s - M)
+// are computed lane-parallel over the splits (M, sum w by DPP reductions in a
+// fixed order); the partial rows are loaded in batches of kCombBatch splits
+// issued together with (and independent of) the weights, so a row costs about
+// one memory round trip per batch; empty splits (l_s = 0) get weight 0.
+constexpr int kCombBatch = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   __shared__ float wsh[4][kMaxSplitsCombine];
@@ -644,6 +676,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int S = a.S;
   const float2 *ml = reinterpret_cast<const float2 *>(a.ml_part) + row * S;
   const float *op = a.o_part + row * S * D;
+
+  // first batch of partial rows, issued before the weights are known
+  float ob[kCombBatch][PER];
+#pragma unroll
+  for (int k = 0; k < kCombBatch; ++k)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = lane + 64 * e;
+      ob[k][e] = (k < S && d < D) ? op[k * D + d] : 0.f;
+    }
+
   constexpr int SPL = kMaxSplitsCombine / 64;  // splits per lane
   float2 v[SPL];
   float M = -INFINITY;
@@ -655,55 +698,74 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   }
   M = reduce_hi<0, OpMax>(M);
   float W = 0.f;
-  if (M != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < SPL; ++k) {
-      const float wk = v[k].y > 0.f ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
-      if (lane + 64 * k < S) wsh[wv][lane + 64 * k] = wk;
-      W += wk;
-    }
-    W = reduce_hi<0, OpSum>(W);
+  for (int k = 0; k < SPL; ++k) {
+    const float wk = (M != -INFINITY && v[k].y > 0.f) ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
+    if (lane + 64 * k < S) wsh[wv][lane + 64 * k] = wk;
+    W += wk;
   }
+  W = reduce_hi<0, OpSum>(W);
   __builtin_amdgcn_wave_barrier();
+
   float o[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  if (W > 0.f) {
-#pragma unroll 8
-    for (int sidx = 0; sidx < S; ++sidx) {
-      const float f = wsh[wv][sidx];
-      if (f == 0.f) continue;
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) o[k] = fmaf(f, op[sidx * D + d], o[k]);
+  for (int k = 0; k < kCombBatch; ++k) {
+    if (k < S) {
+      const float f = wsh[wv][k];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = fmaf(f, ob[k][e], o[e]);
+    }
+  }
+  for (int s0 = kCombBatch; s0 < S; s0 += kCombBatch) {
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int d = lane + 64 * e;
+        ob[k][e] = (s0 + k < S && d < D) ? op[(s0 + k) * D + d] : 0.f;
+      }
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      if (s0 + k < S) {
+        const float f = wsh[wv][s0 + k];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = fmaf(f, ob[k][e], o[e]);
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int d = lane + 64 * k;
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane + 64 * e;
     if (d < D) {
-      const float res = W > 0.f ? o[k] / W : 0.f;
+      const float res = W > 0.f ? o[e] / W : 0.f;
       a.out[row * D + d] = f32_to_bf16_rne(res);
       if (a.out_f32) a.out_f32[row * D + d] = res;
     }
   }
 }
 
-template <int D, int RP, bool C, bool M>
+template <int D, int RP, bool C, bool M, bool U>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
   const int64_t outer_pad = ((int64_t)a.outer + 7) / 8 * 8;
   const int64_t grid = outer_pad * a.inner;
-  hipLaunchKernelGGL((split_decode_valu<D, RP, C, M>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
+  hipLaunchKernelGGL((split_decode_valu<D, RP, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
 
+template <int D, int RP, bool C, bool M>
+hipError_t launch_u(const DecodeArgs &a, hipStream_t s) {
+  // the page of a whole tile is wave-uniform when a page holds at least a tile
+  constexpr int T = Layout<D, RP>::T;
+  return a.page_shift >= ilog2c(T) ? launch_t<D, RP, C, M, true>(a, s) : launch_t<D, RP, C, M, false>(a, s);
+}
+
 template <int D, int RP>
 hipError_t launch_rp(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
-  if (causal) return mask ? launch_t<D, RP, true, true>(a, s) : launch_t<D, RP, true, false>(a, s);
-  return mask ? launch_t<D, RP, false, true>(a, s) : launch_t<D, RP, false, false>(a, s);
+  if (causal) return mask ? launch_u<D, RP, true, true>(a, s) : launch_u<D, RP, true, false>(a, s);
+  return mask ? launch_u<D, RP, false, true>(a, s) : launch_u<D, RP, false, false>(a, s);
 }
 
 template <int D>
@@ -711,8 +773,7 @@ hipError_t launch_d(const DecodeArgs &a, int rp, bool causal, bool mask, hipStre
   switch (rp) {
     case 1: return launch_rp<D, 1>(a, causal, mask, s);
     case 2: return launch_rp<D, 2>(a, causal, mask, s);
-    case 4: return launch_rp<D, 4>(a, causal, mask, s);
-    default: return launch_rp<D, 8>(a, causal, mask, s);
+    default: return launch_rp<D, 4>(a, causal, mask, s);
   }
 }
 

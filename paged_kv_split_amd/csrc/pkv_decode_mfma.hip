@@ -85,7 +85,8 @@ struct MLay {
   static constexpr int TILE_ELEMS = KT * D;  // bf16 per K (or V) tile
   static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
-  static constexpr int MERGE_BYTES = NW * 16 * D * 4 + NW * 32 * 2 * 4;
+  static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
+  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
   static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   // swizzles (16-byte chunk index within a row)
@@ -112,13 +113,13 @@ struct MCtx {
 // Loads of one 16-key tile: full K/V rows, 128 bits per lane.  Rows past the
 // end are clamped to the last valid key (finite data, zero weight); when a
 // page holds the whole tile its page is resolved once, in scalar registers.
-template <int D, int NRB, bool MASK>
+template <int D, int NRB, bool MASK, bool UPAGE>
 __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b, int r0, int base, int lane,
                                       MTile<D, NRB, MASK> &t) {
   using L = MLay<D>;
   const int ch = lane % L::LPR;
   const int jlast = c.ke - 1;
-  if (c.page_shift >= 4) {
+  if constexpr (UPAGE) {
     const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
     const int64_t pofs = (int64_t)page * c.page_stride;
     const uint16_t *kp = c.kbase + pofs;
@@ -274,11 +275,58 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
   __builtin_amdgcn_wave_barrier();
 }
 
+// One pipeline step: tile tt (in registers tr) -> LDS; issue the loads of
+// tile tnext (if >= 0) into tr; compute tile tt from LDS.
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
+__device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int tt,
+                                      int tnext, MTile<D, NRB, MASK> &tr, const uint4 (&qb)[NRB][D / 32],
+                                      const int (&lim)[NRB], uint16_t *kt, uint16_t *vt, int lane,
+                                      MState<D, NRB> &st) {
+  mstore<D, NRB, MASK>(tr, kt, vt, lane);
+  float mk[MASK ? NRB : 1][4];
+#pragma unroll
+  for (int rb = 0; rb < (MASK ? NRB : 1); ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mk[rb][i] = MASK ? tr.mk[rb][i] : 0.f;
+  if (tnext >= 0) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + tnext * KT, lane, tr);
+  mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
+}
+
+// The key-tile loop of one wave: two register tiles; a tile goes to LDS,
+// then the loads of the tile two steps ahead are issued into the freed
+// registers, so the next tile's loads are in flight while this one computes.
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
+__device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int t0,
+                                           int ntiles, const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB],
+                                           uint16_t *kt, uint16_t *vt, int lane, MState<D, NRB> &st) {
+  constexpr int NW = MLay<D>::NW;
+  if constexpr (D >= 256) {
+    // one register tile (two would spill at D = 256): the next tile's loads
+    // are issued right after this tile reaches LDS and fly during its compute
+    MTile<D, NRB, MASK> tr;
+    if (t0 < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, tr);
+    for (int t = t0; t < ntiles; t += NW)
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + NW < ntiles ? t + NW : -1, tr, qb, lim, kt, vt,
+                                         lane, st);
+    return;
+  }
+  MTile<D, NRB, MASK> ta, tb;
+  if (t0 < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, ta);
+  if (t0 + NW < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + NW) * KT, lane, tb);
+  for (int t = t0; t < ntiles; t += 2 * NW) {
+    mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + 2 * NW < ntiles ? t + 2 * NW : -1, ta, qb, lim, kt,
+                                       vt, lane, st);
+    if (t + NW >= ntiles) break;
+    mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t + NW, t + 3 * NW < ntiles ? t + 3 * NW : -1, tb, qb, lim,
+                                       kt, vt, lane, st);
+  }
+}
+
 // Two resident workgroups per CU (2 waves per SIMD) where the registers allow.
 template <int D, int NRB>
 constexpr int mfma_min_blocks() { return (D >= 256 && NRB == 2) ? 1 : 2; }
 
-template <int D, int NRB, bool CAUSAL, bool MASK>
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
 __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) void split_decode_mfma(
     const DecodeArgs a) {
   using L = MLay<D>;
@@ -387,21 +435,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
     c.p0 = wb >> a.page_shift;
     c.ke = we;
     const int ntiles = (we - wb + KT - 1) / KT;
-    // one register tile: this tile goes to LDS, then the next tile's loads
-    // are issued into the freed registers and fly while this tile computes
-    MTile<D, NRB, MASK> tr;
-    int t = w;
-    if (t < ntiles) mload<D, NRB, MASK>(a, c, b, r0, wb + t * KT, lane, tr);
-    for (; t < ntiles; t += NW) {
-      mstore<D, NRB, MASK>(tr, kt, vt, lane);
-      float mk[MASK ? NRB : 1][4];
-#pragma unroll
-      for (int rb = 0; rb < (MASK ? NRB : 1); ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mk[rb][i] = MASK ? tr.mk[rb][i] : 0.f;
-      if (t + NW < ntiles) mload<D, NRB, MASK>(a, c, b, r0, wb + (t + NW) * KT, lane, tr);
-      mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + t * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
-    }
+    mtile_loop<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, w, ntiles, qb, lim, kt, vt, lane, st);
   }
 
   // row sums over the four lanes of each row
@@ -411,14 +445,14 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
 
   // merge the waves, one 16-row block at a time
   float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][D]
-  float *mlb = ob + NW * 16 * D;                          // [NW][32][2]
+  float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW][32][2]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       // lane holds O^T[d = 16nb + 4q + i][row cc]
-      float4 *dst = reinterpret_cast<float4 *>(ob + (w * 16 + cc) * D + 16 * nb + 4 * q);
+      float4 *dst = reinterpret_cast<float4 *>(ob + (w * 16 + cc) * L::OB_STRIDE + 16 * nb + 4 * q);
       dst[0] = make_float4(st.o[rb][nb][0], st.o[rb][nb][1], st.o[rb][nb][2], st.o[rb][nb][3]);
     }
     if (q == 0) {
@@ -443,7 +477,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
           if (lw > 0.f) {
             const float f = fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M);
             W = fmaf(f, lw, W);
-            o = fmaf(f, ob[(ww * 16 + r) * D + d], o);
+            o = fmaf(f, ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
           }
         }
       }
@@ -465,19 +499,25 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   }
 }
 
-template <int D, int NRB, bool C, bool M>
+template <int D, int NRB, bool C, bool M, bool U>
 hipError_t mlaunch_t(const DecodeArgs &a, hipStream_t stream) {
   const int64_t outer_pad = ((int64_t)a.outer + 7) / 8 * 8;
   const int64_t grid = outer_pad * a.inner;
-  hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
+  hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
 
+template <int D, int NRB, bool C, bool M>
+hipError_t mlaunch_u(const DecodeArgs &a, hipStream_t s) {
+  // a 16-key tile's page is wave-uniform when pages hold at least 16 keys
+  return a.page_shift >= 4 ? mlaunch_t<D, NRB, C, M, true>(a, s) : mlaunch_t<D, NRB, C, M, false>(a, s);
+}
+
 template <int D, int NRB>
 hipError_t mlaunch_nrb(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
-  if (causal) return mask ? mlaunch_t<D, NRB, true, true>(a, s) : mlaunch_t<D, NRB, true, false>(a, s);
-  return mask ? mlaunch_t<D, NRB, false, true>(a, s) : mlaunch_t<D, NRB, false, false>(a, s);
+  if (causal) return mask ? mlaunch_u<D, NRB, true, true>(a, s) : mlaunch_u<D, NRB, true, false>(a, s);
+  return mask ? mlaunch_u<D, NRB, false, true>(a, s) : mlaunch_u<D, NRB, false, false>(a, s);
 }
 
 template <int D>

@@ -46,10 +46,12 @@ struct CombineArgs {
   int32_t S;
 };
 
-// Which split kernel serves a problem.  R = G * q_len rows share a kv head:
-// R <= 8 runs on the VALU kernel with R padded to RP in {1, 2, 4, 8}; larger
-// R fills 16-row matrix-core tiles (one or two per workgroup).
-inline bool use_mfma(int R) { return R > 8; }
+// Which split kernel serves a problem.  R = G * q_len rows share a kv head.
+// Up to 4 rows run on the VALU kernel (rows padded to RP in {1, 2, 4}); from
+// 5 rows on, the matrix-core kernel (16-row tiles, one or two per workgroup)
+// was measured faster on gfx950 even with half of a tile padded (R = 6, 8),
+// so it takes over there.
+inline bool use_mfma(int R) { return R > 4; }
 int rows_per_block(int R);         // rows per workgroup: RP (VALU) or 16/32 (MFMA)
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
