@@ -33,6 +33,39 @@ PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E peak
 METRIC = "paged-decode attention µs/call and achieved HBM GB/s (% of peak), B=8..256"
 
 
+def kernel_name(w, S, prob) -> str:
+    import paged_kv_split_amd as pkv
+    return pkv.kernel_family(prob)
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources; counter figures taken on other sources
+    are stale."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_split_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or
+    None when there is none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    e = data.get("workloads", {}).get(workload)
+    if not e or data.get("source_digest") != source_digest():
+        return None
+    return e["hbm_bytes_per_call"]
+
+
 def make_workload(name: str):
     import workloads
     if name in workloads.CONFIGS:
@@ -151,35 +184,21 @@ def main():
     S = pkv.num_splits_for(prob)
     prob.num_splits = S
     out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
-    ob, mb = pkv.partials_bytes(prob, S)
-    o_part = torch.empty(max(ob // 4, 4), dtype=torch.float32, device=dev)
-    ml_part = torch.empty(max(mb // 4, 4), dtype=torch.float32, device=dev)
+    o_part, ml_part = pkv.alloc_workspace(prob, S, dev)      # ml_part zeroed (counter head)
+    ob = 0 if o_part is None else o_part.numel() * 4
+    mb = 0 if ml_part is None else ml_part.numel() * 4
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-    rows = w.B * w.q_len * w.Hq
 
     P = pkv._ptr
     base = (P(q), P(bt), P(kl), P(co), P(mask))
-
-    def split_call(r):
-        if S > 1:
-            st = pkv.paged_decode_partials_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3],
-                                               base[4], P(o_part), ob, P(ml_part), mb, sh)
-        else:
-            st = pkv.paged_decode_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3], base[4],
-                                      0, 0, 0, 0, P(out), 0, sh)
-        if st:
-            raise pkv.PkvError(st, "split")
-
-    def combine_call():
-        st = pkv.combine_raw(rows, S, w.D, P(o_part), P(ml_part), P(out), 0, sh)
-        if st:
-            raise pkv.PkvError(st, "combine")
+    po, pm = P(o_part), P(ml_part)
 
     def step(r):
-        split_call(r)
-        if S > 1:
-            combine_call()
+        st = pkv.paged_decode_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3], base[4],
+                                  po, ob, pm, mb, P(out), 0, sh)
+        if st:
+            raise pkv.PkvError(st, "pkv_paged_decode")
 
     # warmup
     for i in range(args.warmup):
@@ -204,7 +223,7 @@ def main():
     spin = int(min(2.0 * host_per_step * args.steps * 1e3 / max(sleep_ms_per_unit, 1e-9), 2**31 - 1))
 
     def timed(rotate=True):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         torch.cuda._sleep(spin)
@@ -212,22 +231,17 @@ def main():
         for i in range(args.steps):
             r = i % n_rep if rotate else 0
             ev[i][0].record()
-            split_call(r)
+            step(r)
             ev[i][1].record()
-            if S > 1:
-                combine_call()
-            ev[i][2].record()
         end.record()
         torch.cuda.synchronize()
         total = start.elapsed_time(end)
-        split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-        comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps if S > 1 else 0.0
-        return total, split_ms, comb_ms
+        call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        return total, call_ms
 
     runs = [timed(True) for _ in range(max(1, args.runs))]
     total_ms = statistics.median(r[0] for r in runs)
-    split_ms = statistics.median(r[1] for r in runs)
-    comb_ms = statistics.median(r[2] for r in runs)
+    call_ms = statistics.median(r[1] for r in runs)
     warm = timed(False)
     print("bench: timed runs done", file=sys.stderr, flush=True)
 
@@ -240,7 +254,7 @@ def main():
             g = torch.cuda.CUDAGraph()
             sh_saved = sh
             with torch.cuda.stream(gs):
-                sh = int(gs.cuda_stream)        # split_call/combine_call launch on the capture stream
+                sh = int(gs.cuda_stream)        # step() launches on the capture stream
                 with torch.cuda.graph(g, stream=gs):
                     for r in range(nrep_g):
                         step(r)
@@ -263,7 +277,8 @@ def main():
     kv_bytes = w.kv_bytes()
     us_call = total_ms * 1e3 / args.steps
     gbs = kv_bytes / (us_call * 1e-6) / 1e9
-    split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+    kern_gbs = kv_bytes / (call_ms * 1e-3) / 1e9
+    n_kernels = 1 if (S == 1 or pkv.merges_in_kernel(prob, S)) else 2
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -280,13 +295,14 @@ def main():
         "config": describe(w, S, n_rep),
         "us_per_call": round(us_call, 3),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "kernel_us": {"split": round(split_ms * 1e3, 3), "combine": round(comb_ms * 1e3, 3)},
+        "kernels_per_call": n_kernels,
+        "call_us_events": round(call_ms * 1e3, 3),
         "warm_us_per_call": round(warm[0] * 1e3 / args.steps, 3),
         "graph_us_per_call": None if graph_us is None else round(graph_us, 3),
         "kv_bytes_per_call": kv_bytes,
-        "roofline": {"bound": "hbm", "kernel": "split_decode", "achieved": round(split_gbs, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": kernel_name(w, S, prob), "achieved": round(kern_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.name)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

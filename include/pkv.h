@@ -16,15 +16,17 @@
  * page_size].  GQA: query head h reads kv head g(h) = h / (Hq / Hkv).  A row
  * that sees no finite score gets 0.  The work is split along the keys
  * ("split-KV"); each split leaves a normalised partial output and its
- * (max, sum) pair, merged by one log-sum-exp combine kernel.
+ * (max, sum) pair, merged with the log-sum-exp rule; in pkv_paged_decode the
+ * workgroup that finishes last among the splits of a (sequence, kv head, row
+ * block) unit does that merge, so one kernel launch covers the whole path.
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are caller-owned DEVICE memory of the current HIP
  *    device, read or written asynchronously on `stream`.  The library keeps
  *    no pointer after a call returns.
- *  - No entry point allocates, frees, copies, sets memory or synchronises;
- *    pkv_paged_decode and pkv_combine only launch kernels on `stream`, so
- *    they may be captured into a hipGraph.  Kernel arguments depend only on
+ *  - No entry point allocates, frees, copies, sets memory through the
+ *    runtime or synchronises; the entry points taking a stream only launch
+ *    kernels on it, so they may be captured into a hipGraph.  Kernel arguments depend only on
  *    host values, so device data (kv_lens, block_table, q, K/V, mask) may
  *    change between graph replays.
  *  - Every host-side check runs before any HIP call; a failed check returns
@@ -64,6 +66,13 @@ enum {
 
 #define PKV_MAX_SPLITS 256
 
+/* Head of the pkv_paged_decode ml_part workspace holding the per-unit arrival
+ * counters of the in-kernel merge (one int32 per (sequence, kv head, row
+ * block) unit), and the largest unit count merged in-kernel; problems with
+ * more units and several splits use a separate combine launch instead. */
+#define PKV_COUNTER_BYTES 16384
+#define PKV_MAX_FUSED_UNITS (PKV_COUNTER_BYTES / 4)
+
 /* Problem description (host memory; read during the call only).
  * Sizes follow the statement of the paged decode problem: q[B, q_len, Hq, D],
  * k_cache / v_cache[num_pages, page_size, Hkv, D], block_table[B,
@@ -94,11 +103,23 @@ int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out);
 
 /* Workspace pkv_paged_decode needs with `splits` splits:
  *   o_part : fp32 [B, q_len, Hq, splits, D]      (normalised partial outputs)
- *   ml_part: fp32 [B, q_len, Hq, splits, 2]      (m, l) per partial,
+ *   ml_part: PKV_COUNTER_BYTES of int32 arrival counters, then
+ *            fp32 [B, q_len, Hq, splits, 2]      (m, l) per partial,
  * m = max scaled+masked score in natural-log units, l = sum exp(s - m).
- * Both are 0 when splits == 1 (the split kernel then writes `out` itself). */
+ * Both are 0 when splits == 1 (the split kernel then writes `out` itself).
+ * The counter head must read zero when a call starts: clear a new workspace
+ * once (pkv_workspace_clear, or any zero fill); every call returns the
+ * counters it used to zero before its kernel ends, so a workspace stays
+ * ready across calls of any shape.  Calls sharing one workspace must be
+ * ordered (one stream, or synchronised streams). */
 int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
                         size_t *ml_part_bytes);
+
+/* Zero `bytes` (a multiple of 4) of device memory at `ptr` (4-byte aligned)
+ * with a fill kernel on `stream` (not a runtime memset, so it may be
+ * captured into a hipGraph).  Meant for a newly allocated ml_part workspace.
+ * bytes == 0 is a no-op. */
+int pkv_workspace_clear(void *ptr, size_t bytes, hipStream_t stream);
 
 /* Paged decode attention.
  *   q            bf16 [B, q_len, Hq, D], contiguous, 16-byte aligned
@@ -112,13 +133,17 @@ int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
  *                mask[b * mask_stride_b + i * mask_stride_q + j]; -inf removes
  *                a key; entries at j >= kv_lens[b] are never read
  *   o_part, ml_part  workspace of at least pkv_workspace_bytes for the split
- *                count in use (16- and 8-byte aligned); may be NULL when that
- *                count is 1.  Contents on return are the split partials.
+ *                count in use (16- and 8-byte aligned, ml_part's counter
+ *                head zero as described there); may be NULL when that count
+ *                is 1.  Contents on return: the counter head zero, the split
+ *                partials of the splits that saw at least one key (l > 0;
+ *                an empty split writes only (m, l) = (-inf, 0)).
  *   out_bf16     bf16 [B, q_len, Hq, D], 16-byte aligned; round-to-nearest-even
  *                of the fp32 result
  *   out_f32      NULL, or fp32 [B, q_len, Hq, D] (the value before rounding)
- * Returns PKV_OK after enqueueing one split kernel (plus the combine kernel
- * when more than one split is used) on `stream`. */
+ * Returns PKV_OK after enqueueing one kernel on `stream` (two, the split
+ * kernel and the combine kernel, when several splits are used and the
+ * problem has more than PKV_MAX_FUSED_UNITS units). */
 int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                      const void *v_cache, const int32_t *block_table,
                      const int32_t *kv_lens, const int32_t *causal_offsets,
@@ -131,9 +156,10 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
  * that merge partials themselves, e.g. after gathering the partials of key
  * shards held by several devices, with pkv_combine.  o_part (fp32 [B, q_len,
  * Hq, splits, D], 16-byte aligned) and ml_part (fp32 [B, q_len, Hq, splits,
- * 2], 8-byte aligned) are required for every split count, including 1: that
- * is pkv_workspace_bytes for splits >= 2, and rows * D * 4 / rows * 8 bytes
- * for one split.  Other arguments as for pkv_paged_decode. */
+ * 2], 8-byte aligned, no counter head) are required for every split count,
+ * including 1: rows * splits * D * 4 and rows * splits * 8 bytes.  Splits
+ * that see no key write only (m, l) = (-inf, 0) and leave their o_part rows
+ * untouched.  Other arguments as for pkv_paged_decode. */
 int pkv_paged_decode_partials(const pkv_problem *p, const void *q,
                               const void *k_cache, const void *v_cache,
                               const int32_t *block_table,
@@ -145,7 +171,8 @@ int pkv_paged_decode_partials(const pkv_problem *p, const void *q,
 
 /* The combine step alone: merges `splits` partials per row with the
  * log-sum-exp rule  M = max_{l_s>0} m_s,  w_s = l_s exp(m_s - M),
- * out = sum_s w_s o_s / sum_s w_s  (0 when no partial has l_s > 0).
+ * out = sum_s w_s o_s / sum_s w_s  (0 when no partial has l_s > 0); the
+ * o_part rows of partials with l_s = 0 are never read.
  *   o_part   fp32 [rows, splits, head_dim]   (16-byte aligned)
  *   ml_part  fp32 [rows, splits, 2]          (m, l), 8-byte aligned
  *   out_bf16 bf16 [rows, head_dim] (16-byte aligned), out_f32 NULL or fp32 [rows, head_dim]

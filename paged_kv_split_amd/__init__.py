@@ -25,9 +25,11 @@ PKV_ERR_ALIGN = 5
 PKV_ERR_LAUNCH = 6
 PKV_ERR_DEVICE = 7
 PKV_MAX_SPLITS = 256
+PKV_COUNTER_BYTES = 16384
+PKV_MAX_FUSED_UNITS = PKV_COUNTER_BYTES // 4
 
-EXPORTED = ("pkv_num_splits", "pkv_workspace_bytes", "pkv_paged_decode", "pkv_paged_decode_partials",
-            "pkv_combine", "pkv_device_cus", "pkv_status_string")
+EXPORTED = ("pkv_num_splits", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+            "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus", "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -71,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_num_splits.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.pkv_workspace_bytes.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.pkv_workspace_clear.argtypes = [P, ctypes.c_size_t, P]
         L.pkv_paged_decode.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                        ctypes.c_size_t, P, P, P]
         L.pkv_paged_decode_partials.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
@@ -79,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_device_cus.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
-        for name in ("pkv_num_splits", "pkv_workspace_bytes", "pkv_paged_decode",
+        for name in ("pkv_num_splits", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -122,6 +125,29 @@ def workspace_bytes(problem: Problem, splits: int) -> tuple[int, int]:
     _check(lib().pkv_workspace_bytes(ctypes.byref(problem), int(splits), ctypes.byref(o), ctypes.byref(ml)),
            "pkv_workspace_bytes")
     return o.value, ml.value
+
+
+def workspace_clear_raw(ptr: int, nbytes: int, stream: int) -> int:
+    """pkv_workspace_clear on a raw address; returns the status code."""
+    return lib().pkv_workspace_clear(ptr or None, int(nbytes), stream or None)
+
+
+def workspace_clear(t, stream=None) -> None:
+    """Zero a workspace tensor with the library's fill kernel."""
+    _check(workspace_clear_raw(_ptr(t), t.numel() * t.element_size(), _stream_handle(stream)),
+           "pkv_workspace_clear")
+
+
+def alloc_workspace(problem: Problem, splits: int, device):
+    """(o_part, ml_part) fp32 device tensors for pkv_paged_decode with
+    ``splits`` splits, ml_part zeroed (its counter head must start at zero);
+    (None, None) for one split."""
+    import torch
+    if splits <= 1:
+        return None, None
+    ob, mb = workspace_bytes(problem, splits)
+    return (torch.empty(ob // 4, dtype=torch.float32, device=device),
+            torch.zeros(mb // 4, dtype=torch.float32, device=device))
 
 
 def paged_decode_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block_table: int,
@@ -205,8 +231,10 @@ def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
     Hkv, D]; block_table int32 [B, max_pages]; kv_lens int32 [B];
     causal_offsets optional int32 [B]; mask optional fp32 [B, kv] or
     [B, q_len, kv] (last dim contiguous).  ``out``/``out_f32``/``o_part``/
-    ``ml_part`` may be passed preallocated (required for graph capture);
-    missing ones are allocated here, outside the library call.
+    ``ml_part`` may be passed preallocated (required for graph capture; see
+    ``alloc_workspace``: ml_part's counter head must be zero before its first
+    use, and the library leaves it zero); missing ones are allocated here,
+    outside the library call.
     """
     import torch
     _require(q, "q", torch.bfloat16, 4)
@@ -228,9 +256,7 @@ def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if S > 1 and (o_part is None or ml_part is None):
-        ob, mb = workspace_bytes(p, S)
-        o_part = torch.empty(ob // 4, dtype=torch.float32, device=q.device)
-        ml_part = torch.empty(mb // 4, dtype=torch.float32, device=q.device)
+        o_part, ml_part = alloc_workspace(p, S, q.device)
     st = paged_decode_raw(p, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(kv_lens),
                           _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
                           0 if o_part is None else o_part.numel() * o_part.element_size(),
@@ -255,6 +281,47 @@ def partials_bytes(problem: Problem, splits: int) -> tuple[int, int]:
     """o_part / ml_part bytes pkv_paged_decode_partials needs (any split count)."""
     rows = problem.batch * problem.q_len * problem.num_q_heads
     return rows * splits * problem.head_dim * 4, rows * splits * 8
+
+
+def rows_per_block(R: int) -> int:
+    """Rows of one workgroup (mirrors the library): 1, 2 or 4 on the VALU
+    kernel (R <= 4), 16 or 32 on the matrix-core kernel."""
+    if R <= 1:
+        return 1
+    if R <= 2:
+        return 2
+    if R <= 4:
+        return 4
+    return 16 if R <= 16 else 32
+
+
+def units_of(problem: Problem) -> int:
+    """(sequence, kv head, row block) units: the workgroups of one unit
+    differ only in their split; up to PKV_MAX_FUSED_UNITS units are merged
+    inside the split kernel."""
+    R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
+    rp = rows_per_block(R)
+    return problem.batch * problem.num_kv_heads * ((R + rp - 1) // rp)
+
+
+def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
+    """Whether pkv_paged_decode with ``splits`` splits merges them inside the
+    split kernel (mirrors the library's rule: several splits, at most
+    PKV_MAX_FUSED_UNITS units, rows_per_block * splits <= 2048 and at most one
+    workgroup per CU) rather than launching the combine kernel."""
+    if splits <= 1:
+        return False
+    R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
+    if units_of(problem) > PKV_MAX_FUSED_UNITS or rows_per_block(R) * splits > 2048:
+        return False
+    cus = num_cus if num_cus > 0 else device_cus()
+    return units_of(problem) * splits <= cus
+
+
+def kernel_family(problem: Problem) -> str:
+    """Which split kernel serves the problem (R = G * q_len rows per kv head)."""
+    R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
+    return "split_decode_mfma" if R > 4 else "split_decode_valu"
 
 
 def num_splits_for(problem: Problem) -> int:

@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -59,10 +60,9 @@ namespace {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBtCap = 1024;  // page-table entries staged in LDS per window
-constexpr int kMaxSplitsCombine = 256;  // = PKV_MAX_SPLITS
+using namespace dev;
+
+constexpr int kBtCap = 1024;            // page-table entries staged in LDS per window
 constexpr float kRescaleLog2 = 8.f;     // lazy-rescale threshold (base-2 score units)
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -72,46 +72,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
-
-// ---- cross-lane primitives (DPP / permlane; semantics checked on gfx950) ----
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
-constexpr int kRor4 = 0x124;       // lane i receives lane (i-4) mod 16
-constexpr int kRor8 = 0x128;       // lane i receives lane (i-8) mod 16 (= i xor 8)
-
-struct OpSum {
-  __device__ static float f(float a, float b) { return a + b; }
-};
-struct OpMax {
-  __device__ static float f(float a, float b) { return fmaxf(a, b); }
-};
-
-template <class Op>
-__device__ __forceinline__ float xor16(float x) {  // combine lanes i and i^16
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-template <class Op>
-__device__ __forceinline__ float xor32(float x) {  // combine lanes i and i^32
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
 
 // Reduce over lane bits [0, HI) (HI <= 3) of independent values.
 template <int HI, class Op>
@@ -133,30 +94,6 @@ __device__ __forceinline__ float reduce_hi_grouped(float x) {
   if constexpr (LO <= 4) x = xor16<Op>(x);
   x = xor32<Op>(x);
   return x;
-}
-
-// Reduce over lane bits [LO, 6) of independent values (true xor pairings).
-template <int LO, class Op>
-__device__ __forceinline__ float reduce_hi(float x) {
-  if constexpr (LO <= 0) x = Op::f(x, dpp<kXor1>(x));
-  if constexpr (LO <= 1) x = Op::f(x, dpp<kXor2>(x));
-  if constexpr (LO <= 2) {  // bits 2 and 3 together: lanes i, i-4, i+4, i+8 (mod 16)
-    x = Op::f(x, dpp<kRor4>(x));
-    x = Op::f(x, dpp<kRor8>(x));
-  } else if constexpr (LO <= 3) {
-    x = Op::f(x, dpp<kRor8>(x));
-  }
-  if constexpr (LO <= 4) x = xor16<Op>(x);
-  x = xor32<Op>(x);
-  return x;
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// 128-bit streaming load (K/V are read once per unit: non-temporal hint)
-__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ uint32_t comp(const uint4 &v, int e) {
@@ -596,7 +533,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[r][e] = reduce_hi<Lay::LOG_LPV, OpSum>(st.acc[r][e]);
 
-  // ---- merge the waves through LDS and write
+  // ---- merge the waves through LDS, then write (output, or this split's
+  // partial and, fused, the unit's merge by the block that finishes last)
   __syncthreads();
   float *ob = smem;                    // [NW][RP][D]
   float *mlb = smem + NW * RP * D;     // [NW][RP][2]
@@ -616,134 +554,56 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < RP * D; idx += NW * 64) {
-    const int r = idx / D;
-    const int d = idx - r * D;
-    const int rr = r0 + r;
-    if (rr >= a.R) continue;
+  auto Mrow = [&](int r) {
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww)
       if (mlb[(ww * RP + r) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(ww * RP + r) * 2]);
-    float W = 0.f, o = 0.f;
-    if (M != -INFINITY) {
+    return M;
+  };
+  auto Wrow = [&](int r) {
+    const float M = Mrow(r);
+    float W = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float lw = mlb[(ww * RP + r) * 2 + 1];
-        if (lw > 0.f) {
-          const float f = fast_exp2(mlb[(ww * RP + r) * 2] - M);
-          W = fmaf(f, lw, W);
-          o = fmaf(f, ob[(ww * RP + r) * D + d], o);
-        }
-      }
+    for (int ww = 0; ww < NW; ++ww) {
+      const float lw = mlb[(ww * RP + r) * 2 + 1];
+      if (lw > 0.f) W = fmaf(fast_exp2(mlb[(ww * RP + r) * 2] - M), lw, W);
     }
-    const float res = W > 0.f ? o / W : 0.f;
-    const int i = rr / a.G;
-    const int h = g * a.G + (rr - i * a.G);
-    const int64_t row = ((int64_t)b * a.q_len + i) * a.Hq + h;
-    if (!a.partials) {
-      a.out[row * D + d] = f32_to_bf16_rne(res);
-      if (a.out_f32) a.out_f32[row * D + d] = res;
-    } else {
-      a.o_part[(row * a.S + s) * D + d] = res;
-      if (d == 0) {
-        a.ml_part[(row * a.S + s) * 2] = W > 0.f ? M * kLn2 : -INFINITY;
-        a.ml_part[(row * a.S + s) * 2 + 1] = W;
-      }
-    }
-  }
+    return W;
+  };
+  auto res = [&](int r, int d) {
+    const float M = Mrow(r);
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+      if (mlb[(ww * RP + r) * 2 + 1] > 0.f) o = fmaf(fast_exp2(mlb[(ww * RP + r) * 2] - M), ob[(ww * RP + r) * D + d], o);
+    return o;
+  };
+  const int nrows = a.R - r0 < RP ? a.R - r0 : RP;
+  write_rows<D>(a, b, g, s, r0, nrows, res, Mrow, Wrow, NW * 64);
+  fused_tail<D>(a, b, g, (b * a.Hkv + g) * a.nrb + rb, r0, nrows, smem, NW * 64);
 }
 
-// Combine: one wave per output row.  The split weights w_s = l_s exp(m_s - M)
-// are computed lane-parallel over the splits (M, sum w by DPP reductions in a
-// fixed order), parked in LDS, then the partial rows are accumulated in
-// split order with many loads in flight; empty splits (l_s = 0) are skipped.
-// Combine: one wave per output row.  The split weights w_s = l_s exp(m_s - M)
-// are computed lane-parallel over the splits (M, sum w by DPP reductions in a
-// fixed order); the partial rows are loaded in batches of kCombBatch splits
-// issued together with (and independent of) the weights, so a row costs about
-// one memory round trip per batch; empty splits (l_s = 0) get weight 0.
-constexpr int kCombBatch = 16;
+// Combine (the standalone pkv_combine entry point): each block merges
+// combine_rows(D) consecutive rows (about 512 element pairs, so every thread
+// has work) with the same merge code as the split kernels' in-kernel merge.
+constexpr int combine_rows(int D) { return 512 / D; }
 
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  __shared__ float wsh[4][kMaxSplitsCombine];
-  const int wv = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= a.rows) return;
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = (D + 63) / 64;
-  const int S = a.S;
-  const float2 *ml = reinterpret_cast<const float2 *>(a.ml_part) + row * S;
-  const float *op = a.o_part + row * S * D;
+  constexpr int NR = combine_rows(D);
+  __shared__ float lds[NR * (kMaxSplits + 1)];
+  const int64_t base = (int64_t)blockIdx.x * NR;
+  const int64_t left = a.rows - base;
+  const int nrows = left < NR ? (int)left : NR;
+  merge_rows<D, false>(a.o_part, a.ml_part, a.S, [&](int r) { return base + r; }, nrows, a.out, a.out_f32, lds,
+                       256);
+}
 
-  // first batch of partial rows, issued before the weights are known
-  float ob[kCombBatch][PER];
-#pragma unroll
-  for (int k = 0; k < kCombBatch; ++k)
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = lane + 64 * e;
-      ob[k][e] = (k < S && d < D) ? op[k * D + d] : 0.f;
-    }
-
-  constexpr int SPL = kMaxSplitsCombine / 64;  // splits per lane
-  float2 v[SPL];
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < SPL; ++k) {
-    const int sidx = lane + 64 * k;
-    v[k] = sidx < S ? ml[sidx] : make_float2(-INFINITY, 0.f);
-    if (v[k].y > 0.f) M = fmaxf(M, v[k].x);
-  }
-  M = reduce_hi<0, OpMax>(M);
-  float W = 0.f;
-#pragma unroll
-  for (int k = 0; k < SPL; ++k) {
-    const float wk = (M != -INFINITY && v[k].y > 0.f) ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
-    if (lane + 64 * k < S) wsh[wv][lane + 64 * k] = wk;
-    W += wk;
-  }
-  W = reduce_hi<0, OpSum>(W);
-  __builtin_amdgcn_wave_barrier();
-
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-#pragma unroll
-  for (int k = 0; k < kCombBatch; ++k) {
-    if (k < S) {
-      const float f = wsh[wv][k];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = fmaf(f, ob[k][e], o[e]);
-    }
-  }
-  for (int s0 = kCombBatch; s0 < S; s0 += kCombBatch) {
-#pragma unroll
-    for (int k = 0; k < kCombBatch; ++k)
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int d = lane + 64 * e;
-        ob[k][e] = (s0 + k < S && d < D) ? op[(s0 + k) * D + d] : 0.f;
-      }
-#pragma unroll
-    for (int k = 0; k < kCombBatch; ++k) {
-      if (s0 + k < S) {
-        const float f = wsh[wv][s0 + k];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = fmaf(f, ob[k][e], o[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int d = lane + 64 * e;
-    if (d < D) {
-      const float res = W > 0.f ? o[e] / W : 0.f;
-      a.out[row * D + d] = f32_to_bf16_rne(res);
-      if (a.out_f32) a.out_f32[row * D + d] = res;
-    }
-  }
+// Zero-fill (workspace counters); a kernel, not a memset, so it may sit in a
+// captured graph.
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
 template <int D, int RP, bool C, bool M, bool U>
@@ -789,8 +649,17 @@ int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal, bool ha
   }
 }
 
+int launch_zero(void *p, int64_t words, hipStream_t stream) {
+  if (words <= 0) return hipSuccess;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint32_t *>(p), words);
+  return hipGetLastError();
+}
+
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream) {
-  const unsigned grid = (unsigned)((a.rows + 3) / 4);
+  const int nr = combine_rows(head_dim);
+  const unsigned grid = (unsigned)((a.rows + nr - 1) / nr);
   switch (head_dim) {
     case 32: hipLaunchKernelGGL(combine_kernel<32>, dim3(grid), dim3(256), 0, stream, a); break;
     case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, stream, a); break;

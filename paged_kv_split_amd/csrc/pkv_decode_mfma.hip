@@ -25,10 +25,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
+
+using namespace dev;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -36,44 +39,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBtCap = 1024;
 constexpr int KT = 16;  // keys per wave tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (base-2 score units)
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ float xor16_max(float x) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float xor16_sum(float x) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 template <int D>
 struct MLay {
@@ -86,7 +54,7 @@ struct MLay {
   static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
   static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
-  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4;
+  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4 + 16 * 2 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
   static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   // swizzles (16-byte chunk index within a row)
@@ -227,7 +195,7 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float mt = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
-      mt = xor32_max(xor16_max(mt));
+      mt = xor32<OpMax>(xor16<OpMax>(mt));
       const float mnew = fmaxf(st.m[rb], mt);
       const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(st.m[rb] - mnew);
       st.m[rb] = mnew;
@@ -441,11 +409,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   // row sums over the four lanes of each row
   float ltot[NRB];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) ltot[rb] = xor32_sum(xor16_sum(st.l[rb]));
+  for (int rb = 0; rb < NRB; ++rb) ltot[rb] = xor32<OpSum>(xor16<OpSum>(st.l[rb]));
 
   // merge the waves, one 16-row block at a time
-  float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][D]
+  float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][OB_STRIDE]
   float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW][32][2]
+  float *rmw = mlb + NW * 32 * 2;                         // [16][2]: merged (M, W) per row
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     __syncthreads();
@@ -460,43 +429,41 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
       mlb[(w * 32 + cc + 16 * rb) * 2 + 1] = ltot[rb];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * D; idx += NW * 64) {
-      const int r = idx / D;
-      const int d = idx - r * D;
-      const int rr = r0 + 16 * rb + r;
-      if (rr >= a.R) continue;
+    if (threadIdx.x < 16) {
+      const int r = threadIdx.x;
       float M = -INFINITY;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww)
         if (mlb[(ww * 32 + 16 * rb + r) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(ww * 32 + 16 * rb + r) * 2]);
-      float W = 0.f, o = 0.f;
+      float W = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
           const float lw = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
-          if (lw > 0.f) {
-            const float f = fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M);
-            W = fmaf(f, lw, W);
-            o = fmaf(f, ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
-          }
+          if (lw > 0.f) W = fmaf(fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M), lw, W);
         }
       }
-      const float res = W > 0.f ? o / W : 0.f;
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      const int64_t row = ((int64_t)b * a.q_len + i) * a.Hq + h;
-      if (!a.partials) {
-        a.out[row * D + d] = f32_to_bf16_rne(res);
-        if (a.out_f32) a.out_f32[row * D + d] = res;
-      } else {
-        a.o_part[(row * a.S + s) * D + d] = res;
-        if (d == 0) {
-          a.ml_part[(row * a.S + s) * 2] = W > 0.f ? M * kLn2 : -INFINITY;
-          a.ml_part[(row * a.S + s) * 2 + 1] = W;
-        }
-      }
+      rmw[2 * r] = M;
+      rmw[2 * r + 1] = W;
     }
+    __syncthreads();
+    auto Mrow = [&](int r) { return rmw[2 * r]; };
+    auto Wrow = [&](int r) { return rmw[2 * r + 1]; };
+    auto res = [&](int r, int d) {
+      const float M = rmw[2 * r];
+      float o = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float lw = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
+        if (lw > 0.f) o = fmaf(fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M), ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
+      }
+      return o;
+    };
+    const int rs = r0 + 16 * rb;
+    write_rows<D>(a, b, g, s, rs, a.R - rs < 16 ? a.R - rs : 16, res, Mrow, Wrow, NW * 64);
   }
+  fused_tail<D>(a, b, g, (b * a.Hkv + g) * a.nrb + rg, r0, a.R - r0 < RW ? a.R - r0 : RW,
+                reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 
 template <int D, int NRB, bool C, bool M, bool U>

@@ -1,0 +1,274 @@
+// pkv_device.h -- device helpers shared by the split kernels and the combine
+// kernel of libpkv.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace dev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplits = 256;  // = PKV_MAX_SPLITS
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (quiet NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit streaming load (K/V are read once per unit: non-temporal hint)
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---- cross-lane primitives (DPP / permlane; semantics checked on gfx950) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kRor4 = 0x124;       // lane i receives lane (i-4) mod 16
+constexpr int kRor8 = 0x128;       // lane i receives lane (i-8) mod 16 (= i xor 8)
+
+struct OpSum {
+  __device__ static float f(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+};
+
+template <class Op>
+__device__ __forceinline__ float xor16(float x) {  // combine lanes i and i^16
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x) {  // combine lanes i and i^32
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Reduce over lane bits [LO, 6) of independent values.  Over the whole wave
+// (LO = 0) every step pairs lane i with one partner that in turn pairs with
+// lane i (xor 1, xor 2, mirror within 8, mirror within 16, xor 16, xor 32),
+// and the operation is commutative, so every lane ends with the same
+// bit-identical result.  With LO > 0 bits 2 and 3 are reduced by rotations,
+// whose association differs from lane to lane.
+template <int LO, class Op>
+__device__ __forceinline__ float reduce_hi(float x) {
+  if constexpr (LO <= 0) {
+    x = Op::f(x, dpp<kXor1>(x));
+    x = Op::f(x, dpp<kXor2>(x));
+    x = Op::f(x, dpp<kHalfMirror>(x));  // quad sums: lanes 0-3 <-> 4-7
+    x = Op::f(x, dpp<kMirror>(x));      // 8-lane sums: lanes 0-7 <-> 8-15
+    x = xor16<Op>(x);
+    return xor32<Op>(x);
+  }
+  if constexpr (LO <= 1) x = Op::f(x, dpp<kXor2>(x));
+  if constexpr (LO <= 2) {  // bits 2 and 3 together: lanes i, i-4, i+4, i+8 (mod 16)
+    x = Op::f(x, dpp<kRor4>(x));
+    x = Op::f(x, dpp<kRor8>(x));
+  } else if constexpr (LO <= 3) {
+    x = Op::f(x, dpp<kRor8>(x));
+  }
+  if constexpr (LO <= 4) x = xor16<Op>(x);
+  x = xor32<Op>(x);
+  return x;
+}
+
+// ---- partial results: stores and loads at device scope ---------------------
+// The split workgroups of one unit run on different XCDs, whose L2 caches are
+// not kept coherent with each other.  Partials are therefore stored with
+// device-scope stores (written through to the device-coherent level) and the
+// merging workgroup reads them with device-scope loads (which do not hit
+// possibly stale lines of its own L2), so no whole-cache writeback or
+// invalidate is needed; completion of the stores (s_waitcnt) before the
+// arrival counter's atomic orders them before the merge.
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev2(float *p, float x, float y) {  // p 8-byte aligned
+  const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool DEV>
+__device__ __forceinline__ float2 load2(const float *p) {  // p 8-byte aligned
+  if constexpr (DEV) {
+    const uint64_t u =
+        __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+  } else {
+    return *reinterpret_cast<const float2 *>(p);
+  }
+}
+
+// Output row (b, i, h) of packed row rr (= i * G + k) of kv head g.
+__device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, int rr) {
+  const int i = rr / a.G;
+  const int h = g * a.G + (rr - i * a.G);
+  return ((int64_t)b * a.q_len + i) * a.Hq + h;
+}
+
+// ---- log-sum-exp merge of split partials -----------------------------------
+// For each of `nrows` rows (row index rowf(r)):  M = max over partials with
+// l_s > 0 of m_s,  w_s = l_s exp(m_s - M),  W = sum_s w_s,
+// out = sum_s w_s o_s / W  (0 when W = 0).  The sum over s runs in split
+// order 0..S-1 and skips w_s = 0, so the o_part rows of empty partials are
+// never used (nor do rows with W = 0 use any).  Both the in-kernel merge and
+// the combine kernel run this code, so their results are bit-identical.  Run by a whole block of nthreads
+// threads; `lds` holds nrows * (S + 1) floats (nrows * S <= kMaxMergeWeights).
+// DEV: the partials were written by other workgroups of the running launch.
+constexpr int kMergeBatch = 16;  // partial rows loaded together per thread
+
+template <int D, bool DEV, class RowF>
+__device__ void merge_rows(const float *o_part, const float *ml_part, int S, RowF rowf, int nrows, uint16_t *out,
+                           float *out_f32, float *lds, int nthreads) {
+  constexpr int SPL = kMaxSplits / 64;  // splits per lane
+  constexpr int DP = D / 2;             // element pairs per row
+  constexpr int NB = kMergeBatch;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int nwaves = nthreads >> 6;
+  float *rowW = lds;        // [nrows]
+  float *wt = lds + nrows;  // [nrows][S] split weights
+
+  // first batch of this thread's first element pair, issued before the weights
+  float2 ov[NB];
+  if (tid < nrows * DP) {
+    const int r = tid / DP;
+    const float *op = o_part + rowf(r) * S * D + 2 * (tid - r * DP);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) ov[k] = k < S ? load2<DEV>(op + k * D) : make_float2(0.f, 0.f);
+  }
+
+  for (int r = wv; r < nrows; r += nwaves) {
+    const float *ml = ml_part + rowf(r) * S * 2;
+    float2 v[SPL];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int sidx = lane + 64 * k;
+      v[k] = sidx < S ? load2<DEV>(ml + 2 * sidx) : make_float2(-INFINITY, 0.f);
+      if (v[k].y > 0.f) M = fmaxf(M, v[k].x);
+    }
+    M = reduce_hi<0, OpMax>(M);
+    float W = 0.f;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const float wk = (M != -INFINITY && v[k].y > 0.f) ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
+      if (lane + 64 * k < S) wt[r * S + lane + 64 * k] = wk;
+      W += wk;
+    }
+    W = reduce_hi<0, OpSum>(W);
+    if (lane == 0) rowW[r] = W;
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < nrows * DP; idx += nthreads) {
+    const int r = idx / DP;
+    const int d = 2 * (idx - r * DP);
+    const int64_t row = rowf(r);
+    const float *op = o_part + row * S * D + d;
+    const float *w = wt + r * S;
+    const float W = rowW[r];
+    float ox = 0.f, oy = 0.f;
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      if (s0 > 0 || idx != tid) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) ov[k] = s0 + k < S ? load2<DEV>(op + (s0 + k) * D) : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (s0 + k < S) {
+          const float f = w[s0 + k];
+          if (f != 0.f) {
+            ox = fmaf(f, ov[k].x, ox);
+            oy = fmaf(f, ov[k].y, oy);
+          }
+        }
+      }
+    }
+    const float rx = W > 0.f ? ox / W : 0.f;
+    const float ry = W > 0.f ? oy / W : 0.f;
+    *reinterpret_cast<uint32_t *>(out + row * D + d) =
+        (uint32_t)f32_to_bf16_rne(rx) | ((uint32_t)f32_to_bf16_rne(ry) << 16);
+    if (out_f32) *reinterpret_cast<float2 *>(out_f32 + row * D + d) = make_float2(rx, ry);
+  }
+}
+
+// Epilogue shared by the split kernels once a block has its merged result for
+// packed rows r0 .. r0+nrows-1: `res(r, d)` (unnormalised), `Mrow(r)` (base-2
+// reference) and `Wrow(r)` (total weight).  One split: write the output.
+// Several splits: write this split's partial (o = res / W, m in natural-log
+// units, l = W); an empty split (W = 0) writes only (m, l) = (-inf, 0).
+template <int D, class ResF, class MF, class WF>
+__device__ void write_rows(const DecodeArgs &a, int b, int g, int s, int r0, int nrows, ResF res, MF Mrow,
+                           WF Wrow, int nthreads) {
+  constexpr int DP = D / 2;
+  for (int idx = threadIdx.x; idx < nrows * DP; idx += nthreads) {
+    const int r = idx / DP;
+    const int d = 2 * (idx - r * DP);
+    const int64_t row = out_row(a, b, g, r0 + r);
+    const float W = Wrow(r);
+    if (!a.partials) {
+      const float vx = W > 0.f ? res(r, d) / W : 0.f;
+      const float vy = W > 0.f ? res(r, d + 1) / W : 0.f;
+      *reinterpret_cast<uint32_t *>(a.out + row * D + d) =
+          (uint32_t)f32_to_bf16_rne(vx) | ((uint32_t)f32_to_bf16_rne(vy) << 16);
+      if (a.out_f32) *reinterpret_cast<float2 *>(a.out_f32 + row * D + d) = make_float2(vx, vy);
+    } else {
+      float *po = a.o_part + (row * a.S + s) * D + d;
+      float *pm = a.ml_part + (row * a.S + s) * 2;
+      const float mx = W > 0.f ? Mrow(r) * kLn2 : -INFINITY;
+      if (a.fused) {  // merged by another workgroup of this launch
+        if (W > 0.f) store_dev2(po, res(r, d) / W, res(r, d + 1) / W);
+        if (d == 0) store_dev2(pm, mx, W);
+      } else {        // read after this kernel has ended
+        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(res(r, d) / W, res(r, d + 1) / W);
+        if (d == 0) *reinterpret_cast<float2 *>(pm) = make_float2(mx, W);
+      }
+    }
+  }
+}
+
+// With a.fused (several splits, one call): every block of a unit stores its
+// partial, waits for those stores to complete and counts itself in; the block
+// that arrives last merges the unit's partials and resets the counter, so the
+// workspace is ready for the next call.  `lds` holds at least
+// nrows * (S + 1) floats and is free (all block threads are past their last
+// use of it when this is called).
+template <int D>
+__device__ void fused_tail(const DecodeArgs &a, int b, int g, int unit, int r0, int nrows, float *lds,
+                           int nthreads) {
+  if (!a.fused) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();
+  int *flag = reinterpret_cast<int *>(lds);
+  if (threadIdx.x == 0) flag[0] = atomicAdd(a.counters + unit, 1) == a.S - 1;
+  __syncthreads();
+  const bool last = flag[0] != 0;
+  __syncthreads();
+  if (!last) return;
+  merge_rows<D, true>(a.o_part, a.ml_part, a.S, [&](int r) { return out_row(a, b, g, r0 + r); }, nrows, a.out,
+                      a.out_f32, lds, nthreads);
+  if (threadIdx.x == 0) a.counters[unit] = 0;  // ready for the next call
+}
+
+}  // namespace dev
+}  // namespace pkv

@@ -1,5 +1,6 @@
 // pkv_host.cpp -- host side of the C ABI: argument checks, split heuristic,
-// workspace sizing and launch of the split and combine kernels.
+// workspace sizing and launch of the split kernels (which merge their splits
+// themselves up to PKV_MAX_FUSED_UNITS units) and of the combine kernel.
 //
 // Every check runs before the first HIP call, so a rejected call enqueues
 // nothing; the HIP calls made are kernel launches on the caller's stream,
@@ -20,6 +21,9 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];  // 0 = not queried yet
+
+// A launch's work-items (blocks x 256 threads) must fit 32 bits.
+constexpr int64_t kMaxBlocks = (int64_t)0xFFFFFFFF / 256;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -105,6 +109,19 @@ int heuristic_splits(const pkv_problem *p, int cus) {
   return (int)s;
 }
 
+// (sequence, kv head, row block) units of a problem: the workgroups of one
+// unit share a row block and differ only in their split.
+int64_t units_of(const pkv_problem *p) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  return (int64_t)p->batch * p->num_kv_heads * ceil_div(R, pkv::rows_per_block(R));
+}
+
+// ml_part bytes of pkv_paged_decode with S >= 2 splits: counter head + (m, l).
+size_t ml_bytes_split(const pkv_problem *p, int S) {
+  const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
+  return (size_t)PKV_COUNTER_BYTES + rows * (size_t)S * 2 * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,8 +168,16 @@ int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
   if (splits == 1) { *o_part_bytes = 0; *ml_part_bytes = 0; return PKV_OK; }
   const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
   *o_part_bytes = rows * (size_t)splits * (size_t)p->head_dim * sizeof(float);
-  *ml_part_bytes = rows * (size_t)splits * 2 * sizeof(float);
+  *ml_part_bytes = ml_bytes_split(p, splits);
   return PKV_OK;
+}
+
+int pkv_workspace_clear(void *ptr, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!ptr) return PKV_ERR_NULL;
+  if (!aligned(ptr, 4) || (bytes & 3)) return PKV_ERR_ALIGN;
+  (void)hipGetLastError();
+  return pkv::launch_zero(ptr, (int64_t)(bytes / 4), stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 }  // extern "C"
@@ -183,12 +208,14 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
     if (rc) return rc;
     S = heuristic_splits(p, cus);
   }
+  // pkv_paged_decode with several splits: ml_part = counter head + (m, l)
+  const bool split_ws = S > 1 && !partials_only;
   if (S > 1 || partials_only) {
     const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
     const size_t need_o = rows * (size_t)S * (size_t)p->head_dim * sizeof(float);
-    const size_t need_ml = rows * (size_t)S * 2 * sizeof(float);
+    const size_t need_ml = split_ws ? ml_bytes_split(p, S) : rows * (size_t)S * 2 * sizeof(float);
     if (!o_part || !ml_part || o_part_bytes < need_o || ml_part_bytes < need_ml) return PKV_ERR_WORKSPACE;
-    if (!aligned(o_part, 16) || !aligned(ml_part, 8)) return PKV_ERR_ALIGN;
+    if (!aligned(o_part, 16) || !aligned(ml_part, split_ws ? 16 : 8)) return PKV_ERR_ALIGN;
   }
 
   const int G = p->num_q_heads / p->num_kv_heads;
@@ -209,7 +236,8 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->causal_offsets = causal_offsets;
   a->mask = mask;
   a->o_part = (S > 1 || partials_only) ? o_part : nullptr;
-  a->ml_part = (S > 1 || partials_only) ? ml_part : nullptr;
+  a->ml_part = split_ws ? ml_part + PKV_COUNTER_BYTES / sizeof(float)
+                        : ((S > 1 || partials_only) ? ml_part : nullptr);
   a->out = static_cast<uint16_t *>(out_bf16);
   a->out_f32 = out_f32;
   a->mask_sb = p->mask_stride_b;
@@ -231,10 +259,25 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->scale_log2 = p->scale * 1.4426950408889634f;
   const int64_t outer = (int64_t)p->batch * S;
   const int64_t inner = (int64_t)p->num_kv_heads * a->nrb;
-  if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > INT32_MAX) return PKV_ERR_SHAPE;
+  if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
+  // the combine kernel's grid (several splits without the in-kernel merge)
+  const int64_t rows_all = (int64_t)p->batch * p->q_len * p->num_q_heads;
+  if (ceil_div(rows_all, 2) > kMaxBlocks) return PKV_ERR_SHAPE;
   a->outer = (int32_t)outer;
   a->inner = (int32_t)inner;
   a->partials = (S > 1 || partials_only) ? 1 : 0;
+  // In-kernel merge (counters for every unit, merge weights of a workgroup's
+  // rows in LDS) when the grid is at most one workgroup per CU: then the
+  // merging workgroups do not hold up waiting ones and the saved combine
+  // launch is the larger cost.  Larger grids use the combine kernel, measured
+  // faster there (the merge's device-scope traffic then runs under full HBM
+  // load and on the kernel's critical path).
+  a->fused = 0;
+  if (split_ws && units_of(p) <= PKV_MAX_FUSED_UNITS && (int64_t)rp * S <= pkv::kMaxMergeWeights) {
+    int cus = 0;
+    if (query_cus(&cus) == PKV_OK && outer * inner <= cus) a->fused = 1;
+  }
+  a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
   return PKV_OK;
 }
 
@@ -267,10 +310,10 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
   if (rc) return rc;
   rc = launch_plan(a, p, stream);
   if (rc) return rc;
-  if (a.S > 1) {
+  if (a.S > 1 && !a.fused) {
     pkv::CombineArgs c = {};
     c.o_part = o_part;
-    c.ml_part = ml_part;
+    c.ml_part = a.ml_part;
     c.out = static_cast<uint16_t *>(out_bf16);
     c.out_f32 = out_f32;
     c.rows = (int64_t)p->batch * p->q_len * p->num_q_heads;
@@ -305,7 +348,7 @@ int pkv_combine(int64_t rows, int splits, int head_dim, const float *o_part,
   if (!aligned(o_part, 16) || !aligned(ml_part, 8) || !aligned(out_bf16, 16) ||
       (out_f32 && !aligned(out_f32, 16)))
     return PKV_ERR_ALIGN;
-  if (rows > (int64_t)1 << 40) return PKV_ERR_SHAPE;
+  if (ceil_div(rows, 2) > kMaxBlocks) return PKV_ERR_SHAPE;  // combine: >= 2 rows per block
   pkv::CombineArgs c = {};
   c.o_part = o_part;
   c.ml_part = ml_part;

@@ -35,6 +35,8 @@ struct DecodeArgs {
   int32_t outer;                  // B * S
   int32_t inner;                  // Hkv * nrb
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
+  int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
+  int32_t *counters;              // [units] arrival counters (fused), zero between calls
 };
 
 struct CombineArgs {
@@ -55,6 +57,9 @@ inline bool use_mfma(int R) { return R > 4; }
 int rows_per_block(int R);         // rows per workgroup: RP (VALU) or 16/32 (MFMA)
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
+// Rows x splits whose merge weights one workgroup holds in LDS: the split
+// kernels merge in-kernel only when rows_per_block * S stays within it.
+constexpr int kMaxMergeWeights = 2048;
 
 // Launchers (return a hipError_t value).
 int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
@@ -62,5 +67,6 @@ int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
 int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
                       hipStream_t stream);
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
+int launch_zero(void *p, int64_t words, hipStream_t stream);
 
 }  // namespace pkv

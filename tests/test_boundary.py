@@ -109,12 +109,15 @@ def test_workspace_checks():
     p = base_problem(num_splits=4)
     ob, mb = pkv.workspace_bytes(p, 4)
     rows = 2 * 1 * 8
-    assert ob == rows * 4 * 64 * 4 and mb == rows * 4 * 2 * 4
+    # o_part [rows, S, D]; ml_part = the counter head, then (m, l) [rows, S, 2]
+    assert ob == rows * 4 * 64 * 4 and mb == pkv.PKV_COUNTER_BYTES + rows * 4 * 2 * 4
+    assert pkv.PKV_MAX_FUSED_UNITS == pkv.PKV_COUNTER_BYTES // 4
     assert call(p) == pkv.PKV_ERR_WORKSPACE
     assert call(p, o=FAKE, ob=ob, ml=FAKE, mb=mb - 1) == pkv.PKV_ERR_WORKSPACE
     assert call(p, o=FAKE, ob=ob - 4, ml=FAKE, mb=mb) == pkv.PKV_ERR_WORKSPACE
     assert call(p, o=FAKE + 8, ob=ob, ml=FAKE, mb=mb) == pkv.PKV_ERR_ALIGN
     assert call(p, o=FAKE, ob=ob, ml=FAKE + 4, mb=mb) == pkv.PKV_ERR_ALIGN
+    assert call(p, o=FAKE, ob=ob, ml=FAKE + 8, mb=mb) == pkv.PKV_ERR_ALIGN
     assert pkv.workspace_bytes(p, 1) == (0, 0)
     with pytest.raises(pkv.PkvError):
         pkv.workspace_bytes(p, 0)
@@ -175,3 +178,16 @@ def test_status_strings_are_distinct():
 def test_problem_struct_layout():
     assert ctypes.sizeof(pkv.Problem) == 64
     assert pkv.Problem.mask_stride_b.offset == 48
+
+
+def test_workspace_clear_checks():
+    assert pkv.workspace_clear_raw(0, 0, 0) == pkv.PKV_OK          # nothing to clear
+    assert pkv.workspace_clear_raw(0, 64, 0) == pkv.PKV_ERR_NULL
+    assert pkv.workspace_clear_raw(FAKE + 2, 64, 0) == pkv.PKV_ERR_ALIGN
+    assert pkv.workspace_clear_raw(FAKE, 66, 0) == pkv.PKV_ERR_ALIGN
+
+
+def test_grid_beyond_32bit_work_items_is_rejected():
+    # 2^23 sequences x 2 kv heads = 2^24 workgroups of 256 threads: 2^32 work-items
+    assert call(base_problem(batch=1 << 23, num_splits=1)) == pkv.PKV_ERR_SHAPE
+    assert pkv.combine_raw((1 << 25) * 2 + 8, 2, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_SHAPE

@@ -12,7 +12,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, dev_tensors, note, problem, run  # noqa: E402
+from gpu_util import check, dev_tensors, note, problem, run, sub_batch  # noqa: E402
 
 
 def permute_pages(w, seed):
@@ -153,9 +153,7 @@ def test_graph_capture_replay_matches_eager():
                         kv_lens=[1500, 900, 64, 1000], seed=3080, mask="2d")
     d = dev_tensors(w)
     p = problem(w, num_splits=4)
-    ob, mb = pkv.workspace_bytes(p, 4)
-    o_part = torch.empty(ob // 4, dtype=torch.float32, device="cuda:0")
-    ml_part = torch.empty(mb // 4, dtype=torch.float32, device="cuda:0")
+    o_part, ml_part = pkv.alloc_workspace(p, 4, "cuda:0")
     out = torch.empty(tuple(d["q"].shape), dtype=torch.bfloat16, device="cuda:0")
     out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
 
@@ -228,6 +226,8 @@ def test_guard_bands_untouched():
     buf32 = torch.full((n + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
     bufo = torch.full((ob // 4 + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
     bufm = torch.full((mb // 4 + 2 * G,), sent32, dtype=torch.float32, device="cuda:0")
+    H = pkv.PKV_COUNTER_BYTES // 4
+    bufm[G:G + H].zero_()          # the counter head starts at zero ...
     out = buf16[G:G + n].view(torch.bfloat16).view(d["q"].shape)
     out32 = buf32[G:G + n].view(d["q"].shape)
     pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale, causal_offsets=d["co"],
@@ -237,6 +237,7 @@ def test_guard_bands_untouched():
     for buf, val in ((buf16, 0x5A5A), (buf32, sent32), (bufo, sent32), (bufm, sent32)):
         h = buf.cpu().numpy()
         assert (h[:G] == val).all() and (h[-G:] == val).all()
+    assert not bufm[G:G + H].any().item()   # ... and the call leaves it at zero
     check(out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), oracle.decode(w), "canary")
 
 
@@ -259,3 +260,98 @@ def test_combine_entry_point_on_hand_made_partials():
     torch.cuda.synchronize()
     check(out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref, "combine")
     assert not out32[3].any()
+
+
+def _partials_then_combine(w, d, S):
+    """The two-launch path: pkv_paged_decode_partials, then pkv_combine."""
+    p = problem(w, num_splits=S)
+    ob, mb = pkv.partials_bytes(p, S)
+    o_part = torch.empty(ob // 4, dtype=torch.float32, device="cuda:0")
+    ml_part = torch.empty(mb // 4, dtype=torch.float32, device="cuda:0")
+    pkv.paged_decode_partials(d["q"], d["k"], d["v"], d["bt"], d["kl"], o_part=o_part, ml_part=ml_part,
+                              problem=p, causal_offsets=d["co"], mask=d["mask"])
+    rows = w.B * w.q_len * w.Hq
+    out32 = torch.empty((rows, w.D), dtype=torch.float32, device="cuda:0")
+    out = pkv.combine(o_part, ml_part, rows=rows, splits=S, head_dim=w.D, out_f32=out32)
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]),              # VALU, R=4
+    dict(B=2, q_len=2, Hq=16, Hkv=2, D=64, page_size=16, kv_lens=[900, 77], causal="last"),      # MFMA, R=16
+    dict(B=2, q_len=1, Hq=48, Hkv=1, D=256, page_size=64, kv_lens=[700, 1000], mask="2d"),        # MFMA, R=48
+])
+@pytest.mark.parametrize("S", [2, 7, 64])
+def test_in_kernel_merge_equals_separate_combine(shape, S):
+    """pkv_paged_decode (in-kernel merge by the last workgroup of each unit,
+    or the combine kernel for larger grids) equals the split step followed by
+    pkv_combine bit for bit: both merges run the same code in split order."""
+    w = workloads.build("fusedeq", seed=3200 + S, **shape)
+    d = dev_tensors(w)
+    note(f"fusedeq S={S} in-kernel merge: {pkv.merges_in_kernel(problem(w, S), S)}")
+    a16, a32 = run(w, d, num_splits=S)
+    b16, b32 = _partials_then_combine(w, d, S)
+    shp = a32.shape
+    assert np.array_equal(a16, b16.reshape(shp))
+    assert np.array_equal(a32.view(np.uint32), b32.reshape(shp).view(np.uint32))
+    check(a16, a32, oracle.decode(w), "fused")
+
+
+def test_many_units_use_the_combine_kernel():
+    """More than PKV_MAX_FUSED_UNITS units with several splits: split kernel +
+    combine kernel, with the (m, l) data after the counter head."""
+    B = pkv.PKV_MAX_FUSED_UNITS // 8 + 9
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 150, B)
+    w = workloads.build("manyunits", B=B, q_len=1, Hq=8, Hkv=8, D=32, page_size=16,
+                        kv_lens=lens, seed=3300)
+    assert w.B * w.Hkv > pkv.PKV_MAX_FUSED_UNITS
+    out16, out32 = run(w, num_splits=3)
+    seqs = [0, 1, int(np.argmax(lens)), B // 2, B - 1]
+    ref = oracle.decode(sub_batch(w, seqs))
+    check(out16[seqs], out32[seqs], ref, "manyunits")
+
+
+def test_one_workspace_serves_calls_of_any_shape():
+    """A workspace cleared once serves a sequence of calls of different shapes
+    and split counts (in-kernel merge and combine-kernel paths mixed); the
+    counter head is zero after every call."""
+    shapes = [
+        dict(B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[800, 20, 0, 1400]),
+        dict(B=600, q_len=1, Hq=8, Hkv=8, D=64, page_size=16, kv_lens=[70] * 600),  # 4800 units
+        dict(B=2, q_len=3, Hq=16, Hkv=2, D=64, page_size=8, kv_lens=[300, 41], causal="last"),
+        dict(B=1, q_len=1, Hq=8, Hkv=1, D=32, page_size=64, kv_lens=[5000]),
+    ]
+    ws = [workloads.build(f"reuse{i}", seed=3400 + i, **kw) for i, kw in enumerate(shapes)]
+    plans = [(w, S) for w in ws for S in (5, 2)]
+    need_o = max(pkv.workspace_bytes(problem(w, num_splits=S), S)[0] for w, S in plans)
+    need_m = max(pkv.workspace_bytes(problem(w, num_splits=S), S)[1] for w, S in plans)
+    o_part = torch.empty(need_o // 4, dtype=torch.float32, device="cuda:0")
+    ml_part = torch.empty(need_m // 4, dtype=torch.float32, device="cuda:0")
+    ml_part.fill_(3.5)
+    pkv.workspace_clear(ml_part)
+    torch.cuda.synchronize()
+    assert not ml_part.any().item()
+    H = pkv.PKV_COUNTER_BYTES // 4
+    for w, S in plans:
+        note(f"reuse {w.name} B={w.B} S={S}")
+        d = dev_tensors(w)
+        p = problem(w, num_splits=S)
+        out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
+        out = pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale,
+                               causal_offsets=d["co"], mask=d["mask"], out_f32=out32,
+                               o_part=o_part, ml_part=ml_part, problem=p)
+        torch.cuda.synchronize()
+        assert not ml_part[:H].any().item()
+        seqs = list(range(min(w.B, 6)))
+        ref = oracle.decode(sub_batch(w, seqs))
+        check(out.view(torch.int16).cpu().numpy().view(np.uint16)[seqs], out32.cpu().numpy()[seqs], ref,
+              w.name)
+
+
+def test_both_merge_paths_are_exercised():
+    shapes = [(dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 7),
+              (dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 64)]
+    flags = [pkv.merges_in_kernel(problem(workloads.build("paths", seed=1, **kw), S), S) for kw, S in shapes]
+    assert flags == [True, False]
