@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
 """Paged-KV split-KV decode attention benchmark on one MI355X.
 
-One step = one full decode call (split kernel, plus the combine kernel when
-more than one split is used) over one batch of synthetic, seeded input that
-is already resident in HBM.  The default workload is the 1B-model decode shape
-(B=8, Hq=24, Hkv=4, D=64, page 32, kv_lens uniform on [128, 2048]);
-``--workload`` selects the other decode shapes.
+One step = one full pkv_paged_decode call (the split kernel, which also
+merges the splits for small grids, or the split kernel then the combine
+kernel) over one batch of synthetic, seeded input that is already resident in
+HBM.  The default workload is the 1B-model decode shape (B=8, Hq=24, Hkv=4,
+D=64, page 32, kv_lens uniform on [128, 2048]); ``--workload`` selects the
+other decode shapes.
 
-Protocol: W untimed warmup steps; then K timed steps back to back on one
-stream, each reading a different replica of the K/V pools (same logical
-content, different addresses, replicas spanning >= 1 GiB so no step finds its
-K/V in L2 or the 256 MB Infinity Cache).  A spin kernel queued first keeps the
-host's launches ahead of the GPU, so the HIP events measure GPU time.  Events
-between the kernels give each kernel's own average duration (on the stream
-the kernels run on).  Prints one JSON line.
+Protocol: W untimed warmup steps; then K timed eager steps back to back on
+one stream, bracketed by two HIP events (median of --runs repetitions), each
+step reading a different replica of the K/V pools (same logical content,
+different addresses, replicas spanning >= 1 GiB so no step finds its K/V in
+L2 or the 256 MB Infinity Cache).  A spin kernel queued first keeps the host's
+launches ahead of the GPU, so the events measure GPU time.  `value` is K/V
+bytes per call over that eager time per call.  The dominant kernel's own
+average duration (for the roofline) comes from a hipGraph of back-to-back
+launches of that kernel alone, replayed between two events on its stream.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -38,19 +42,6 @@ def kernel_name(w, S, prob) -> str:
     return pkv.kernel_family(prob)
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources; counter figures taken on other sources
-    are stale."""
-    import hashlib
-    csrc = os.path.join(ROOT, "paged_kv_split_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload: str):
     """HBM bytes per call from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or
@@ -61,9 +52,25 @@ def measured_traffic(workload: str):
     with open(path) as fh:
         data = json.load(fh)
     e = data.get("workloads", {}).get(workload)
+    from paged_kv_split_amd.profiling import source_digest
     if not e or data.get("source_digest") != source_digest():
         return None
     return e["hbm_bytes_per_call"]
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the split kernel must move at minimum in one call: the K and V
+    rows of every visible key, q, the bf16 output, the block-table entries of
+    the pages in use and, when present, the mask entries of those keys."""
+    import numpy as np
+    L = w.kv_lens.astype(np.int64)
+    kv = int(L.sum()) * w.Hkv * w.D * 2 * 2
+    qo = w.B * w.q_len * w.Hq * w.D * 2 * 2
+    bt = int(((L + w.page_size - 1) // w.page_size).sum()) * 4
+    mask = 0
+    if w.mask is not None:
+        mask = int(L.sum()) * 4 * (w.q_len if w.mask.ndim == 3 else 1)
+    return kv + qo + bt + mask
 
 
 def make_workload(name: str):
@@ -222,63 +229,103 @@ def main():
     sleep_ms_per_unit = e0.elapsed_time(e1) / 1_000_000
     spin = int(min(2.0 * host_per_step * args.steps * 1e3 / max(sleep_ms_per_unit, 1e-9), 2**31 - 1))
 
-    def timed(rotate=True):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    def timed(fn, rotate=True):
+        """ms per call of `steps` back-to-back eager calls, bracketed by two events."""
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         torch.cuda._sleep(spin)
         start.record()
         for i in range(args.steps):
-            r = i % n_rep if rotate else 0
-            ev[i][0].record()
-            step(r)
-            ev[i][1].record()
+            fn(i % n_rep if rotate else 0)
         end.record()
         torch.cuda.synchronize()
-        total = start.elapsed_time(end)
-        call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-        return total, call_ms
+        return start.elapsed_time(end) / args.steps
 
-    runs = [timed(True) for _ in range(max(1, args.runs))]
-    total_ms = statistics.median(r[0] for r in runs)
-    call_ms = statistics.median(r[1] for r in runs)
-    warm = timed(False)
+    runs = [timed(step) for _ in range(max(1, args.runs))]
+    call_ms = statistics.median(runs)
+    warm_ms = timed(step, rotate=False)
     print("bench: timed runs done", file=sys.stderr, flush=True)
 
-    graph_us = None
-    if not args.no_graph:
+    def graph_ms(fn):
+        """ms per launch when one call per replica (up to 64) is captured into
+        a hipGraph and the graph is replayed back to back, bracketed by two
+        events on the stream the kernels run on: the launches' own average
+        duration, without the host's per-launch gaps."""
+        nonlocal sh
+        nrep_g = min(n_rep, 64)
+        cur = torch.cuda.current_stream()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(cur)
+        g = torch.cuda.CUDAGraph()
+        saved = sh
         try:
-            nrep_g = min(n_rep, 64)
-            gs = torch.cuda.Stream()
-            gs.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            sh_saved = sh
             with torch.cuda.stream(gs):
-                sh = int(gs.cuda_stream)        # step() launches on the capture stream
+                sh = int(gs.cuda_stream)        # the raw calls launch on the capture stream
                 with torch.cuda.graph(g, stream=gs):
                     for r in range(nrep_g):
-                        step(r)
-            sh = sh_saved
-            torch.cuda.current_stream().wait_stream(gs)
-            torch.cuda.synchronize()
+                        fn(r)
+        finally:
+            sh = saved
+        cur.wait_stream(gs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // nrep_g)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
             g.replay()
-            torch.cuda.synchronize()
-            reps = max(1, args.steps // nrep_g)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            graph_us = a.elapsed_time(b) * 1e3 / (reps * nrep_g)
-        except Exception as ex:  # graph timing is a side figure; report why it is missing
-            print(f"bench: graph replay skipped: {ex}", file=sys.stderr, flush=True)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * nrep_g)
+
+    # The dominant kernel's own average duration: the whole call when it is
+    # one kernel; otherwise the split kernel alone (the same kernel, run
+    # through pkv_paged_decode_partials), and the combine kernel alone.
+    n_kernels = 1 if (S == 1 or pkv.merges_in_kernel(prob, S)) else 2
+    rows = w.B * w.q_len * w.Hq
+    pob, pmb = pkv.partials_bytes(prob, S)
+    po2 = torch.empty(max(pob // 4, 4), dtype=torch.float32, device=dev)
+    pm2 = torch.empty(max(pmb // 4, 4), dtype=torch.float32, device=dev)
+
+    def split_only(r):
+        st = pkv.paged_decode_partials_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3],
+                                           base[4], P(po2), pob, P(pm2), pmb, sh)
+        if st:
+            raise pkv.PkvError(st, "pkv_paged_decode_partials")
+
+    def combine_only(r):
+        st = pkv.combine_raw(rows, S, w.D, P(po2), P(pm2), P(out), 0, sh)
+        if st:
+            raise pkv.PkvError(st, "pkv_combine")
+
+    if n_kernels == 2:
+        split_only(0)
+        combine_only(0)
+    timing = "graph"
+    graph_call_ms = split_ms = None
+    comb_ms = 0.0
+    if not args.no_graph:
+        try:
+            graph_call_ms = graph_ms(step)
+            if n_kernels == 1:
+                split_ms = graph_call_ms
+            else:
+                split_ms = graph_ms(split_only)
+                comb_ms = graph_ms(combine_only)
+        except Exception as ex:  # report why, and fall back to eager timing
+            print(f"bench: graph timing unavailable: {ex}", file=sys.stderr, flush=True)
+            graph_call_ms = split_ms = None
+    if split_ms is None:
+        timing = "eager"
+        split_ms = call_ms if n_kernels == 1 else timed(split_only)
+        comb_ms = 0.0 if n_kernels == 1 else timed(combine_only)
 
     kv_bytes = w.kv_bytes()
-    us_call = total_ms * 1e3 / args.steps
+    us_call = call_ms * 1e3
     gbs = kv_bytes / (us_call * 1e-6) / 1e9
-    kern_gbs = kv_bytes / (call_ms * 1e-3) / 1e9
-    n_kernels = 1 if (S == 1 or pkv.merges_in_kernel(prob, S)) else 2
+    algo = algorithmic_bytes(w)
+    kern_gbs = algo / (split_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -286,7 +333,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 6),
+        "ms_per_step": round(call_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -296,9 +343,11 @@ def main():
         "us_per_call": round(us_call, 3),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "kernels_per_call": n_kernels,
-        "call_us_events": round(call_ms * 1e3, 3),
-        "warm_us_per_call": round(warm[0] * 1e3 / args.steps, 3),
-        "graph_us_per_call": None if graph_us is None else round(graph_us, 3),
+        "kernel_us": {"split": round(split_ms * 1e3, 3), "combine": round(comb_ms * 1e3, 3),
+                      "timing": timing},
+        "algorithmic_bytes_per_call": algo,
+        "warm_us_per_call": round(warm_ms * 1e3, 3),
+        "graph_us_per_call": None if graph_call_ms is None else round(graph_call_ms * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
         "roofline": {"bound": "hbm", "kernel": kernel_name(w, S, prob), "achieved": round(kern_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),

@@ -1,0 +1,39 @@
+#!/bin/bash
+# Collect, for each bench.py workload named, a rocprofv3 kernel trace with
+# per-kernel statistics and two counter passes (FETCH_SIZE, then WRITE_SIZE),
+# plus the same two counters for a plain 1 GiB device copy (calibration).
+# usage: bash paged_kv_split_amd/profiling/collect.sh OUTDIR WORKLOAD...
+set -u
+cd "$(dirname "$0")/../.." || exit 1
+export TMPDIR=/tmp
+out=$1
+shift
+mkdir -p "$out"
+BENCH="python3 -u bench.py --warmup 3 --runs 1 --no-cpu-baseline"
+
+step() {  # step TAG LIMIT_SECONDS COMMAND...
+  local tag=$1 lim=$2
+  shift 2
+  echo "step $tag" >&2
+  timeout -s KILL "$lim" "$@" > "$out/$tag.out" 2> "$out/$tag.log"
+  local rc=$?
+  if [ $rc -ne 0 ]; then
+    echo "failed: $tag (status $rc)" >&2
+    tail -5 "$out/$tag.log" >&2
+    exit $rc
+  fi
+}
+
+step copy_fetch 120 rocprofv3 --pmc FETCH_SIZE -d "$out/copy_fetch" -o copy_fetch --output-format csv -- \
+  python3 -u bench.py --copy-calibration 1073741824
+step copy_write 120 rocprofv3 --pmc WRITE_SIZE -d "$out/copy_write" -o copy_write --output-format csv -- \
+  python3 -u bench.py --copy-calibration 1073741824
+for wl in "$@"; do
+  step "${wl}_trace" 300 rocprofv3 --kernel-trace --stats -d "$out/${wl}_trace" -o trace --output-format csv -- \
+    $BENCH --workload "$wl" --steps 20
+  step "${wl}_fetch" 120 rocprofv3 --pmc FETCH_SIZE -d "$out/${wl}_fetch" -o fetch --output-format csv -- \
+    $BENCH --workload "$wl" --steps 4
+  step "${wl}_write" 120 rocprofv3 --pmc WRITE_SIZE -d "$out/${wl}_write" -o write --output-format csv -- \
+    $BENCH --workload "$wl" --steps 4
+done
+echo "collected in $out" >&2
