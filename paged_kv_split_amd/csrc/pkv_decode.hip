@@ -121,7 +121,7 @@ struct Layout {
   static constexpr int SW_SHIFT = LPK >= 4 ? 0 : (LPK == 2 ? 1 : 2);
   static constexpr int SW_MASK = LPK >= 8 ? 1 : 3;
   __device__ static int kslot(int ch, int row) { return ch ^ (SW_MUL * ((row >> SW_SHIFT) & SW_MASK)); }
-  static constexpr int MERGE = NW * RP * D + NW * RP * 2;
+  static constexpr int MERGE = NW * RP * D + NW * RP * 2 + RP * 2 + NW * RP;
   static constexpr int QLDS = QREG ? 0 : RP * D / 2;  // q rows as packed bf16 pairs (floats)
   static constexpr int MAIN = kBtCap + 4 + QLDS + PBUF + KBUF;  // page-table slice (+1 page when a window
                                                          // starts mid-page), q, p slices
@@ -389,6 +389,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, LPK = Lay::LPK, T = Lay::T, LPV = Lay::LPV;
   __shared__ __attribute__((aligned(16))) float smem[Lay::SMEM];
+  __shared__ int64_t rowtab[RP];  // output row of each packed row of the block
 
   // ---- unit decode (XCD-aware): siblings (kv head, row block) of one
   // (b, split) unit get consecutive slots on the same XCD
@@ -508,6 +509,10 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
     for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
   };
+  if (threadIdx.x < RP) {
+    const int rr = r0 + threadIdx.x;
+    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, g, rr) : 0;
+  }
   load_bt(c.kb);
   __syncthreads();
   for (int wb = c.kb; wb < kend; wb += win_keys) {
@@ -553,51 +558,49 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
       mlb[(w * RP + r) * 2 + 1] = l_tot[r];
     }
   }
+  float *rmw = mlb + NW * RP * 2;      // [RP][2]: merged (M, W) per row
+  float *fw = rmw + RP * 2;            // [NW][RP]: normalised wave factors
   __syncthreads();
-  auto Mrow = [&](int r) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww)
-      if (mlb[(ww * RP + r) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(ww * RP + r) * 2]);
-    return M;
-  };
-  auto Wrow = [&](int r) {
-    const float M = Mrow(r);
-    float W = 0.f;
+  if (threadIdx.x < RP) {
+    const int r = threadIdx.x;
+    float mw[NW], lw[NW], f[NW], M, W;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float lw = mlb[(ww * RP + r) * 2 + 1];
-      if (lw > 0.f) W = fmaf(fast_exp2(mlb[(ww * RP + r) * 2] - M), lw, W);
+      mw[ww] = mlb[(ww * RP + r) * 2];
+      lw[ww] = mlb[(ww * RP + r) * 2 + 1];
     }
-    return W;
-  };
-  auto res = [&](int r, int d) {
-    const float M = Mrow(r);
+    wave_factors<NW>(mw, lw, M, W, f);
+    rmw[2 * r] = M;
+    rmw[2 * r + 1] = W;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) fw[ww * RP + r] = f[ww];
+  }
+  __syncthreads();
+  auto Mrow = [&](int r) { return rmw[2 * r]; };
+  auto Wrow = [&](int r) { return rmw[2 * r + 1]; };
+  auto resn = [&](int r, int d) {
     float o = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww)
-      if (mlb[(ww * RP + r) * 2 + 1] > 0.f) o = fmaf(fast_exp2(mlb[(ww * RP + r) * 2] - M), ob[(ww * RP + r) * D + d], o);
+    for (int ww = 0; ww < NW; ++ww) o = fmaf(fw[ww * RP + r], ob[(ww * RP + r) * D + d], o);
     return o;
   };
   const int nrows = a.R - r0 < RP ? a.R - r0 : RP;
-  write_rows<D>(a, b, g, s, r0, nrows, res, Mrow, Wrow, NW * 64);
-  fused_tail<D>(a, b, g, (b * a.Hkv + g) * a.nrb + rb, r0, nrows, smem, NW * 64);
+  write_rows<D>(a, s, rowtab, nrows, resn, Mrow, Wrow, NW * 64);
+  fused_tail<D>(a, (b * a.Hkv + g) * a.nrb + rb, rowtab, nrows, smem, NW * 64);
 }
 
 // Combine (the standalone pkv_combine entry point): each block merges
-// combine_rows(D) consecutive rows (about 512 element pairs, so every thread
-// has work) with the same merge code as the split kernels' in-kernel merge.
-constexpr int combine_rows(int D) { return 512 / D; }
+// combine_rows(D) consecutive rows (one 4-element group per thread) with the
+// same merge code as the split kernels' in-kernel merge.
+constexpr int combine_rows(int D) { return 1024 / D; }
 
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   constexpr int NR = combine_rows(D);
-  __shared__ float lds[NR * (kMaxSplits + 1)];
   const int64_t base = (int64_t)blockIdx.x * NR;
   const int64_t left = a.rows - base;
   const int nrows = left < NR ? (int)left : NR;
-  merge_rows<D, false>(a.o_part, a.ml_part, a.S, [&](int r) { return base + r; }, nrows, a.out, a.out_f32, lds,
-                       256);
+  merge_rows<D, false>(a.o_part, a.ml_part, a.S, [&](int r) { return base + r; }, nrows, a.out, a.out_f32, 256);
 }
 
 // Zero-fill (workspace counters); a kernel, not a memset, so it may sit in a

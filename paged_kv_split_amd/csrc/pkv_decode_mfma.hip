@@ -54,7 +54,7 @@ struct MLay {
   static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
   static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
-  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4 + 16 * 2 * 4;
+  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4 + 16 * 2 * 4 + NW * 16 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
   static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   // swizzles (16-byte chunk index within a row)
@@ -260,10 +260,14 @@ __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b,
   mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
 }
 
-// The key-tile loop of one wave: two register tiles; a tile goes to LDS,
-// then the loads of the tile two steps ahead are issued into the freed
-// registers, so the next tile's loads are in flight while this one computes.
-template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
+// Register tiles per wave: two (one at D = 256, where two would spill).
+// Four were measured slower at every D < 256, even where the occupancy
+// stayed the same.
+template <int D, int NRB>
+constexpr int mfma_nbuf() { return D >= 256 ? 1 : 2; }
+
+// The key-tile loop of one wave.
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE, int NBUF = mfma_nbuf<D, NRB>()>
 __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int t0,
                                            int ntiles, const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB],
                                            uint16_t *kt, uint16_t *vt, int lane, MState<D, NRB> &st) {
@@ -278,15 +282,22 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
                                          lane, st);
     return;
   }
-  MTile<D, NRB, MASK> ta, tb;
-  if (t0 < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, ta);
-  if (t0 + NW < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + NW) * KT, lane, tb);
-  for (int t = t0; t < ntiles; t += 2 * NW) {
-    mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + 2 * NW < ntiles ? t + 2 * NW : -1, ta, qb, lim, kt,
-                                       vt, lane, st);
-    if (t + NW >= ntiles) break;
-    mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t + NW, t + 3 * NW < ntiles ? t + 3 * NW : -1, tb, qb, lim,
-                                       kt, vt, lane, st);
+  // NBUF register tiles in a ring: tile t sits in buffer (t / NW) % NBUF; a
+  // tile goes to LDS, then the loads of the tile NBUF steps ahead are issued
+  // into the freed registers
+  MTile<D, NRB, MASK> tr[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i)
+    if (t0 + i * NW < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * KT, lane, tr[i]);
+  for (int t = t0; t < ntiles; t += NBUF * NW) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      const int tt = t + i * NW;
+      if (tt >= ntiles) break;
+      const int tn = tt + NBUF * NW;
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tn < ntiles ? tn : -1, tr[i], qb, lim, kt, vt, lane,
+                                         st);
+    }
   }
 }
 
@@ -301,6 +312,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   constexpr int NW = L::NW;
   constexpr int RW = 16 * NRB;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[L::SMEM_BYTES];
+  __shared__ int64_t rowtab[RW];  // output row of each packed row of the block
 
   const int x = blockIdx.x;
   const int xcd = x & 7;
@@ -391,6 +403,10 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
     for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  if (threadIdx.x < RW) {
+    const int rr = r0 + threadIdx.x;
+    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, g, rr) : 0;
+  }
   load_bt(kb);
   __syncthreads();
   for (int wb = kb; wb < kend; wb += win_keys) {
@@ -415,6 +431,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][OB_STRIDE]
   float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW][32][2]
   float *rmw = mlb + NW * 32 * 2;                         // [16][2]: merged (M, W) per row
+  float *fw = rmw + 16 * 2;                               // [NW][16]: normalised wave factors
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     __syncthreads();
@@ -431,38 +448,31 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
     __syncthreads();
     if (threadIdx.x < 16) {
       const int r = threadIdx.x;
-      float M = -INFINITY;
+      float mw[NW], lw[NW], f[NW], M, W;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww)
-        if (mlb[(ww * 32 + 16 * rb + r) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(ww * 32 + 16 * rb + r) * 2]);
-      float W = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float lw = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
-          if (lw > 0.f) W = fmaf(fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M), lw, W);
-        }
+      for (int ww = 0; ww < NW; ++ww) {
+        mw[ww] = mlb[(ww * 32 + 16 * rb + r) * 2];
+        lw[ww] = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
       }
+      wave_factors<NW>(mw, lw, M, W, f);
       rmw[2 * r] = M;
       rmw[2 * r + 1] = W;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) fw[ww * 16 + r] = f[ww];
     }
     __syncthreads();
     auto Mrow = [&](int r) { return rmw[2 * r]; };
     auto Wrow = [&](int r) { return rmw[2 * r + 1]; };
-    auto res = [&](int r, int d) {
-      const float M = rmw[2 * r];
+    auto resn = [&](int r, int d) {
       float o = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float lw = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
-        if (lw > 0.f) o = fmaf(fast_exp2(mlb[(ww * 32 + 16 * rb + r) * 2] - M), ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
-      }
+      for (int ww = 0; ww < NW; ++ww) o = fmaf(fw[ww * 16 + r], ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
       return o;
     };
     const int rs = r0 + 16 * rb;
-    write_rows<D>(a, b, g, s, rs, a.R - rs < 16 ? a.R - rs : 16, res, Mrow, Wrow, NW * 64);
+    write_rows<D>(a, s, rowtab + 16 * rb, a.R - rs < 16 ? a.R - rs : 16, resn, Mrow, Wrow, NW * 64);
   }
-  fused_tail<D>(a, b, g, (b * a.Hkv + g) * a.nrb + rg, r0, a.R - r0 < RW ? a.R - r0 : RW,
+  fused_tail<D>(a, (b * a.Hkv + g) * a.nrb + rg, rowtab, a.R - r0 < RW ? a.R - r0 : RW,
                 reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 

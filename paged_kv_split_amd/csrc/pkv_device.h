@@ -125,110 +125,140 @@ __device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, in
 }
 
 // ---- log-sum-exp merge of split partials -----------------------------------
-// For each of `nrows` rows (row index rowf(r)):  M = max over partials with
-// l_s > 0 of m_s,  w_s = l_s exp(m_s - M),  W = sum_s w_s,
-// out = sum_s w_s o_s / W  (0 when W = 0).  The sum over s runs in split
-// order 0..S-1 and skips w_s = 0, so the o_part rows of empty partials are
-// never used (nor do rows with W = 0 use any).  Both the in-kernel merge and
-// the combine kernel run this code, so their results are bit-identical.  Run by a whole block of nthreads
-// threads; `lds` holds nrows * (S + 1) floats (nrows * S <= kMaxMergeWeights).
-// DEV: the partials were written by other workgroups of the running launch.
-constexpr int kMergeBatch = 16;  // partial rows loaded together per thread
+// For each of `nrows` rows (row index rowf(r)) and each 4-element group of
+// its D outputs, one thread walks the S partials in split order 0..S-1 with
+// an online merge: partials with l_s = 0 are skipped (their o rows are never
+// used); otherwise, when m_s exceeds the running max M the running sums are
+// rescaled by exp(M - m_s), then w_s = l_s exp(m_s - M) is added to W and
+// w_s o_s to the accumulator.  out = acc * (1 / W), 0 when W = 0.  This is
+// the log-sum-exp rule M = max m_s, out = sum_s l_s e^(m_s - M) o_s / sum_s
+// l_s e^(m_s - M), evaluated in one pass.  Each thread loads the (m, l) of
+// the splits itself, so no LDS and no barrier are needed.  Both the in-kernel
+// merge and the combine kernel run this code, so their results are
+// bit-identical.  Run by nthreads threads (any number); rowf must be cheap
+// (it is evaluated once per group).  DEV: the partials were written by other
+// workgroups of the running launch.
+constexpr int kMergeBatch = 16;  // partials in flight per thread
 
-template <int D, bool DEV, class RowF>
-__device__ void merge_rows(const float *o_part, const float *ml_part, int S, RowF rowf, int nrows, uint16_t *out,
-                           float *out_f32, float *lds, int nthreads) {
-  constexpr int SPL = kMaxSplits / 64;  // splits per lane
-  constexpr int DP = D / 2;             // element pairs per row
-  constexpr int NB = kMergeBatch;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int nwaves = nthreads >> 6;
-  float *rowW = lds;        // [nrows]
-  float *wt = lds + nrows;  // [nrows][S] split weights
-
-  // first batch of this thread's first element pair, issued before the weights
-  float2 ov[NB];
-  if (tid < nrows * DP) {
-    const int r = tid / DP;
-    const float *op = o_part + rowf(r) * S * D + 2 * (tid - r * DP);
-#pragma unroll
-    for (int k = 0; k < NB; ++k) ov[k] = k < S ? load2<DEV>(op + k * D) : make_float2(0.f, 0.f);
-  }
-
-  for (int r = wv; r < nrows; r += nwaves) {
-    const float *ml = ml_part + rowf(r) * S * 2;
-    float2 v[SPL];
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < SPL; ++k) {
-      const int sidx = lane + 64 * k;
-      v[k] = sidx < S ? load2<DEV>(ml + 2 * sidx) : make_float2(-INFINITY, 0.f);
-      if (v[k].y > 0.f) M = fmaxf(M, v[k].x);
-    }
-    M = reduce_hi<0, OpMax>(M);
-    float W = 0.f;
-#pragma unroll
-    for (int k = 0; k < SPL; ++k) {
-      const float wk = (M != -INFINITY && v[k].y > 0.f) ? v[k].y * fast_exp2((v[k].x - M) * kLog2e) : 0.f;
-      if (lane + 64 * k < S) wt[r * S + lane + 64 * k] = wk;
-      W += wk;
-    }
-    W = reduce_hi<0, OpSum>(W);
-    if (lane == 0) rowW[r] = W;
-  }
-  __syncthreads();
-
-  for (int idx = tid; idx < nrows * DP; idx += nthreads) {
-    const int r = idx / DP;
-    const int d = 2 * (idx - r * DP);
-    const int64_t row = rowf(r);
-    const float *op = o_part + row * S * D + d;
-    const float *w = wt + r * S;
-    const float W = rowW[r];
-    float ox = 0.f, oy = 0.f;
-    for (int s0 = 0; s0 < S; s0 += NB) {
-      if (s0 > 0 || idx != tid) {
-#pragma unroll
-        for (int k = 0; k < NB; ++k) ov[k] = s0 + k < S ? load2<DEV>(op + (s0 + k) * D) : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        if (s0 + k < S) {
-          const float f = w[s0 + k];
-          if (f != 0.f) {
-            ox = fmaf(f, ov[k].x, ox);
-            oy = fmaf(f, ov[k].y, oy);
-          }
-        }
-      }
-    }
-    const float rx = W > 0.f ? ox / W : 0.f;
-    const float ry = W > 0.f ? oy / W : 0.f;
-    *reinterpret_cast<uint32_t *>(out + row * D + d) =
-        (uint32_t)f32_to_bf16_rne(rx) | ((uint32_t)f32_to_bf16_rne(ry) << 16);
-    if (out_f32) *reinterpret_cast<float2 *>(out_f32 + row * D + d) = make_float2(rx, ry);
+template <bool DEV>
+__device__ __forceinline__ float4 load4(const float *p) {  // p 16-byte aligned
+  if constexpr (DEV) {
+    const float2 lo = load2<true>(p);
+    const float2 hi = load2<true>(p + 2);
+    return make_float4(lo.x, lo.y, hi.x, hi.y);
+  } else {
+    return *reinterpret_cast<const float4 *>(p);
   }
 }
 
-// Epilogue shared by the split kernels once a block has its merged result for
-// packed rows r0 .. r0+nrows-1: `res(r, d)` (unnormalised), `Mrow(r)` (base-2
-// reference) and `Wrow(r)` (total weight).  One split: write the output.
-// Several splits: write this split's partial (o = res / W, m in natural-log
-// units, l = W); an empty split (W = 0) writes only (m, l) = (-inf, 0).
+template <int D, bool DEV, class RowF>
+__device__ void merge_rows(const float *o_part, const float *ml_part, int S, RowF rowf, int nrows, uint16_t *out,
+                           float *out_f32, int nthreads) {
+  constexpr int DQ = D / 4;  // 4-element groups per row (a power of two)
+  constexpr int NB = kMergeBatch;
+  const int tid = threadIdx.x;
+  // this thread's groups: tid, tid + nthreads, ...; its items: (group,
+  // split) pairs, group-major, split order within a group
+  const int ngroups = nrows * DQ;
+  const int mine = tid < ngroups ? (ngroups - 1 - tid) / nthreads + 1 : 0;
+  const int items = mine * S;
+  float4 ov[NB];
+  float2 mv[NB];
+  int ig = tid, isp = 0;
+  const float *ip = o_part, *im = ml_part;
+  auto group_start = [&](int gidx) {
+    const int r = gidx / DQ;
+    const int64_t row = rowf(r);
+    ip = o_part + row * S * D + 4 * (gidx - r * DQ);
+    im = ml_part + row * S * 2;
+  };
+  if (items > 0) group_start(ig);
+  auto issue = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (i0 + k < items) {
+        ov[k] = load4<DEV>(ip);
+        mv[k] = load2<DEV>(im);
+        if (++isp == S) {
+          isp = 0;
+          ig += nthreads;
+          if (i0 + k + 1 < items) group_start(ig);
+        } else {
+          ip += D;
+          im += 2;
+        }
+      }
+    }
+  };
+  issue(0);
+
+  float M = -INFINITY, W = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int cg = tid, csp = 0;
+  for (int i0 = 0; i0 < items; i0 += NB) {
+    if (i0 > 0) issue(i0);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (i0 + k < items) {
+        const float m = mv[k].x;
+        const float l = mv[k].y;
+        if (l > 0.f) {
+          if (m > M) {
+            const float sc = fast_exp2((M - m) * kLog2e);
+            W *= sc;
+            acc.x *= sc;
+            acc.y *= sc;
+            acc.z *= sc;
+            acc.w *= sc;
+            M = m;
+          }
+          const float wk = l * fast_exp2((m - M) * kLog2e);
+          W += wk;
+          acc.x = fmaf(wk, ov[k].x, acc.x);
+          acc.y = fmaf(wk, ov[k].y, acc.y);
+          acc.z = fmaf(wk, ov[k].z, acc.z);
+          acc.w = fmaf(wk, ov[k].w, acc.w);
+        }
+        if (++csp == S) {
+          const int r = cg / DQ;
+          const int64_t row = rowf(r);
+          const int d = 4 * (cg - r * DQ);
+          const float inv = W > 0.f ? 1.f / W : 0.f;
+          const float4 res = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res.x) | ((uint32_t)f32_to_bf16_rne(res.y) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res.z) | ((uint32_t)f32_to_bf16_rne(res.w) << 16);
+          *reinterpret_cast<uint2 *>(out + row * D + d) = make_uint2(lo, hi);
+          if (out_f32) *reinterpret_cast<float4 *>(out_f32 + row * D + d) = res;
+          M = -INFINITY;
+          W = 0.f;
+          acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          csp = 0;
+          cg += nthreads;
+        }
+      }
+    }
+  }
+}
+
+// Epilogue shared by the split kernels once a block has merged its waves for
+// packed rows r0 .. r0+nrows-1: `rowtab[r]` is the output row of packed row
+// r0 + r, `resn(r, d)` the normalised result (0 when the row saw no key),
+// `Mrow(r)` the base-2 reference max and `Wrow(r)` the total weight.  One
+// split: write the output.  Several splits: write this split's partial
+// (o = resn, m in natural-log units, l = W); an empty split (W = 0) writes
+// only (m, l) = (-inf, 0).
 template <int D, class ResF, class MF, class WF>
-__device__ void write_rows(const DecodeArgs &a, int b, int g, int s, int r0, int nrows, ResF res, MF Mrow,
+__device__ void write_rows(const DecodeArgs &a, int s, const int64_t *rowtab, int nrows, ResF resn, MF Mrow,
                            WF Wrow, int nthreads) {
   constexpr int DP = D / 2;
   for (int idx = threadIdx.x; idx < nrows * DP; idx += nthreads) {
     const int r = idx / DP;
     const int d = 2 * (idx - r * DP);
-    const int64_t row = out_row(a, b, g, r0 + r);
+    const int64_t row = rowtab[r];
     const float W = Wrow(r);
     if (!a.partials) {
-      const float vx = W > 0.f ? res(r, d) / W : 0.f;
-      const float vy = W > 0.f ? res(r, d + 1) / W : 0.f;
+      const float vx = resn(r, d);
+      const float vy = resn(r, d + 1);
       *reinterpret_cast<uint32_t *>(a.out + row * D + d) =
           (uint32_t)f32_to_bf16_rne(vx) | ((uint32_t)f32_to_bf16_rne(vy) << 16);
       if (a.out_f32) *reinterpret_cast<float2 *>(a.out_f32 + row * D + d) = make_float2(vx, vy);
@@ -237,24 +267,44 @@ __device__ void write_rows(const DecodeArgs &a, int b, int g, int s, int r0, int
       float *pm = a.ml_part + (row * a.S + s) * 2;
       const float mx = W > 0.f ? Mrow(r) * kLn2 : -INFINITY;
       if (a.fused) {  // merged by another workgroup of this launch
-        if (W > 0.f) store_dev2(po, res(r, d) / W, res(r, d + 1) / W);
+        if (W > 0.f) store_dev2(po, resn(r, d), resn(r, d + 1));
         if (d == 0) store_dev2(pm, mx, W);
       } else {        // read after this kernel has ended
-        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(res(r, d) / W, res(r, d + 1) / W);
+        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(resn(r, d), resn(r, d + 1));
         if (d == 0) *reinterpret_cast<float2 *>(pm) = make_float2(mx, W);
       }
     }
   }
 }
 
+// Wave merge factors of one row: from the NW waves' (m, l) (base-2 m), the
+// row's reference max M, total weight W and each wave's normalised factor
+// exp2(m_w - M) / W (0 for waves that saw no key, all 0 when W = 0).
+template <int NW>
+__device__ __forceinline__ void wave_factors(const float (&m)[NW], const float (&l)[NW], float &M, float &W,
+                                             float (&f)[NW]) {
+  M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww)
+    if (l[ww] > 0.f) M = fmaxf(M, m[ww]);
+  W = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    f[ww] = (l[ww] > 0.f) ? fast_exp2(m[ww] - M) : 0.f;
+    W = fmaf(f[ww], l[ww], W);
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) f[ww] *= inv;
+}
+
 // With a.fused (several splits, one call): every block of a unit stores its
 // partial, waits for those stores to complete and counts itself in; the block
 // that arrives last merges the unit's partials and resets the counter, so the
-// workspace is ready for the next call.  `lds` holds at least
-// nrows * (S + 1) floats and is free (all block threads are past their last
-// use of it when this is called).
+// workspace is ready for the next call.  `lds` (one int) is free: all block
+// threads are past their last use of it when this is called.
 template <int D>
-__device__ void fused_tail(const DecodeArgs &a, int b, int g, int unit, int r0, int nrows, float *lds,
+__device__ void fused_tail(const DecodeArgs &a, int unit, const int64_t *rowtab, int nrows, float *lds,
                            int nthreads) {
   if (!a.fused) return;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
@@ -265,8 +315,8 @@ __device__ void fused_tail(const DecodeArgs &a, int b, int g, int unit, int r0, 
   const bool last = flag[0] != 0;
   __syncthreads();
   if (!last) return;
-  merge_rows<D, true>(a.o_part, a.ml_part, a.S, [&](int r) { return out_row(a, b, g, r0 + r); }, nrows, a.out,
-                      a.out_f32, lds, nthreads);
+  merge_rows<D, true>(a.o_part, a.ml_part, a.S, [&](int r) { return rowtab[r]; }, nrows, a.out, a.out_f32,
+                      nthreads);
   if (threadIdx.x == 0) a.counters[unit] = 0;  // ready for the next call
 }
 

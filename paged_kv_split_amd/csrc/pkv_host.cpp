@@ -266,14 +266,14 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->outer = (int32_t)outer;
   a->inner = (int32_t)inner;
   a->partials = (S > 1 || partials_only) ? 1 : 0;
-  // In-kernel merge (counters for every unit, merge weights of a workgroup's
-  // rows in LDS) when the grid is at most one workgroup per CU: then the
+  // In-kernel merge (a counter for every unit) when the grid is at most one
+  // workgroup per CU: then the
   // merging workgroups do not hold up waiting ones and the saved combine
   // launch is the larger cost.  Larger grids use the combine kernel, measured
   // faster there (the merge's device-scope traffic then runs under full HBM
   // load and on the kernel's critical path).
   a->fused = 0;
-  if (split_ws && units_of(p) <= PKV_MAX_FUSED_UNITS && (int64_t)rp * S <= pkv::kMaxMergeWeights) {
+  if (split_ws && units_of(p) <= PKV_MAX_FUSED_UNITS) {
     int cus = 0;
     if (query_cus(&cus) == PKV_OK && outer * inner <= cus) a->fused = 1;
   }

@@ -57,9 +57,6 @@ inline bool use_mfma(int R) { return R > 4; }
 int rows_per_block(int R);         // rows per workgroup: RP (VALU) or 16/32 (MFMA)
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
-// Rows x splits whose merge weights one workgroup holds in LDS: the split
-// kernels merge in-kernel only when rows_per_block * S stays within it.
-constexpr int kMaxMergeWeights = 2048;
 
 // Launchers (return a hipError_t value).
 int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
