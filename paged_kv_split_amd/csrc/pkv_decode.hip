@@ -188,7 +188,9 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
     }
   }
   if constexpr (UPAGE) {
-    const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
+    // a tile past the window end (an unconditional prefetch) reads the last key's page
+    const int bj = base < jlast ? base : jlast;
+    const int page = __builtin_amdgcn_readfirstlane(c.bt[(bj >> c.page_shift) - c.p0]);
     const int64_t pofs = (int64_t)page * c.page_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
@@ -365,21 +367,30 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
 }
 
 // The key-tile loop of one wave, double-buffered in registers: the next
-// tile's loads fly during this tile's compute.
+// tile's loads fly during this tile's compute.  The prefetch is issued
+// unconditionally (a tile past the end loads the last key again, clamped in
+// load_tile), so the number of loads in flight is the same on every path and
+// the wait before a tile's compute leaves the next tile's loads in flight; a
+// conditional prefetch makes the compiler wait for all loads there.
 template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int wb,
                                           int t0, int ntiles, const Q &qrows, const int (&lim)[RP], float *pbuf,
                                           float *kbuf, State<RP> &st) {
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, T = Lay::T;
+  if (t0 >= ntiles) return;
   Tile<D, RP, MASK> ta, tb;
-  int t = t0;
-  if (t < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + t * T, ta);
-  for (; t < ntiles; t += 2 * NW) {
-    if (t + NW < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + NW) * T, tb);
+  load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + t0 * T, ta);
+  // no early exit between the two halves: a half past the last tile computes
+  // a tile whose keys are all past the window end (weight 0); an exit there
+  // would give the loop a second path into its header and the compiler
+  // would then wait for all loads at the header
+  for (int t = t0; t < ntiles; t += 2 * NW) {
+    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + NW) * T, tb);
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, kbuf, st);
-    if (t + NW >= ntiles) break;
-    if (t + 2 * NW < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
+    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, kbuf, st);
   }
 }

@@ -88,7 +88,9 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
   const int ch = lane % L::LPR;
   const int jlast = c.ke - 1;
   if constexpr (UPAGE) {
-    const int page = __builtin_amdgcn_readfirstlane(c.bt[(base >> c.page_shift) - c.p0]);
+    // a tile past the window end (an unconditional prefetch) reads the last key's page
+    const int bj = base < jlast ? base : jlast;
+    const int page = __builtin_amdgcn_readfirstlane(c.bt[(bj >> c.page_shift) - c.p0]);
     const int64_t pofs = (int64_t)page * c.page_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
@@ -98,7 +100,9 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
       j = j < jlast ? j : jlast;
       const uint32_t off = (uint32_t)((j & c.pmask) * c.row_stride);
       t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + ch);
+      __builtin_amdgcn_sched_barrier(0);  // fixed issue order (see mtile_loop)
       t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + ch);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
@@ -108,7 +112,9 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
       const int page = c.bt[(j >> c.page_shift) - c.p0];
       const int64_t off = (int64_t)page * c.page_stride + (int64_t)(j & c.pmask) * c.row_stride;
       t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(c.kbase + off) + ch);
+      __builtin_amdgcn_sched_barrier(0);  // fixed issue order (see mtile_loop)
       t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(c.vbase + off) + ch);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (MASK) {
@@ -244,7 +250,7 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
 }
 
 // One pipeline step: tile tt (in registers tr) -> LDS; issue the loads of
-// tile tnext (if >= 0) into tr; compute tile tt from LDS.
+// tile tnext into tr; compute tile tt from LDS.
 template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
 __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int tt,
                                       int tnext, MTile<D, NRB, MASK> &tr, const uint4 (&qb)[NRB][D / 32],
@@ -256,7 +262,10 @@ __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b,
   for (int rb = 0; rb < (MASK ? NRB : 1); ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mk[rb][i] = MASK ? tr.mk[rb][i] : 0.f;
-  if (tnext >= 0) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + tnext * KT, lane, tr);
+  // unconditional (a tile past the end loads the last key again, clamped in
+  // mload): the loads in flight are then the same on every path, and the
+  // wait before the next tile leaves this prefetch in flight
+  mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + tnext * KT, lane, tr);
   mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
 }
 
@@ -275,28 +284,34 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
   if constexpr (D >= 256) {
     // one register tile (two would spill at D = 256): the next tile's loads
     // are issued right after this tile reaches LDS and fly during its compute
+    if (t0 >= ntiles) return;
     MTile<D, NRB, MASK> tr;
-    if (t0 < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, tr);
+    mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, tr);
     for (int t = t0; t < ntiles; t += NW)
-      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + NW < ntiles ? t + NW : -1, tr, qb, lim, kt, vt,
-                                         lane, st);
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + NW, tr, qb, lim, kt, vt, lane, st);
     return;
   }
   // NBUF register tiles in a ring: tile t sits in buffer (t / NW) % NBUF; a
   // tile goes to LDS, then the loads of the tile NBUF steps ahead are issued
   // into the freed registers
+  if (t0 >= ntiles) return;
   MTile<D, NRB, MASK> tr[NBUF];
+  // issue the tiles in order, not interleaved by the scheduler, so that the
+  // wait for tile i leaves the loads of tiles i+1.. in flight
 #pragma unroll
-  for (int i = 0; i < NBUF; ++i)
-    if (t0 + i * NW < ntiles) mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * KT, lane, tr[i]);
+  for (int i = 0; i < NBUF; ++i) {
+    mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * KT, lane, tr[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // no early exit inside a round: a step past the last tile computes a tile
+  // whose keys are all past the window end (weight 0); an exit there would
+  // give the loop a second path into its header and the compiler would then
+  // wait for all loads at the header
   for (int t = t0; t < ntiles; t += NBUF * NW) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
       const int tt = t + i * NW;
-      if (tt >= ntiles) break;
-      const int tn = tt + NBUF * NW;
-      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tn < ntiles ? tn : -1, tr[i], qb, lim, kt, vt, lane,
-                                         st);
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tt + NBUF * NW, tr[i], qb, lim, kt, vt, lane, st);
     }
   }
 }
