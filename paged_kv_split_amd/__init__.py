@@ -307,14 +307,14 @@ def units_of(problem: Problem) -> int:
 def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
     """Whether pkv_paged_decode with ``splits`` splits merges them inside the
     split kernel (mirrors the library's rule: several splits, at most
-    PKV_MAX_FUSED_UNITS units and at most one workgroup per CU) rather than
+    PKV_MAX_FUSED_UNITS units and at most two workgroups per CU) rather than
     launching the combine kernel."""
     if splits <= 1:
         return False
     if units_of(problem) > PKV_MAX_FUSED_UNITS:
         return False
     cus = num_cus if num_cus > 0 else device_cus()
-    return units_of(problem) * splits <= cus
+    return units_of(problem) * splits <= 2 * cus
 
 
 def kernel_family(problem: Problem) -> str:

@@ -84,12 +84,25 @@ int query_cus(int *out) {
 }
 
 // Split heuristic (keys only along the sequence axis, in the spirit of the
-// pages' compute_num_splits and ejkernel's num_splits = 0 "auto"): use one
-// split when the (sequence, kv-head, row-block) units already give every CU
-// several workgroups; otherwise split each sequence so the grid reaches about
-// kTargetPerCu workgroups per CU, never below kMinTilesPerWave tiles per wave.
-constexpr int kTargetPerCu = 4;
+// pages' compute_num_splits and ejkernel's num_splits = 0 "auto"): split each
+// sequence so that the grid has about blocks_per_cu() workgroups per CU (no
+// split when the (sequence, kv head, row block) units alone reach that),
+// never below kMinTilesPerWave tiles per wave and never above 64 splits.
 constexpr int kMinTilesPerWave = 2;
+
+// Workgroups per CU to aim at, measured on MI355X over the decode shapes:
+// one where a workgroup keeps enough K/V bytes in flight to cover memory
+// latency (VALU kernel: 8-16 KB tiles per wave; matrix-core kernel at
+// D = 128); two where a workgroup keeps fewer bytes in flight (matrix-core
+// 16-key tiles of 2-4 KB at D <= 64, a single register tile at D = 256) or
+// spends more VALU time per byte (four packed rows with a mask, hinted by a
+// nonzero mask stride).
+int blocks_per_cu(const pkv_problem *p) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  if (pkv::use_mfma(R)) return p->head_dim == 128 ? 1 : 2;
+  const bool mask_hint = p->mask_stride_b > 0 || p->mask_stride_q > 0;
+  return (pkv::rows_per_block(R) >= 4 && mask_hint) ? 2 : 1;
+}
 
 int heuristic_splits(const pkv_problem *p, int cus) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
@@ -97,12 +110,12 @@ int heuristic_splits(const pkv_problem *p, int cus) {
   const int64_t nrb = ceil_div(R, rp);
   const int64_t units = (int64_t)p->batch * p->num_kv_heads * nrb;
   if (units <= 0) return 1;
-  const int64_t target = (int64_t)cus * kTargetPerCu;
+  const int64_t target = (int64_t)cus * blocks_per_cu(p);
   if (units >= target) return 1;
   const int T = pkv::tile_keys(p->head_dim);
   const int64_t min_keys = (int64_t)T * pkv::kWavesPerBlock * kMinTilesPerWave;
   const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
-  int64_t s = ceil_div(target, units);
+  int64_t s = target / units;
   if (s > max_by_len) s = max_by_len;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -266,16 +279,15 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->outer = (int32_t)outer;
   a->inner = (int32_t)inner;
   a->partials = (S > 1 || partials_only) ? 1 : 0;
-  // In-kernel merge (a counter for every unit) when the grid is at most one
-  // workgroup per CU: then the
-  // merging workgroups do not hold up waiting ones and the saved combine
-  // launch is the larger cost.  Larger grids use the combine kernel, measured
-  // faster there (the merge's device-scope traffic then runs under full HBM
-  // load and on the kernel's critical path).
+  // In-kernel merge (a counter for every unit) when the grid has at most two
+  // workgroups per CU: the merging workgroups then hold up few others and the
+  // saved combine launch is the larger cost.  Larger grids use the combine
+  // kernel, measured faster there (the merge's device-scope traffic then runs
+  // under full HBM load and on the kernel's critical path).
   a->fused = 0;
   if (split_ws && units_of(p) <= PKV_MAX_FUSED_UNITS) {
     int cus = 0;
-    if (query_cus(&cus) == PKV_OK && outer * inner <= cus) a->fused = 1;
+    if (query_cus(&cus) == PKV_OK && outer * inner <= 2 * (int64_t)cus) a->fused = 1;
   }
   a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
   return PKV_OK;

@@ -137,15 +137,25 @@ def test_forced_splits_are_returned_unchanged():
 def test_split_heuristic_shapes():
     """Heuristic: one split when units fill the chip, more for few long sequences,
     bounded by the key count and 64."""
-    # B=256, Hkv=8, R=32 -> 4 row blocks: 8192 units >= 4*256 -> 1
+    # B=256, Hkv=8, R=32 -> 2 row blocks of 16: 4096 units >= 2*256 -> 1
     big = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
                        max_pages_per_seq=256, max_kv_len=8192, num_pages=13000)
     assert pkv.num_splits(big, 256) == 1
-    # B=4, Hkv=8, G=4 -> 32 units, 32768 keys -> splits to reach 1024 workgroups
+    # B=4, Hkv=8, G=4 (four rows, no mask) -> 32 units, 32768 keys -> one workgroup per CU
     long = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                         max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
-    s = pkv.num_splits(long, 256)
-    assert s == 32
+    assert pkv.num_splits(long, 256) == 8
+    # the same with a mask: two workgroups per CU
+    masked = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
+                          max_pages_per_seq=512, max_kv_len=32768, num_pages=2048, mask_stride_b=32768)
+    assert pkv.num_splits(masked, 256) == 16
+    # matrix-core rows (G=8) at D=64: two workgroups per CU; at D=128: one
+    mf64 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
+                        max_kv_len=4096, num_pages=2048)
+    assert pkv.num_splits(mf64, 256) == 4
+    mf128 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
+                         max_kv_len=4096, num_pages=2048)
+    assert pkv.num_splits(mf128, 256) == 2
     # short sequences cap the split count
     short = base_problem(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
                          max_kv_len=100)
