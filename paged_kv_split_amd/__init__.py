@@ -284,14 +284,12 @@ def partials_bytes(problem: Problem, splits: int) -> tuple[int, int]:
 
 
 def rows_per_block(R: int) -> int:
-    """Rows of one workgroup (mirrors the library): 1, 2 or 4 on the VALU
-    kernel (R <= 4), 16 or 32 on the matrix-core kernel."""
+    """Rows of one workgroup (mirrors the library): 1 or 2 on the VALU kernel
+    (R <= 2), 16 or 32 on the matrix-core kernel."""
     if R <= 1:
         return 1
     if R <= 2:
         return 2
-    if R <= 4:
-        return 4
     return 16 if R <= 16 else 32
 
 
@@ -320,7 +318,7 @@ def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
 def kernel_family(problem: Problem) -> str:
     """Which split kernel serves the problem (R = G * q_len rows per kv head)."""
     R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
-    return "split_decode_mfma" if R > 4 else "split_decode_valu"
+    return "split_decode_mfma" if R > 2 else "split_decode_valu"
 
 
 def num_splits_for(problem: Problem) -> int:

@@ -45,7 +45,6 @@ namespace pkv {
 int rows_per_block(int R) {
   if (R <= 1) return 1;
   if (R <= 2) return 2;
-  if (R <= 4) return 4;
   return R <= 16 ? 16 : 32;
 }
 
@@ -646,8 +645,7 @@ template <int D>
 hipError_t launch_d(const DecodeArgs &a, int rp, bool causal, bool mask, hipStream_t s) {
   switch (rp) {
     case 1: return launch_rp<D, 1>(a, causal, mask, s);
-    case 2: return launch_rp<D, 2>(a, causal, mask, s);
-    default: return launch_rp<D, 4>(a, causal, mask, s);
+    default: return launch_rp<D, 2>(a, causal, mask, s);
   }
 }
 

@@ -93,15 +93,12 @@ constexpr int kMinTilesPerWave = 2;
 // Workgroups per CU to aim at, measured on MI355X over the decode shapes:
 // one where a workgroup keeps enough K/V bytes in flight to cover memory
 // latency (VALU kernel: 8-16 KB tiles per wave; matrix-core kernel at
-// D = 128); two where a workgroup keeps fewer bytes in flight (matrix-core
-// 16-key tiles of 2-4 KB at D <= 64, a single register tile at D = 256) or
-// spends more VALU time per byte (four packed rows with a mask, hinted by a
-// nonzero mask stride).
+// D = 128), two where it keeps fewer (matrix-core 16-key tiles of 2-4 KB at
+// D <= 64) or has a single register tile (matrix-core kernel at D = 256).
 int blocks_per_cu(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
   if (pkv::use_mfma(R)) return p->head_dim == 128 ? 1 : 2;
-  const bool mask_hint = p->mask_stride_b > 0 || p->mask_stride_q > 0;
-  return (pkv::rows_per_block(R) >= 4 && mask_hint) ? 2 : 1;
+  return 1;
 }
 
 int heuristic_splits(const pkv_problem *p, int cus) {

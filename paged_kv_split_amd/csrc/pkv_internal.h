@@ -49,12 +49,12 @@ struct CombineArgs {
 };
 
 // Which split kernel serves a problem.  R = G * q_len rows share a kv head.
-// Up to 4 rows run on the VALU kernel (rows padded to RP in {1, 2, 4}); from
-// 5 rows on, the matrix-core kernel (16-row tiles, one or two per workgroup)
-// was measured faster on gfx950 even with half of a tile padded (R = 6, 8),
-// so it takes over there.
-inline bool use_mfma(int R) { return R > 4; }
-int rows_per_block(int R);         // rows per workgroup: RP (VALU) or 16/32 (MFMA)
+// Up to 2 rows run on the VALU kernel (rows padded to RP in {1, 2}); from 3
+// rows on, the matrix-core kernel (16-row tiles, one or two per workgroup)
+// was measured as fast or faster on gfx950 even with most of a tile padded
+// (R = 3, 4, 6, 8), so it takes over there.
+inline bool use_mfma(int R) { return R > 2; }
+int rows_per_block(int R);         // rows per workgroup: RP (VALU, 1 or 2) or 16/32 (MFMA)
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
 

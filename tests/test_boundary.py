@@ -141,14 +141,14 @@ def test_split_heuristic_shapes():
     big = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
                        max_pages_per_seq=256, max_kv_len=8192, num_pages=13000)
     assert pkv.num_splits(big, 256) == 1
-    # B=4, Hkv=8, G=4 (four rows, no mask) -> 32 units, 32768 keys -> one workgroup per CU
+    # B=4, Hkv=8, G=4 (matrix-core rows, D=128) -> 32 units, 32768 keys -> one workgroup per CU
     long = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                         max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
     assert pkv.num_splits(long, 256) == 8
-    # the same with a mask: two workgroups per CU
-    masked = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
-                          max_pages_per_seq=512, max_kv_len=32768, num_pages=2048, mask_stride_b=32768)
-    assert pkv.num_splits(masked, 256) == 16
+    # one row per kv head (VALU kernel): one workgroup per CU
+    mha = base_problem(batch=4, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=64,
+                       max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
+    assert pkv.num_splits(mha, 256) == 8
     # matrix-core rows (G=8) at D=64: two workgroups per CU; at D=128: one
     mf64 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
                         max_kv_len=4096, num_pages=2048)

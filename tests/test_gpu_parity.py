@@ -84,6 +84,10 @@ SMALL = [
     dict(B=2, q_len=4, Hq=16, Hkv=4, D=32, page_size=8, kv_lens=[200, 5], mask="3d", causal="last"),
     dict(B=1, q_len=2, Hq=64, Hkv=4, D=128, page_size=64, kv_lens=[777], mask="2d", mask_p=0.3),  # R=32
     dict(B=3, q_len=1, Hq=24, Hkv=2, D=64, page_size=32, kv_lens=[90, 1, 0], outlier_p=0.05),  # R=12
+    # two rows per kv head (VALU kernel with two rows) and three (matrix-core, mostly padding)
+    dict(B=3, q_len=1, Hq=16, Hkv=8, D=32, page_size=16, kv_lens=[70, 513, 1]),                # R=2
+    dict(B=2, q_len=2, Hq=4, Hkv=4, D=256, page_size=32, kv_lens=[300, 9], causal="last"),     # R=2
+    dict(B=2, q_len=1, Hq=12, Hkv=4, D=64, page_size=64, kv_lens=[1000, 257], mask="2d"),      # R=3
 ]
 
 
