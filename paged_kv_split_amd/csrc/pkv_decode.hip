@@ -365,32 +365,38 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
   __builtin_amdgcn_wave_barrier();
 }
 
-// The key-tile loop of one wave, double-buffered in registers: the next
-// tile's loads fly during this tile's compute.  The prefetch is issued
+// Register tiles per wave in the key loop (see tile_loop).
+template <int D, int RP>
+constexpr int valu_nbuf() { return 2; }
+
+// The key-tile loop of one wave, NBUF register tiles in a ring: while tile i
+// computes, the loads of tiles i+1 .. i+NBUF-1 are in flight; after it, its
+// registers take the loads of tile i+NBUF.  The loads are issued
 // unconditionally (a tile past the end loads the last key again, clamped in
-// load_tile), so the number of loads in flight is the same on every path and
-// the wait before a tile's compute leaves the next tile's loads in flight; a
-// conditional prefetch makes the compiler wait for all loads there.
-template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q>
+// load_tile) and in a fixed order, and a round has no early exit (a step past
+// the last tile computes a tile whose keys all get weight 0), so the number
+// of loads in flight is the same on every path into the loop header; a
+// conditional load or an exit there makes the compiler wait for all loads.
+template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q, int NBUF = valu_nbuf<D, RP>()>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int wb,
                                           int t0, int ntiles, const Q &qrows, const int (&lim)[RP], float *pbuf,
                                           float *kbuf, State<RP> &st) {
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, T = Lay::T;
   if (t0 >= ntiles) return;
-  Tile<D, RP, MASK> ta, tb;
-  load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + t0 * T, ta);
-  // no early exit between the two halves: a half past the last tile computes
-  // a tile whose keys are all past the window end (weight 0); an exit there
-  // would give the loop a second path into its header and the compiler
-  // would then wait for all loads at the header
-  for (int t = t0; t < ntiles; t += 2 * NW) {
-    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + NW) * T, tb);
+  Tile<D, RP, MASK> tr[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) {
+    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * T, tr[i]);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + t * T, ta, qrows, lim, b, r0, pbuf, kbuf, st);
-    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + 2 * NW) * T, ta);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + NW) * T, tb, qrows, lim, b, r0, pbuf, kbuf, st);
+  }
+  for (int t = t0; t < ntiles; t += NBUF * NW) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * NW) * T, tr[i], qrows, lim, b, r0, pbuf, kbuf, st);
+      load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + (i + NBUF) * NW) * T, tr[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
