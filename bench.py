@@ -83,12 +83,13 @@ def make_workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def describe(w, splits, replicas):
+def describe(w, splits, replicas, heads_per_block):
     L = w.kv_lens
     return {"workload": w.name, "B": w.B, "q_len": w.q_len, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "page_size": w.page_size, "kv_len_min": int(L.min()), "kv_len_max": int(L.max()),
             "kv_len_mean": round(float(L.mean()), 1), "mask": None if w.mask is None else list(w.mask.shape),
             "causal": w.causal_offsets is not None or w.causal_offset >= 0, "splits": splits,
+            "heads_per_block": heads_per_block,
             "replicas": replicas, "seed": w.seed}
 
 
@@ -131,6 +132,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_1b")
     ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--heads-per-block", type=int, default=0, help="kv heads per workgroup; 0 = library heuristic")
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -187,9 +189,11 @@ def main():
                             page_size=w.page_size, num_pages=w.num_pages,
                             max_pages_per_seq=w.max_pages_per_seq, max_kv_len=w.max_kv_len,
                             scale=w.scale, causal_offset=w.causal_offset, num_splits=args.splits,
-                            mask_stride_b=msb, mask_stride_q=msq)
-    S = pkv.num_splits_for(prob)
+                            mask_stride_b=msb, mask_stride_q=msq, heads_per_block=args.heads_per_block)
+    plan = pkv.plan(prob)
+    S = plan.splits
     prob.num_splits = S
+    prob.heads_per_block = plan.heads_per_block
     out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
     o_part, ml_part = pkv.alloc_workspace(prob, S, dev)      # ml_part zeroed (counter head)
     ob = 0 if o_part is None else o_part.numel() * 4
@@ -282,7 +286,7 @@ def main():
     # The dominant kernel's own average duration: the whole call when it is
     # one kernel; otherwise the split kernel alone (the same kernel, run
     # through pkv_paged_decode_partials), and the combine kernel alone.
-    n_kernels = 1 if (S == 1 or pkv.merges_in_kernel(prob, S)) else 2
+    n_kernels = plan.kernels
     rows = w.B * w.q_len * w.Hq
     pob, pmb = pkv.partials_bytes(prob, S)
     po2 = torch.empty(max(pob // 4, 4), dtype=torch.float32, device=dev)
@@ -339,7 +343,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": describe(w, S, n_rep),
+        "config": describe(w, S, n_rep, plan.heads_per_block),
         "us_per_call": round(us_call, 3),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "kernels_per_call": n_kernels,

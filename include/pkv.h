@@ -17,8 +17,9 @@
  * that sees no finite score gets 0.  The work is split along the keys
  * ("split-KV"); each split leaves a normalised partial output and its
  * (max, sum) pair, merged with the log-sum-exp rule; in pkv_paged_decode the
- * workgroup that finishes last among the splits of a (sequence, kv head, row
- * block) unit does that merge, so one kernel launch covers the whole path.
+ * workgroup that finishes last among the splits of a (sequence, kv-head
+ * group, row block) unit does that merge, so one kernel launch covers the
+ * whole path.
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are caller-owned DEVICE memory of the current HIP
@@ -56,8 +57,8 @@ extern "C" {
 enum {
   PKV_OK = 0,
   PKV_ERR_NULL = 1,        /* a required pointer is NULL */
-  PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, max_kv_len too big, bad stride */
-  PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS */
+  PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, Hkv % heads_per_block != 0, max_kv_len too big, bad stride */
+  PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS, heads_per_block not in {0, 1, 2, 4} */
   PKV_ERR_WORKSPACE = 4,   /* o_part / ml_part missing or smaller than pkv_workspace_bytes */
   PKV_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
   PKV_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
@@ -67,9 +68,10 @@ enum {
 #define PKV_MAX_SPLITS 256
 
 /* Head of the pkv_paged_decode ml_part workspace holding the per-unit arrival
- * counters of the in-kernel merge (one int32 per (sequence, kv head, row
- * block) unit), and the largest unit count merged in-kernel; problems with
- * more units and several splits use a separate combine launch instead. */
+ * counters of the in-kernel merge (one int32 per (sequence, kv-head group,
+ * row block) unit, see pkv_plan), and the largest unit count merged
+ * in-kernel; problems with more units and several splits use a separate
+ * combine launch instead. */
 #define PKV_COUNTER_BYTES 16384
 #define PKV_MAX_FUSED_UNITS (PKV_COUNTER_BYTES / 4)
 
@@ -93,6 +95,9 @@ typedef struct pkv_problem {
   int32_t num_splits;        /* 0 heuristic; 1..PKV_MAX_SPLITS forced */
   int64_t mask_stride_b;     /* mask element stride between sequences (>= 0) */
   int64_t mask_stride_q;     /* mask element stride between query tokens; 0 => 2D [B, kv] mask */
+  int32_t heads_per_block;   /* kv heads per split workgroup: 0 heuristic; 1, 2 or 4 forced
+                                (must divide num_kv_heads); a launch-shape choice only, the
+                                results do not depend on it beyond rounding order */
 } pkv_problem;
 
 /* Number of splits pkv_paged_decode uses for this problem on a device with
@@ -100,6 +105,24 @@ typedef struct pkv_problem {
  * forced p->num_splits is returned unchanged.  Pure host arithmetic once the
  * CU count is known. */
 int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out);
+
+/* The launch plan pkv_paged_decode follows for this problem on a device with
+ * `num_cus` compute units (num_cus <= 0: the current device's count).  Pure
+ * host arithmetic once the CU count is known; forced num_splits and
+ * heads_per_block are reported unchanged. */
+typedef struct pkv_plan_info {
+  int32_t splits;           /* key splits per sequence */
+  int32_t heads_per_block;  /* kv heads per split workgroup (1, 2 or 4) */
+  int32_t rows_per_block;   /* packed query rows (G * q_len) per kv head per workgroup:
+                               1 or 2 (vector kernel), 16 or 32 (matrix-core kernel) */
+  int32_t matrix_core;      /* 1: the matrix-core split kernel; 0: the vector one */
+  int64_t units;            /* (sequence, kv-head group, row block) units */
+  int64_t workgroups;       /* split-kernel workgroups: units * splits */
+  int32_t merge_in_kernel;  /* 1: the split kernel merges the splits itself */
+  int32_t kernels;          /* kernel launches per pkv_paged_decode call (0 when batch == 0) */
+} pkv_plan_info;
+
+int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info);
 
 /* Workspace pkv_paged_decode needs with `splits` splits:
  *   o_part : fp32 [B, q_len, Hq, splits, D]      (normalised partial outputs)

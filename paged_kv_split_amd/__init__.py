@@ -28,7 +28,7 @@ PKV_MAX_SPLITS = 256
 PKV_COUNTER_BYTES = 16384
 PKV_MAX_FUSED_UNITS = PKV_COUNTER_BYTES // 4
 
-EXPORTED = ("pkv_num_splits", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
             "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus", "pkv_status_string")
 
 
@@ -55,6 +55,21 @@ class Problem(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("mask_stride_b", ctypes.c_int64),
         ("mask_stride_q", ctypes.c_int64),
+        ("heads_per_block", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``pkv_plan_info`` (include/pkv.h)."""
+    _fields_ = [
+        ("splits", ctypes.c_int32),
+        ("heads_per_block", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32),
+        ("matrix_core", ctypes.c_int32),
+        ("units", ctypes.c_int64),
+        ("workgroups", ctypes.c_int64),
+        ("merge_in_kernel", ctypes.c_int32),
+        ("kernels", ctypes.c_int32),
     ]
 
 
@@ -71,6 +86,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         PP = ctypes.POINTER(Problem)
         L.pkv_num_splits.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.pkv_plan.argtypes = [PP, ctypes.c_int, ctypes.POINTER(PlanInfo)]
         L.pkv_workspace_bytes.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.pkv_workspace_clear.argtypes = [P, ctypes.c_size_t, P]
@@ -82,7 +98,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_device_cus.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
-        for name in ("pkv_num_splits", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+        for name in ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -101,10 +117,10 @@ def _check(status: int, where: str) -> None:
 def make_problem(*, batch: int, q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  page_size: int, num_pages: int, max_pages_per_seq: int, max_kv_len: int = 0,
                  scale: float = 1.0, causal_offset: int = -1, num_splits: int = 0,
-                 mask_stride_b: int = 0, mask_stride_q: int = 0) -> Problem:
+                 mask_stride_b: int = 0, mask_stride_q: int = 0, heads_per_block: int = 0) -> Problem:
     return Problem(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                    max_pages_per_seq, max_kv_len, scale, causal_offset, num_splits,
-                   mask_stride_b, mask_stride_q)
+                   mask_stride_b, mask_stride_q, heads_per_block)
 
 
 def device_cus() -> int:
@@ -117,6 +133,14 @@ def num_splits(problem: Problem, num_cus: int = 0) -> int:
     s = ctypes.c_int(0)
     _check(lib().pkv_num_splits(ctypes.byref(problem), int(num_cus), ctypes.byref(s)), "pkv_num_splits")
     return s.value
+
+
+def plan(problem: Problem, num_cus: int = 0) -> PlanInfo:
+    """pkv_plan: the launch plan pkv_paged_decode follows (splits, kv heads
+    per workgroup, kernel, units, merge path, launches per call)."""
+    info = PlanInfo()
+    _check(lib().pkv_plan(ctypes.byref(problem), int(num_cus), ctypes.byref(info)), "pkv_plan")
+    return info
 
 
 def workspace_bytes(problem: Problem, splits: int) -> tuple[int, int]:
@@ -283,42 +307,17 @@ def partials_bytes(problem: Problem, splits: int) -> tuple[int, int]:
     return rows * splits * problem.head_dim * 4, rows * splits * 8
 
 
-def rows_per_block(R: int) -> int:
-    """Rows of one workgroup (mirrors the library): 1 or 2 on the VALU kernel
-    (R <= 2), 16 or 32 on the matrix-core kernel."""
-    if R <= 1:
-        return 1
-    if R <= 2:
-        return 2
-    return 16 if R <= 16 else 32
-
-
-def units_of(problem: Problem) -> int:
-    """(sequence, kv head, row block) units: the workgroups of one unit
-    differ only in their split; up to PKV_MAX_FUSED_UNITS units are merged
-    inside the split kernel."""
-    R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
-    rp = rows_per_block(R)
-    return problem.batch * problem.num_kv_heads * ((R + rp - 1) // rp)
-
-
 def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
     """Whether pkv_paged_decode with ``splits`` splits merges them inside the
-    split kernel (mirrors the library's rule: several splits, at most
-    PKV_MAX_FUSED_UNITS units and at most two workgroups per CU) rather than
-    launching the combine kernel."""
-    if splits <= 1:
-        return False
-    if units_of(problem) > PKV_MAX_FUSED_UNITS:
-        return False
-    cus = num_cus if num_cus > 0 else device_cus()
-    return units_of(problem) * splits <= 2 * cus
+    split kernel rather than launching the combine kernel (pkv_plan)."""
+    p = Problem.from_buffer_copy(problem)
+    p.num_splits = splits
+    return bool(plan(p, num_cus).merge_in_kernel)
 
 
 def kernel_family(problem: Problem) -> str:
-    """Which split kernel serves the problem (R = G * q_len rows per kv head)."""
-    R = problem.num_q_heads // problem.num_kv_heads * problem.q_len
-    return "split_decode_mfma" if R > 2 else "split_decode_valu"
+    """Which split kernel serves the problem (pkv_plan)."""
+    return "split_decode_mfma" if plan(problem).matrix_core else "split_decode_valu"
 
 
 def num_splits_for(problem: Problem) -> int:

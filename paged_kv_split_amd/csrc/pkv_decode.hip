@@ -2,18 +2,22 @@
 //
 // Method (AstrAI commit d565d44, "csrc/kernels/attn_paged_decode.cu", commit
 // notes on the scalar split-KV paged decode kernel and the MMA variant): every
-// workgroup takes one (sequence b, kv head g, key split s, row block) unit.
-// The query rows that share kv head g (G query heads x q_len tokens: "GQA head
-// packing") are processed together, so every K/V byte is read from HBM once
-// per unit.  Keys are resolved through the page table, scores are accumulated
+// workgroup takes one key split s of one (sequence b, kv-head group, row
+// block) unit; the group holds hpb kv heads (1, 2 or 4).  The query rows that
+// share kv head g (G query heads x q_len tokens: "GQA head packing") are
+// processed together, so every K/V byte is read from HBM once per split.  Keys are resolved through the page table, scores are accumulated
 // with an online softmax (running max m and sum l per row), and the split
 // leaves either the final output (one split) or a normalised partial plus
 // (m, l) for the combine kernel.
 //
 // gfx950 mapping:
-//  * a workgroup is kWavesPerBlock wave64s; wave w takes tiles w, w+NW, ...
-//    of T keys and keeps its own (m, l, acc); waves merge once at the end
-//    through LDS, so the key loop has no workgroup barrier;
+//  * a workgroup is kWavesPerBlock wave64s; wave w works on kv head
+//    w % hpb of the group and, with the other NW / hpb waves of that head,
+//    takes every (NW / hpb)-th tile of T keys, keeping its own (m, l, acc);
+//    the waves of a head merge once at the end through LDS, so the key loop
+//    has no workgroup barrier.  With several heads per workgroup its waves
+//    read the neighbouring head slices of the same page slots at about the
+//    same time, which suits HBM better than one head's short slices alone;
 //  * the split's slice of the page table is staged in LDS once (in windows of
 //    kBtCap pages), so a K/V address costs an LDS read, not an HBM round trip;
 //  * K/V tiles are double-buffered in registers: the loads of a wave's next
@@ -28,10 +32,10 @@
 //    gfx950 permlane16/32 swaps, no LDS traffic;
 //  * K and V rows are fetched with 128-bit loads; rows past the split end are
 //    never loaded (tails read as zero);
-//  * the workgroup index is decoded so that the Hkv x row-block siblings of a
-//    (b, s) unit land on the same XCD back to back (blocks are dealt to the 8
-//    XCDs round-robin), so they share that XCD's L2 for the interleaved kv
-//    heads of a page slot;
+//  * the workgroup index is decoded so that the head-group x row-block
+//    siblings of a (b, s) pair land on the same XCD back to back (blocks are
+//    dealt to the 8 XCDs round-robin), so they share that XCD's L2 for the
+//    interleaved kv heads of a page slot;
 //  * scores live in base 2 (scale * log2 e folded in) and use v_exp_f32;
 //    exclusion (tail, causal, -inf mask) is a select, never an add.
 #include <hip/hip_runtime.h>
@@ -106,7 +110,6 @@ struct Layout {
   static constexpr int KPP = 64 / LPK;     // keys per QK pass
   static constexpr int NPASS = 1;
   static constexpr int T = KPP * NPASS;    // keys per wave tile
-  static constexpr bool QREG = RP <= 2;    // q in registers; else read from LDS (shared by the block)
   static constexpr int LPV = D / 8;        // lanes per key, PV layout
   static constexpr int KPV = 64 / LPV;     // keys per PV step
   static constexpr int NSTEP = T / KPV;    // PV steps per tile
@@ -120,10 +123,10 @@ struct Layout {
   static constexpr int SW_SHIFT = LPK >= 4 ? 0 : (LPK == 2 ? 1 : 2);
   static constexpr int SW_MASK = LPK >= 8 ? 1 : 3;
   __device__ static int kslot(int ch, int row) { return ch ^ (SW_MUL * ((row >> SW_SHIFT) & SW_MASK)); }
-  static constexpr int MERGE = NW * RP * D + NW * RP * 2 + RP * 2 + NW * RP;
-  static constexpr int QLDS = QREG ? 0 : RP * D / 2;  // q rows as packed bf16 pairs (floats)
-  static constexpr int MAIN = kBtCap + 4 + QLDS + PBUF + KBUF;  // page-table slice (+1 page when a window
-                                                         // starts mid-page), q, p slices
+  // merge phase: per-wave O rows, per-wave (m, l), per-row (M, W), wave factors
+  static constexpr int MERGE = NW * RP * D + NW * RP * 2 + RP * kMaxHeadsPerBlock * 2 + NW * RP;
+  static constexpr int MAIN = kBtCap + 4 + PBUF + KBUF;  // page-table slice (+1 page when a window
+                                                         // starts mid-page), p and K slices
   static constexpr int SMEM = MAIN > MERGE ? MAIN : MERGE;
 };
 
@@ -221,20 +224,11 @@ struct State {
   float acc[RP][8];   // PV accumulator, this lane's 8 columns and key group
 };
 
-// q rows of a block: in registers (few rows) or read from the block's LDS copy
-template <int D, int RP, bool QREG>
-struct QRows;
+// q rows of a wave, in registers: this lane's chunks qq + LPK*c4 of every row
 template <int D, int RP>
-struct QRows<D, RP, true> {
-  uint4 v[RP][4];  // this lane's chunks qq + LPK*c4 of every row
+struct QRows {
+  uint4 v[RP][4];
   __device__ __forceinline__ uint4 get(int r, int c4, int) const { return v[r][c4]; }
-};
-template <int D, int RP>
-struct QRows<D, RP, false> {
-  const uint4 *lds;  // [RP][D/8] in LDS
-  __device__ __forceinline__ uint4 get(int r, int c4, int qq) const {
-    return lds[r * (D / 8) + qq + (D / 32) * c4];
-  }
 };
 
 template <int D, int RP, bool CAUSAL, bool MASK, class Q>
@@ -369,9 +363,9 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
 template <int D, int RP>
 constexpr int valu_nbuf() { return 2; }
 
-// The key-tile loop of one wave, NBUF register tiles in a ring: while tile i
-// computes, the loads of tiles i+1 .. i+NBUF-1 are in flight; after it, its
-// registers take the loads of tile i+NBUF.  The loads are issued
+// The key-tile loop of one wave (tiles t0, t0 + tstep, ...), NBUF register
+// tiles in a ring: while tile i computes, the loads of tiles i+1 .. i+NBUF-1
+// are in flight; after it, its registers take the loads of tile i+NBUF.  The loads are issued
 // unconditionally (a tile past the end loads the last key again, clamped in
 // load_tile) and in a fixed order, and a round has no early exit (a step past
 // the last tile computes a tile whose keys all get weight 0), so the number
@@ -379,22 +373,22 @@ constexpr int valu_nbuf() { return 2; }
 // conditional load or an exit there makes the compiler wait for all loads.
 template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q, int NBUF = valu_nbuf<D, RP>()>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int wb,
-                                          int t0, int ntiles, const Q &qrows, const int (&lim)[RP], float *pbuf,
-                                          float *kbuf, State<RP> &st) {
+                                          int t0, int tstep, int ntiles, const Q &qrows, const int (&lim)[RP],
+                                          float *pbuf, float *kbuf, State<RP> &st) {
   using Lay = Layout<D, RP>;
-  constexpr int NW = Lay::NW, T = Lay::T;
+  constexpr int T = Lay::T;
   if (t0 >= ntiles) return;
   Tile<D, RP, MASK> tr[NBUF];
 #pragma unroll
   for (int i = 0; i < NBUF; ++i) {
-    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * T, tr[i]);
+    load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * tstep) * T, tr[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int t = t0; t < ntiles; t += NBUF * NW) {
+  for (int t = t0; t < ntiles; t += NBUF * tstep) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
-      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * NW) * T, tr[i], qrows, lim, b, r0, pbuf, kbuf, st);
-      load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + (i + NBUF) * NW) * T, tr[i]);
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * tstep) * T, tr[i], qrows, lim, b, r0, pbuf, kbuf, st);
+      load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + (i + NBUF) * tstep) * T, tr[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -405,10 +399,11 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, LPK = Lay::LPK, T = Lay::T, LPV = Lay::LPV;
   __shared__ __attribute__((aligned(16))) float smem[Lay::SMEM];
-  __shared__ int64_t rowtab[RP];  // output row of each packed row of the block
+  // output row of packed row r of head slot hh of the block, at r * hpb + hh
+  __shared__ int64_t rowtab[RP * kMaxHeadsPerBlock];
 
-  // ---- unit decode (XCD-aware): siblings (kv head, row block) of one
-  // (b, split) unit get consecutive slots on the same XCD
+  // ---- unit decode (XCD-aware): siblings (kv-head group, row block) of one
+  // (b, split) pair get consecutive slots on the same XCD
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int slot = x >> 3;
@@ -417,11 +412,15 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   if (outer_idx >= a.outer) return;
   const int b = outer_idx / a.S;
   const int s = outer_idx - b * a.S;
-  const int g = inner_idx / a.nrb;
-  const int rb = inner_idx - g * a.nrb;
+  const int hg = inner_idx / a.nrb;
+  const int rb = inner_idx - hg * a.nrb;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int hw = w & (a.hpb - 1);   // this wave's head slot in the group
+  const int wk = w >> a.lhpb;       // its index among the waves of that head
+  const int wph = NW >> a.lhpb;     // waves per head
+  const int g = hg * a.hpb + hw;
 
   const int r0 = rb * RP;
   const int L = a.kv_lens[b];
@@ -462,43 +461,25 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   c.kg = lane / LPV;
   c.ds = lane % LPV;
 
-  // ---- q rows of this block: registers (QK layout: chunks qq + LPK*c4) or
-  // the block's LDS copy [RP][D] (zero rows past R)
-  QRows<D, RP, Lay::QREG> qrows;
-  if constexpr (Lay::QREG) {
+  // ---- q rows of this wave's head, in registers (QK layout: chunks qq + LPK*c4)
+  QRows<D, RP> qrows;
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int rr = r0 + r;
-      if (rr < a.R) {
-        const int i = rr / a.G;
-        const int h = g * a.G + (rr - i * a.G);
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
+  for (int r = 0; r < RP; ++r) {
+    const int rr = r0 + r;
+    if (rr < a.R) {
+      const int i = rr / a.G;
+      const int h = g * a.G + (rr - i * a.G);
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
-      } else {
+      for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
+    } else {
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
     }
-  } else {
-    uint4 *qs = reinterpret_cast<uint4 *>(smem + kBtCap + 4);
-    for (int idx = threadIdx.x; idx < RP * (D / 8); idx += NW * 64) {
-      const int r = idx / (D / 8);
-      const int ch = idx - r * (D / 8);
-      const int rr = r0 + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (rr < a.R) {
-        const int i = rr / a.G;
-        const int h = g * a.G + (rr - i * a.G);
-        v = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D)[ch];
-      }
-      qs[idx] = v;
-    }
-    qrows.lds = qs;  // published by the barrier before the first tile
   }
 
-  float *pbuf = smem + kBtCap + 4 + Lay::QLDS + w * (T * RP);
-  float *kbuf = smem + kBtCap + 4 + Lay::QLDS + Lay::PBUF + w * (T * D / 2);
+  float *pbuf = smem + kBtCap + 4 + w * (T * RP);
+  float *kbuf = smem + kBtCap + 4 + Lay::PBUF + w * (T * D / 2);
   int *bt_lds = reinterpret_cast<int *>(smem);
   const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
 
@@ -525,9 +506,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
     for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
   };
-  if (threadIdx.x < RP) {
-    const int rr = r0 + threadIdx.x;
-    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, g, rr) : 0;
+  if (threadIdx.x < RP * a.hpb) {
+    const int rr = r0 + (threadIdx.x >> a.lhpb);
+    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
   load_bt(c.kb);
   __syncthreads();
@@ -542,7 +523,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     c.ke = we;
     const int ntiles = (we - wb + T - 1) / T;
 
-    tile_loop<D, RP, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, w, ntiles, qrows, lim, pbuf, kbuf, st);
+    tile_loop<D, RP, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, wk, wph, ntiles, qrows, lim, pbuf, kbuf, st);
   }
 
   // ---- wave totals: l over QK key groups, acc over PV key groups
@@ -554,15 +535,19 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[r][e] = reduce_hi<Lay::LOG_LPV, OpSum>(st.acc[r][e]);
 
-  // ---- merge the waves through LDS, then write (output, or this split's
-  // partial and, fused, the unit's merge by the block that finishes last)
+  // ---- merge the waves of each head through LDS, then write (output, or
+  // this split's partial and, fused, the unit's merge by the block that
+  // finishes last).  Row slot u = wk * HR + r * hpb + hw: the row index
+  // ri = r * hpb + hw of the block's output rows, once per wave of a head.
   __syncthreads();
-  float *ob = smem;                    // [NW][RP][D]
-  float *mlb = smem + NW * RP * D;     // [NW][RP][2]
+  const int HR = RP * a.hpb;
+  float *ob = smem;                    // [NW * RP][D]
+  float *mlb = smem + NW * RP * D;     // [NW * RP][2]
   if (c.kg == 0) {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      float4 *dst = reinterpret_cast<float4 *>(ob + (w * RP + r) * D + c.ds * 8);
+      const int u = wk * HR + r * a.hpb + hw;
+      float4 *dst = reinterpret_cast<float4 *>(ob + u * D + c.ds * 8);
       dst[0] = make_float4(st.acc[r][0], st.acc[r][1], st.acc[r][2], st.acc[r][3]);
       dst[1] = make_float4(st.acc[r][4], st.acc[r][5], st.acc[r][6], st.acc[r][7]);
     }
@@ -570,39 +555,42 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      mlb[(w * RP + r) * 2] = st.m[r];
-      mlb[(w * RP + r) * 2 + 1] = l_tot[r];
+      const int u = wk * HR + r * a.hpb + hw;
+      mlb[u * 2] = st.m[r];
+      mlb[u * 2 + 1] = l_tot[r];
     }
   }
-  float *rmw = mlb + NW * RP * 2;      // [RP][2]: merged (M, W) per row
-  float *fw = rmw + RP * 2;            // [NW][RP]: normalised wave factors
+  float *rmw = mlb + NW * RP * 2;                  // [RP * hpb][2]: merged (M, W) per row
+  float *fw = rmw + RP * kMaxHeadsPerBlock * 2;    // [NW * RP]: normalised wave factors
+  const int nrows = (a.R - r0 < RP ? a.R - r0 : RP) * a.hpb;
   __syncthreads();
-  if (threadIdx.x < RP) {
-    const int r = threadIdx.x;
+  if (threadIdx.x < nrows) {
+    const int ri = threadIdx.x;
     float mw[NW], lw[NW], f[NW], M, W;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      mw[ww] = mlb[(ww * RP + r) * 2];
-      lw[ww] = mlb[(ww * RP + r) * 2 + 1];
+    for (int kk = 0; kk < NW; ++kk) {
+      mw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2] : -INFINITY;
+      lw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2 + 1] : 0.f;
     }
     wave_factors<NW>(mw, lw, M, W, f);
-    rmw[2 * r] = M;
-    rmw[2 * r + 1] = W;
+    rmw[2 * ri] = M;
+    rmw[2 * ri + 1] = W;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) fw[ww * RP + r] = f[ww];
+    for (int kk = 0; kk < NW; ++kk)
+      if (kk < wph) fw[kk * HR + ri] = f[kk];
   }
   __syncthreads();
-  auto Mrow = [&](int r) { return rmw[2 * r]; };
-  auto Wrow = [&](int r) { return rmw[2 * r + 1]; };
-  auto resn = [&](int r, int d) {
+  auto Mrow = [&](int ri) { return rmw[2 * ri]; };
+  auto Wrow = [&](int ri) { return rmw[2 * ri + 1]; };
+  auto resn = [&](int ri, int d) {
     float o = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) o = fmaf(fw[ww * RP + r], ob[(ww * RP + r) * D + d], o);
+    for (int kk = 0; kk < NW; ++kk)
+      if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * D + d], o);
     return o;
   };
-  const int nrows = a.R - r0 < RP ? a.R - r0 : RP;
   write_rows<D>(a, s, rowtab, nrows, resn, Mrow, Wrow, NW * 64);
-  fused_tail<D>(a, (b * a.Hkv + g) * a.nrb + rb, rowtab, nrows, smem, NW * 64);
+  fused_tail<D>(a, b * a.inner + inner_idx, rowtab, nrows, smem, NW * 64);
 }
 
 // Combine (the standalone pkv_combine entry point): each block merges

@@ -6,9 +6,10 @@
 // commit notes: the MMA split-KV paged decode kernel packs the query heads of
 // one kv head into tensor-core tiles and resolves the page table once per key
 // tile).  gfx950 mapping:
-//  * a workgroup covers up to 32 rows (two 16-row blocks) of one kv head and
-//    one key split; its kWavesPerBlock waves take 16-key tiles in turn and
-//    merge their (m, l, O) once at the end through LDS;
+//  * a workgroup covers one key split of up to 32 rows (two 16-row blocks)
+//    of each of hpb kv heads (1, 2 or 4); wave w works on head w % hpb and
+//    takes every (NW / hpb)-th 16-key tile; the waves of a head merge their
+//    (m, l, O) once at the end through LDS;
 //  * K and V tiles are fetched with full-row 128-bit loads into registers
 //    (double-buffered, so the next tile's loads fly during this tile's math)
 //    and written to a per-wave LDS slice with an XOR chunk swizzle;
@@ -54,7 +55,9 @@ struct MLay {
   static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
   static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
-  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 32 * 2 * 4 + 16 * 2 * 4 + NW * 16 * 4;
+  // merge phase: per-wave O rows, per-wave (m, l), per-row (M, W), wave factors
+  static constexpr int MERGE_BYTES =
+      NW * 16 * OB_STRIDE * 4 + NW * 16 * 2 * 4 + 16 * kMaxHeadsPerBlock * 2 * 4 + NW * 16 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
   static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   // swizzles (16-byte chunk index within a row)
@@ -275,23 +278,23 @@ __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b,
 template <int D, int NRB>
 constexpr int mfma_nbuf() { return D >= 256 ? 1 : 2; }
 
-// The key-tile loop of one wave.
+// The key-tile loop of one wave: tiles t0, t0 + tstep, ...
 template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE, int NBUF = mfma_nbuf<D, NRB>()>
 __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int t0,
-                                           int ntiles, const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB],
-                                           uint16_t *kt, uint16_t *vt, int lane, MState<D, NRB> &st) {
-  constexpr int NW = MLay<D>::NW;
+                                           int tstep, int ntiles, const uint4 (&qb)[NRB][D / 32],
+                                           const int (&lim)[NRB], uint16_t *kt, uint16_t *vt, int lane,
+                                           MState<D, NRB> &st) {
   if constexpr (D >= 256) {
     // one register tile (two would spill at D = 256): the next tile's loads
     // are issued right after this tile reaches LDS and fly during its compute
     if (t0 >= ntiles) return;
     MTile<D, NRB, MASK> tr;
     mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, tr);
-    for (int t = t0; t < ntiles; t += NW)
-      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + NW, tr, qb, lim, kt, vt, lane, st);
+    for (int t = t0; t < ntiles; t += tstep)
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + tstep, tr, qb, lim, kt, vt, lane, st);
     return;
   }
-  // NBUF register tiles in a ring: tile t sits in buffer (t / NW) % NBUF; a
+  // NBUF register tiles in a ring: tile t sits in buffer (t / tstep) % NBUF; a
   // tile goes to LDS, then the loads of the tile NBUF steps ahead are issued
   // into the freed registers
   if (t0 >= ntiles) return;
@@ -300,18 +303,19 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
   // wait for tile i leaves the loads of tiles i+1.. in flight
 #pragma unroll
   for (int i = 0; i < NBUF; ++i) {
-    mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * NW) * KT, lane, tr[i]);
+    mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * tstep) * KT, lane, tr[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
   // no early exit inside a round: a step past the last tile computes a tile
   // whose keys are all past the window end (weight 0); an exit there would
   // give the loop a second path into its header and the compiler would then
   // wait for all loads at the header
-  for (int t = t0; t < ntiles; t += NBUF * NW) {
+  for (int t = t0; t < ntiles; t += NBUF * tstep) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
-      const int tt = t + i * NW;
-      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tt + NBUF * NW, tr[i], qb, lim, kt, vt, lane, st);
+      const int tt = t + i * tstep;
+      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tt + NBUF * tstep, tr[i], qb, lim, kt, vt, lane,
+                                         st);
     }
   }
 }
@@ -327,7 +331,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   constexpr int NW = L::NW;
   constexpr int RW = 16 * NRB;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[L::SMEM_BYTES];
-  __shared__ int64_t rowtab[RW];  // output row of each packed row of the block
+  // output row of packed row rr of head slot hh of the block, at rr * hpb + hh
+  __shared__ int64_t rowtab[RW * kMaxHeadsPerBlock];
 
   const int x = blockIdx.x;
   const int xcd = x & 7;
@@ -337,11 +342,15 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
   if (outer_idx >= a.outer) return;
   const int b = outer_idx / a.S;
   const int s = outer_idx - b * a.S;
-  const int g = inner_idx / a.nrb;
-  const int rg = inner_idx - g * a.nrb;
+  const int hg = inner_idx / a.nrb;
+  const int rg = inner_idx - hg * a.nrb;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int hw = w & (a.hpb - 1);   // this wave's head slot in the group
+  const int wk = w >> a.lhpb;       // its index among the waves of that head
+  const int wph = NW >> a.lhpb;     // waves per head
+  const int g = hg * a.hpb + hw;
   const int cc = lane & 15;
   const int q = lane >> 4;
   const int r0 = rg * RW;
@@ -418,9 +427,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
     for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (threadIdx.x < RW) {
-    const int rr = r0 + threadIdx.x;
-    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, g, rr) : 0;
+  if (threadIdx.x < RW * a.hpb) {
+    const int rr = r0 + (threadIdx.x >> a.lhpb);
+    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
   load_bt(kb);
   __syncthreads();
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
     c.p0 = wb >> a.page_shift;
     c.ke = we;
     const int ntiles = (we - wb + KT - 1) / KT;
-    mtile_loop<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, w, ntiles, qb, lim, kt, vt, lane, st);
+    mtile_loop<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, wk, wph, ntiles, qb, lim, kt, vt, lane, st);
   }
 
   // row sums over the four lanes of each row
@@ -442,52 +451,59 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) v
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) ltot[rb] = xor32<OpSum>(xor16<OpSum>(st.l[rb]));
 
-  // merge the waves, one 16-row block at a time
-  float *ob = reinterpret_cast<float *>(smem_raw);        // [NW][16][OB_STRIDE]
-  float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW][32][2]
-  float *rmw = mlb + NW * 32 * 2;                         // [16][2]: merged (M, W) per row
-  float *fw = rmw + 16 * 2;                               // [NW][16]: normalised wave factors
+  // merge the waves of each head, one 16-row block at a time.  Row slot
+  // u = wk * HR + cc * hpb + hw: the block-local row index ri = cc * hpb + hw
+  // (matching rowtab), once per wave of a head.
+  const int HR = 16 * a.hpb;
+  float *ob = reinterpret_cast<float *>(smem_raw);        // [NW * 16][OB_STRIDE]
+  float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW * 16][2]
+  float *rmw = mlb + NW * 16 * 2;                         // [16 * hpb][2]: merged (M, W) per row
+  float *fw = rmw + 16 * kMaxHeadsPerBlock * 2;           // [NW * 16]: normalised wave factors
+  const int u = wk * HR + cc * a.hpb + hw;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       // lane holds O^T[d = 16nb + 4q + i][row cc]
-      float4 *dst = reinterpret_cast<float4 *>(ob + (w * 16 + cc) * L::OB_STRIDE + 16 * nb + 4 * q);
+      float4 *dst = reinterpret_cast<float4 *>(ob + u * L::OB_STRIDE + 16 * nb + 4 * q);
       dst[0] = make_float4(st.o[rb][nb][0], st.o[rb][nb][1], st.o[rb][nb][2], st.o[rb][nb][3]);
     }
     if (q == 0) {
-      mlb[(w * 32 + cc + 16 * rb) * 2] = st.m[rb];
-      mlb[(w * 32 + cc + 16 * rb) * 2 + 1] = ltot[rb];
+      mlb[u * 2] = st.m[rb];
+      mlb[u * 2 + 1] = ltot[rb];
     }
+    const int rs = r0 + 16 * rb;
+    const int nrows = (a.R - rs < 16 ? a.R - rs : 16) * a.hpb;
     __syncthreads();
-    if (threadIdx.x < 16) {
-      const int r = threadIdx.x;
+    if (threadIdx.x < nrows) {
+      const int ri = threadIdx.x;
       float mw[NW], lw[NW], f[NW], M, W;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        mw[ww] = mlb[(ww * 32 + 16 * rb + r) * 2];
-        lw[ww] = mlb[(ww * 32 + 16 * rb + r) * 2 + 1];
+      for (int kk = 0; kk < NW; ++kk) {
+        mw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2] : -INFINITY;
+        lw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2 + 1] : 0.f;
       }
       wave_factors<NW>(mw, lw, M, W, f);
-      rmw[2 * r] = M;
-      rmw[2 * r + 1] = W;
+      rmw[2 * ri] = M;
+      rmw[2 * ri + 1] = W;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) fw[ww * 16 + r] = f[ww];
+      for (int kk = 0; kk < NW; ++kk)
+        if (kk < wph) fw[kk * HR + ri] = f[kk];
     }
     __syncthreads();
-    auto Mrow = [&](int r) { return rmw[2 * r]; };
-    auto Wrow = [&](int r) { return rmw[2 * r + 1]; };
-    auto resn = [&](int r, int d) {
+    auto Mrow = [&](int ri) { return rmw[2 * ri]; };
+    auto Wrow = [&](int ri) { return rmw[2 * ri + 1]; };
+    auto resn = [&](int ri, int d) {
       float o = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) o = fmaf(fw[ww * 16 + r], ob[(ww * 16 + r) * L::OB_STRIDE + d], o);
+      for (int kk = 0; kk < NW; ++kk)
+        if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * L::OB_STRIDE + d], o);
       return o;
     };
-    const int rs = r0 + 16 * rb;
-    write_rows<D>(a, s, rowtab + 16 * rb, a.R - rs < 16 ? a.R - rs : 16, resn, Mrow, Wrow, NW * 64);
+    write_rows<D>(a, s, rowtab + 16 * rb * a.hpb, nrows, resn, Mrow, Wrow, NW * 64);
   }
-  fused_tail<D>(a, (b * a.Hkv + g) * a.nrb + rg, rowtab, a.R - r0 < RW ? a.R - r0 : RW,
+  fused_tail<D>(a, b * a.inner + inner_idx, rowtab, (a.R - r0 < RW ? a.R - r0 : RW) * a.hpb,
                 reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 

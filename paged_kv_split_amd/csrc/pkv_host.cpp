@@ -56,6 +56,11 @@ int check_problem(const pkv_problem *p) {
   if (p->causal_offset < -1) return PKV_ERR_SHAPE;
   if (p->num_splits < 0) return PKV_ERR_SHAPE;
   if (p->num_splits > PKV_MAX_SPLITS) return PKV_ERR_UNSUPPORTED;
+  if (p->heads_per_block < 0) return PKV_ERR_SHAPE;
+  if (p->heads_per_block > 0) {
+    if (!is_pow2(p->heads_per_block) || p->heads_per_block > pkv::kMaxHeadsPerBlock) return PKV_ERR_UNSUPPORTED;
+    if (p->num_kv_heads % p->heads_per_block) return PKV_ERR_SHAPE;
+  }
   if (p->mask_stride_b < 0 || p->mask_stride_q < 0) return PKV_ERR_SHAPE;
   // rows * D and pool sizes must fit the 64-bit element arithmetic used on device
   const int64_t rows = (int64_t)p->batch * p->q_len * p->num_q_heads;
@@ -86,8 +91,9 @@ int query_cus(int *out) {
 // Split heuristic (keys only along the sequence axis, in the spirit of the
 // pages' compute_num_splits and ejkernel's num_splits = 0 "auto"): split each
 // sequence so that the grid has about blocks_per_cu() workgroups per CU (no
-// split when the (sequence, kv head, row block) units alone reach that),
-// never below kMinTilesPerWave tiles per wave and never above 64 splits.
+// split when the (sequence, kv-head group, row block) units alone reach
+// that), never below kMinTilesPerWave tiles per wave and never above 64
+// splits.
 constexpr int kMinTilesPerWave = 2;
 
 // Workgroups per CU to aim at, measured on MI355X over the decode shapes:
@@ -101,16 +107,25 @@ int blocks_per_cu(const pkv_problem *p) {
   return 1;
 }
 
-int heuristic_splits(const pkv_problem *p, int cus) {
+// Row blocks per kv head.
+int64_t row_blocks(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  const int rp = pkv::rows_per_block(R);
-  const int64_t nrb = ceil_div(R, rp);
-  const int64_t units = (int64_t)p->batch * p->num_kv_heads * nrb;
+  return ceil_div(R, pkv::rows_per_block(R));
+}
+
+// (sequence, kv-head group, row block) units with hpb kv heads per group:
+// the workgroups of one unit differ only in their split.
+int64_t units_of(const pkv_problem *p, int hpb) {
+  return (int64_t)p->batch * (p->num_kv_heads / hpb) * row_blocks(p);
+}
+
+int heuristic_splits(const pkv_problem *p, int cus, int hpb) {
+  const int64_t units = units_of(p, hpb);
   if (units <= 0) return 1;
   const int64_t target = (int64_t)cus * blocks_per_cu(p);
   if (units >= target) return 1;
   const int T = pkv::tile_keys(p->head_dim);
-  const int64_t min_keys = (int64_t)T * pkv::kWavesPerBlock * kMinTilesPerWave;
+  const int64_t min_keys = (int64_t)T * (pkv::kWavesPerBlock / hpb) * kMinTilesPerWave;
   const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
   int64_t s = target / units;
   if (s > max_by_len) s = max_by_len;
@@ -119,11 +134,50 @@ int heuristic_splits(const pkv_problem *p, int cus) {
   return (int)s;
 }
 
-// (sequence, kv head, row block) units of a problem: the workgroups of one
-// unit share a row block and differ only in their split.
-int64_t units_of(const pkv_problem *p) {
+// Kv heads per workgroup.  Grouping the heads of a page slot in one
+// workgroup (one wave per head at hpb = 4) makes it read longer runs of each
+// slot, which HBM serves faster than separate D * 2-byte head slices: on
+// MI355X the VALU kernel gains 13% at D = 64 and 5% at D = 128 (B = 16,
+// 4096 keys, Hkv = 8), nothing at D = 256.  Grouping multiplies the splits
+// needed to fill the chip by hpb; it is taken only while that count stays in
+// [2, kMaxGroupedSplits]: at one split a workgroup holds hpb whole sequences
+// and ragged lengths unbalance the grid (B = 256 lognormal lengths: 1.65x
+// slower), and more splits cost more partial traffic.  The matrix-core kernel
+// measured no gain (its 16-key tiles keep fewer bytes in flight per wave),
+// so it keeps one head per workgroup.
+constexpr int kMaxGroupedSplits = 8;
+
+int heuristic_hpb(const pkv_problem *p, int cus) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  return (int64_t)p->batch * p->num_kv_heads * ceil_div(R, pkv::rows_per_block(R));
+  if (pkv::use_mfma(R) || p->head_dim > 128) return 1;
+  for (int hpb = pkv::kMaxHeadsPerBlock; hpb > 1; hpb /= 2) {
+    if (p->num_kv_heads % hpb) continue;
+    const int s = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, hpb);
+    if (s >= 2 && s <= kMaxGroupedSplits) return hpb;
+  }
+  return 1;
+}
+
+// The launch plan of a problem on a device with `cus` compute units.
+struct Plan {
+  int S;          // splits
+  int hpb;        // kv heads per workgroup
+  int64_t units;  // (sequence, kv-head group, row block) units
+  bool fused;     // pkv_paged_decode merges the splits inside the split kernel
+};
+
+Plan make_plan(const pkv_problem *p, int cus) {
+  Plan pl;
+  pl.hpb = p->heads_per_block > 0 ? p->heads_per_block : heuristic_hpb(p, cus);
+  pl.S = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, pl.hpb);
+  pl.units = units_of(p, pl.hpb);
+  // In-kernel merge (a counter for every unit) when the grid has at most two
+  // workgroups per CU: the merging workgroups then hold up few others and the
+  // saved combine launch is the larger cost.  Larger grids use the combine
+  // kernel, measured faster there (the merge's device-scope traffic then runs
+  // under full HBM load and on the kernel's critical path).
+  pl.fused = pl.S > 1 && pl.units <= PKV_MAX_FUSED_UNITS && pl.units * pl.S <= 2 * (int64_t)cus;
+  return pl;
 }
 
 // ml_part bytes of pkv_paged_decode with S >= 2 splits: counter head + (m, l).
@@ -164,7 +218,29 @@ int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out) {
     rc = query_cus(&num_cus);
     if (rc) return rc;
   }
-  *splits_out = heuristic_splits(p, num_cus);
+  *splits_out = make_plan(p, num_cus).S;
+  return PKV_OK;
+}
+
+int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info) {
+  if (!info) return PKV_ERR_NULL;
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (num_cus <= 0) {
+    rc = query_cus(&num_cus);
+    if (rc) return rc;
+  }
+  const Plan pl = make_plan(p, num_cus);
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  *info = pkv_plan_info{};
+  info->splits = pl.S;
+  info->heads_per_block = pl.hpb;
+  info->rows_per_block = pkv::rows_per_block(R);
+  info->matrix_core = pkv::use_mfma(R) ? 1 : 0;
+  info->units = pl.units;
+  info->workgroups = pl.units * pl.S;
+  info->merge_in_kernel = pl.fused ? 1 : 0;
+  info->kernels = (pl.S > 1 && !pl.fused && p->batch > 0) ? 2 : (p->batch > 0 ? 1 : 0);
   return PKV_OK;
 }
 
@@ -211,12 +287,12 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
     return PKV_ERR_ALIGN;
 
   // split count: forced, or the heuristic (needs the device's CU count)
+  int cus = 0;
   int S = p->num_splits;
   if (S == 0) {
-    int cus = 0;
-    int rc = query_cus(&cus);
+    const int rc = query_cus(&cus);
     if (rc) return rc;
-    S = heuristic_splits(p, cus);
+    S = make_plan(p, cus).S;
   }
   // pkv_paged_decode with several splits: ml_part = counter head + (m, l)
   const bool split_ws = S > 1 && !partials_only;
@@ -227,6 +303,18 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
     if (!o_part || !ml_part || o_part_bytes < need_o || ml_part_bytes < need_ml) return PKV_ERR_WORKSPACE;
     if (!aligned(o_part, 16) || !aligned(ml_part, split_ws ? 16 : 8)) return PKV_ERR_ALIGN;
   }
+
+  // heads per workgroup and merge path (the CU count is needed unless both
+  // are fixed: one forced split and forced heads per workgroup)
+  Plan pl{S, p->heads_per_block, 0, false};
+  if (S > 1 || p->heads_per_block == 0) {
+    if (cus == 0) {
+      const int rc = query_cus(&cus);
+      if (rc) return rc;
+    }
+    pl = make_plan(p, cus);
+  }
+  pl.units = units_of(p, pl.hpb);
 
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
@@ -265,10 +353,12 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->S = S;
   a->chunk = (int32_t)chunk;
   a->nrb = (R + rp - 1) / rp;
+  a->hpb = pl.hpb;
+  a->lhpb = ilog2(pl.hpb);
   a->causal_offset = p->causal_offset;
   a->scale_log2 = p->scale * 1.4426950408889634f;
   const int64_t outer = (int64_t)p->batch * S;
-  const int64_t inner = (int64_t)p->num_kv_heads * a->nrb;
+  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * a->nrb;
   if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
   // the combine kernel's grid (several splits without the in-kernel merge)
   const int64_t rows_all = (int64_t)p->batch * p->q_len * p->num_q_heads;
@@ -276,16 +366,7 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->outer = (int32_t)outer;
   a->inner = (int32_t)inner;
   a->partials = (S > 1 || partials_only) ? 1 : 0;
-  // In-kernel merge (a counter for every unit) when the grid has at most two
-  // workgroups per CU: the merging workgroups then hold up few others and the
-  // saved combine launch is the larger cost.  Larger grids use the combine
-  // kernel, measured faster there (the merge's device-scope traffic then runs
-  // under full HBM load and on the kernel's critical path).
-  a->fused = 0;
-  if (split_ws && units_of(p) <= PKV_MAX_FUSED_UNITS) {
-    int cus = 0;
-    if (query_cus(&cus) == PKV_OK && outer * inner <= 2 * (int64_t)cus) a->fused = 1;
-  }
+  a->fused = split_ws && pl.fused ? 1 : 0;
   a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
   return PKV_OK;
 }

@@ -36,20 +36,20 @@ def dev_tensors(w, device="cuda:0"):
     )
 
 
-def problem(w, num_splits=0):
+def problem(w, num_splits=0, heads_per_block=0):
     msb, msq = w.mask_strides
     return pkv.make_problem(batch=w.B, q_len=w.q_len, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
                             head_dim=w.D, page_size=w.page_size, num_pages=w.num_pages,
                             max_pages_per_seq=w.max_pages_per_seq, max_kv_len=w.max_kv_len,
                             scale=w.scale, causal_offset=w.causal_offset, num_splits=num_splits,
-                            mask_stride_b=msb, mask_stride_q=msq)
+                            mask_stride_b=msb, mask_stride_q=msq, heads_per_block=heads_per_block)
 
 
-def run(w, d=None, num_splits=0, stream=None, sync=True):
+def run(w, d=None, num_splits=0, stream=None, sync=True, heads_per_block=0):
     """Call pkv_paged_decode; return (out_bf16 bits uint16, out_f32 float32) as numpy."""
     if d is None:
         d = dev_tensors(w)
-    p = problem(w, num_splits)
+    p = problem(w, num_splits, heads_per_block)
     out = torch.empty(tuple(d["q"].shape), dtype=torch.bfloat16, device=d["q"].device)
     out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device=d["q"].device)
     pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale,

@@ -134,38 +134,102 @@ def test_forced_splits_are_returned_unchanged():
         assert pkv.num_splits(base_problem(num_splits=s), 256) == s
 
 
+def plan_of(p, cus=256):
+    info = pkv.plan(p, cus)
+    return info.splits, info.heads_per_block
+
+
 def test_split_heuristic_shapes():
     """Heuristic: one split when units fill the chip, more for few long sequences,
-    bounded by the key count and 64."""
-    # B=256, Hkv=8, R=32 -> 2 row blocks of 16: 4096 units >= 2*256 -> 1
+    bounded by the key count and 64; kv heads grouped per workgroup only on the
+    VALU kernel at D <= 128 and only for 2..8 splits."""
+    # B=256, Hkv=8, R=32 -> 2 row blocks of 16: 4096 units >= 2*256 -> 1 (matrix-core: one head)
     big = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
                        max_pages_per_seq=256, max_kv_len=8192, num_pages=13000)
-    assert pkv.num_splits(big, 256) == 1
+    assert plan_of(big) == (1, 1) and pkv.num_splits(big, 256) == 1
     # B=4, Hkv=8, G=4 (matrix-core rows, D=128) -> 32 units, 32768 keys -> one workgroup per CU
     long = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                         max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
-    assert pkv.num_splits(long, 256) == 8
-    # one row per kv head (VALU kernel): one workgroup per CU
+    assert plan_of(long) == (8, 1)
+    # one row per kv head (VALU kernel): grouping 4 or 2 heads would need 32 or 16 splits
     mha = base_problem(batch=4, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=64,
                        max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
-    assert pkv.num_splits(mha, 256) == 8
+    assert plan_of(mha) == (8, 1)
     # matrix-core rows (G=8) at D=64: two workgroups per CU; at D=128: one
     mf64 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
                         max_kv_len=4096, num_pages=2048)
-    assert pkv.num_splits(mf64, 256) == 4
+    assert plan_of(mf64) == (4, 1)
     mf128 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
                          max_kv_len=4096, num_pages=2048)
-    assert pkv.num_splits(mf128, 256) == 2
-    # short sequences cap the split count
+    assert plan_of(mf128) == (2, 1)
+    # VALU kernel, B=16, Hkv=8: four heads per workgroup and 8 splits at D <= 128, one head at 256
+    for d, want in ((32, (8, 4)), (64, (8, 4)), (128, (8, 4)), (256, (2, 1))):
+        v = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
+                         max_kv_len=4096, num_pages=2048)
+        assert plan_of(v) == want, d
+    # more sequences: fewer splits; at one split the heads stay apart (ragged lengths)
+    v64 = base_problem(batch=64, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
+                       max_kv_len=4096, num_pages=8192)
+    assert plan_of(v64) == (2, 4)
+    v256 = base_problem(batch=256, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
+                        max_kv_len=4096, num_pages=32768)
+    assert plan_of(v256) == (1, 1)
+    # short sequences cap the split count (two tiles per wave)
     short = base_problem(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
                          max_kv_len=100)
-    assert pkv.num_splits(short, 256) == 1
+    assert plan_of(short) == (4, 4)
+    short1 = base_problem(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
+                          max_kv_len=100, heads_per_block=1)
+    assert plan_of(short1) == (1, 1)
     # more CUs never means fewer splits
     assert pkv.num_splits(long, 512) >= pkv.num_splits(long, 256)
     # the heuristic never exceeds 64
     huge = base_problem(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=32, page_size=4096,
                         max_pages_per_seq=500, max_kv_len=2_000_000)
-    assert pkv.num_splits(huge, 1024) == 64
+    assert plan_of(huge, 1024) == (64, 1)
+
+
+def test_plan_report():
+    """pkv_plan: forced values unchanged, units and workgroups consistent, the
+    merge path and launch count as documented."""
+    v = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
+                     max_kv_len=4096, num_pages=2048)
+    info = pkv.plan(v, 256)
+    assert (info.splits, info.heads_per_block, info.rows_per_block, info.matrix_core) == (8, 4, 1, 0)
+    assert info.units == 16 * 2 and info.workgroups == info.units * 8
+    assert info.merge_in_kernel == 1 and info.kernels == 1      # 256 workgroups <= 2 per CU
+    forced = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
+                          max_kv_len=4096, num_pages=2048, num_splits=5, heads_per_block=2)
+    info = pkv.plan(forced, 256)
+    assert (info.splits, info.heads_per_block, info.units) == (5, 2, 16 * 4)
+    one = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
+                       max_kv_len=4096, num_pages=2048, num_splits=1)
+    info = pkv.plan(one, 256)
+    assert (info.splits, info.heads_per_block, info.merge_in_kernel, info.kernels) == (1, 1, 0, 1)
+    # many workgroups: the separate combine kernel
+    many = base_problem(batch=64, q_len=1, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
+                        max_kv_len=4096, num_pages=8192, num_splits=4)
+    info = pkv.plan(many, 256)
+    assert info.matrix_core == 1 and info.rows_per_block == 16 and info.units == 64 * 8
+    assert info.merge_in_kernel == 0 and info.kernels == 2
+    # more than PKV_MAX_FUSED_UNITS units never merge in-kernel
+    lots = base_problem(batch=4096, num_q_heads=8, num_kv_heads=2, head_dim=64, max_pages_per_seq=4,
+                        max_kv_len=100, num_pages=8, num_splits=2)
+    info = pkv.plan(lots, 100000)
+    assert info.units > pkv.PKV_MAX_FUSED_UNITS and info.merge_in_kernel == 0 and info.kernels == 2
+    empty = base_problem(batch=0)
+    assert pkv.plan(empty, 256).kernels == 0
+    with pytest.raises(pkv.PkvError):
+        pkv.plan(base_problem(heads_per_block=4), 256)          # Hkv = 2
+
+
+def test_heads_per_block_checks():
+    assert call(base_problem(num_splits=1, heads_per_block=-1)) == pkv.PKV_ERR_SHAPE
+    assert call(base_problem(num_splits=1, heads_per_block=3)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(base_problem(num_splits=1, heads_per_block=8, num_kv_heads=8)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(base_problem(num_splits=1, heads_per_block=4)) == pkv.PKV_ERR_SHAPE   # Hkv = 2
+    # a valid forced grouping passes every host check (the launch then fails without a GPU)
+    assert call(base_problem(num_splits=1, heads_per_block=2)) == pkv.PKV_ERR_LAUNCH
 
 
 def test_combine_argument_checks():
@@ -186,8 +250,12 @@ def test_status_strings_are_distinct():
 
 
 def test_problem_struct_layout():
-    assert ctypes.sizeof(pkv.Problem) == 64
+    # the C struct: twelve 4-byte fields, two int64 strides, heads_per_block, tail padding
+    assert ctypes.sizeof(pkv.Problem) == 72
     assert pkv.Problem.mask_stride_b.offset == 48
+    assert pkv.Problem.heads_per_block.offset == 64
+    assert ctypes.sizeof(pkv.PlanInfo) == 40
+    assert pkv.PlanInfo.units.offset == 16 and pkv.PlanInfo.merge_in_kernel.offset == 32
 
 
 def test_workspace_clear_checks():
@@ -199,5 +267,5 @@ def test_workspace_clear_checks():
 
 def test_grid_beyond_32bit_work_items_is_rejected():
     # 2^23 sequences x 2 kv heads = 2^24 workgroups of 256 threads: 2^32 work-items
-    assert call(base_problem(batch=1 << 23, num_splits=1)) == pkv.PKV_ERR_SHAPE
+    assert call(base_problem(batch=1 << 23, num_splits=1, heads_per_block=1)) == pkv.PKV_ERR_SHAPE
     assert pkv.combine_raw((1 << 25) * 2 + 8, 2, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_SHAPE

@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 from gpu_util import check, note, run, sub_batch  # noqa: E402
 
 
-def compare(w, num_splits=0, seqs=None):
+def compare(w, num_splits=0, seqs=None, heads_per_block=0):
     note(f"case {w.name} B={w.B} q_len={w.q_len} Hq={w.Hq} Hkv={w.Hkv} D={w.D} P={w.page_size} "
-         f"maxL={w.max_kv_len} splits={num_splits} seed={w.seed}")
-    out16, out32 = run(w, num_splits=num_splits)
+         f"maxL={w.max_kv_len} splits={num_splits} heads_per_block={heads_per_block} seed={w.seed}")
+    out16, out32 = run(w, num_splits=num_splits, heads_per_block=heads_per_block)
     if seqs is None:
         ref = oracle.decode(w)
         return check(out16, out32, ref, w.name)
@@ -97,6 +97,27 @@ def test_small_cases(i, splits):
     kw = dict(SMALL[i])
     w = workloads.build(f"small{i}", seed=2000 + i, spare_pages=3, **kw)
     compare(w, num_splits=splits)
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+@pytest.mark.parametrize("splits", [1, 5])
+@pytest.mark.parametrize("hpb", [1, 2, 4])
+def test_small_cases_heads_per_block(i, splits, hpb):
+    """Every kv-head grouping of a workgroup (one to four heads, one or more
+    waves per head) on the same cases."""
+    kw = dict(SMALL[i])
+    if kw["Hkv"] % hpb:
+        pytest.skip("heads per workgroup must divide Hkv")
+    w = workloads.build(f"small{i}", seed=2000 + i, spare_pages=3, **kw)
+    compare(w, num_splits=splits, heads_per_block=hpb)
+
+
+@pytest.mark.parametrize("hpb", [1, 2, 4])
+def test_sweep_heads_per_block_sampled(hpb):
+    """Full-size sweep shapes (VALU and matrix-core kernels) with each grouping."""
+    for D, Hq in ((64, 8), (32, 16), (128, 64), (256, 32)):
+        w = workloads.sweep(D, Hq)
+        compare(w, seqs=[0, 15], heads_per_block=hpb)
 
 
 def test_all_masked_and_empty_rows_are_zero():
