@@ -176,16 +176,13 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
       int j = base + pp * Lay::KPP + c.jq;
       j = j < jlast ? j : jlast;
       const float *mrow = a.mask + (int64_t)b * a.mask_sb + j;
-      if (a.mask_sq == 0) {
-        const float m0 = *mrow;
+      // one load per row on every path (a 2D mask, mask_sq = 0, loads the same
+      // entry for each row): a load count that depends on a runtime branch
+      // would make the compiler wait for all loads at the loop header
 #pragma unroll
-        for (int r = 0; r < RP; ++r) t.mk[pp][r] = m0;
-      } else {
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-          const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
-          t.mk[pp][r] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
-        }
+      for (int r = 0; r < RP; ++r) {
+        const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
+        t.mk[pp][r] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
       }
     }
   }

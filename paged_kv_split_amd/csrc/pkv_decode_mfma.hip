@@ -52,7 +52,8 @@ struct MLay {
   static constexpr int RPI = 64 / LPR;       // rows per load instruction
   static constexpr int NLD = KT / RPI;       // load instructions per 16-key tile (K or V)
   static constexpr int TILE_ELEMS = KT * D;  // bf16 per K (or V) tile
-  static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2;  // bytes: K + V tile
+  static constexpr int MASK_BYTES = 2 * 64 * 16;      // mask values: [row block][lane] float4
+  static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2 + MASK_BYTES;  // bytes: K + V tile, mask
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
   static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
   // merge phase: per-wave O rows, per-wave (m, l), per-row (M, W), wave factors
@@ -128,16 +129,13 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
       int j = base + 4 * q + i;
       j = j < jlast ? j : jlast;
       const float *mrow = a.mask + (int64_t)b * a.mask_sb + j;
-      if (a.mask_sq == 0) {
-        const float m0 = *mrow;
+      // one load per row block on every path (2D masks, mask_sq = 0, load the
+      // same entry): a branch-dependent load count makes the compiler wait for
+      // all loads at the loop header
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) t.mk[rb][i] = m0;
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
-          t.mk[rb][i] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
-        }
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
+        t.mk[rb][i] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
       }
     }
   }
@@ -150,9 +148,14 @@ struct MState {
   f32x4_t o[NRB][D / 16]; // O^T: d = 16*nb + 4q + i, row c
 };
 
-// Registers of one tile -> the wave's LDS slice (rows XOR-swizzled by chunk).
+// Registers of one tile -> the wave's LDS slice (rows XOR-swizzled by chunk;
+// each lane's mask values at [row block][lane]).  The mask goes through LDS
+// too, although each lane reads back its own values: kept in registers past
+// the reload of the tile, they would need a copy, and a copy of registers
+// whose loads are in flight makes the compiler wait for every load.
 template <int D, int NRB, bool MASK>
-__device__ __forceinline__ void mstore(const MTile<D, NRB, MASK> &t, uint16_t *kt, uint16_t *vt, int lane) {
+__device__ __forceinline__ void mstore(const MTile<D, NRB, MASK> &t, uint16_t *kt, uint16_t *vt, float *mkt,
+                                       int lane) {
   using L = MLay<D>;
 #pragma unroll
   for (int ii = 0; ii < L::NLD; ++ii) {
@@ -161,15 +164,19 @@ __device__ __forceinline__ void mstore(const MTile<D, NRB, MASK> &t, uint16_t *k
     reinterpret_cast<uint4 *>(kt + row * D)[L::swk(ch, row)] = t.k[ii];
     reinterpret_cast<uint4 *>(vt + row * D)[L::swv(ch, row)] = t.v[ii];
   }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      reinterpret_cast<float4 *>(mkt)[rb * 64 + lane] = make_float4(t.mk[rb][0], t.mk[rb][1], t.mk[rb][2], t.mk[rb][3]);
+  }
   __builtin_amdgcn_wave_barrier();
 }
 
 template <int D, int NRB, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int base,
-                                         const float (&mk)[MASK ? NRB : 1][4],
-                                         const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB], int b,
-                                         int r0, const uint16_t *kt, const uint16_t *vt, int lane,
-                                         MState<D, NRB> &st) {
+                                         const float *mkt, const uint4 (&qb)[NRB][D / 32],
+                                         const int (&lim)[NRB], int b, int r0, const uint16_t *kt,
+                                         const uint16_t *vt, int lane, MState<D, NRB> &st) {
   using L = MLay<D>;
   const int cc = lane & 15;
   const int q = lane >> 4;
@@ -190,14 +197,23 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
   float sv[NRB][4];
   float dmax = -INFINITY;   // NaN (-inf - -inf) is ignored by fmaxf
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+  for (int rb = 0; rb < NRB; ++rb) {
+    float mk[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (MASK) {
+      const float4 m4 = reinterpret_cast<const float4 *>(mkt)[rb * 64 + lane];
+      mk[0] = m4.x;
+      mk[1] = m4.y;
+      mk[2] = m4.z;
+      mk[3] = m4.w;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = base + 4 * q + i;
-      const float v = MASK ? fmaf(s4[rb][i], a.scale_log2, mk[rb][i] * kLog2e) : s4[rb][i] * a.scale_log2;
+      const float v = MASK ? fmaf(s4[rb][i], a.scale_log2, mk[i] * kLog2e) : s4[rb][i] * a.scale_log2;
       sv[rb][i] = (j < c.ke && j < lim[rb]) ? v : -INFINITY;
       dmax = fmaxf(dmax, sv[rb][i] - st.m[rb]);
     }
+  }
   // lazy reference max: move it (and rescale O, l) only when a score exceeds
   // it by more than kRescaleLog2; the branch is wave-uniform
   if (__builtin_amdgcn_ballot_w64(dmax > kRescaleLog2) != 0) {
@@ -259,41 +275,31 @@ __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b,
                                       int tnext, MTile<D, NRB, MASK> &tr, const uint4 (&qb)[NRB][D / 32],
                                       const int (&lim)[NRB], uint16_t *kt, uint16_t *vt, int lane,
                                       MState<D, NRB> &st) {
-  mstore<D, NRB, MASK>(tr, kt, vt, lane);
-  float mk[MASK ? NRB : 1][4];
-#pragma unroll
-  for (int rb = 0; rb < (MASK ? NRB : 1); ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mk[rb][i] = MASK ? tr.mk[rb][i] : 0.f;
+  float *mkt = reinterpret_cast<float *>(vt + MLay<D>::TILE_ELEMS);
+  mstore<D, NRB, MASK>(tr, kt, vt, mkt, lane);
   // unconditional (a tile past the end loads the last key again, clamped in
   // mload): the loads in flight are then the same on every path, and the
   // wait before the next tile leaves this prefetch in flight
   mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + tnext * KT, lane, tr);
-  mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mk, qb, lim, b, r0, kt, vt, lane, st);
+  mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mkt, qb, lim, b, r0, kt, vt, lane, st);
 }
 
-// Register tiles per wave: two (one at D = 256, where two would spill).
-// Four were measured slower at every D < 256, even where the occupancy
-// stayed the same.
-template <int D, int NRB>
-constexpr int mfma_nbuf() { return D >= 256 ? 1 : 2; }
+// Register tiles per wave, as measured on MI355X (B = 16 x 4096 keys and
+// B = 4 x 32768 keys, Hkv = 8): one, so that each wave keeps a single tile's
+// loads in flight while it computes the previous tile -- at D <= 64 (two
+// workgroups per CU) that is 8-11% faster than two, and at D = 128 without a
+// mask 7-9% faster; two at D = 128 with a mask (5% faster there); one at
+// D = 256, where two would spill.  More bytes in flight per CU than that
+// made the random-page K/V stream slower, not faster (four tiles: up to 60%).
+template <int D, int NRB, bool MASK>
+constexpr int mfma_nbuf() { return (D == 128 && MASK) ? 2 : 1; }
 
 // The key-tile loop of one wave: tiles t0, t0 + tstep, ...
-template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE, int NBUF = mfma_nbuf<D, NRB>()>
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE, int NBUF = mfma_nbuf<D, NRB, MASK>()>
 __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, int b, int r0, int wb, int t0,
                                            int tstep, int ntiles, const uint4 (&qb)[NRB][D / 32],
                                            const int (&lim)[NRB], uint16_t *kt, uint16_t *vt, int lane,
                                            MState<D, NRB> &st) {
-  if constexpr (D >= 256) {
-    // one register tile (two would spill at D = 256): the next tile's loads
-    // are issued right after this tile reaches LDS and fly during its compute
-    if (t0 >= ntiles) return;
-    MTile<D, NRB, MASK> tr;
-    mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + t0 * KT, lane, tr);
-    for (int t = t0; t < ntiles; t += tstep)
-      mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, t, t + tstep, tr, qb, lim, kt, vt, lane, st);
-    return;
-  }
   // NBUF register tiles in a ring: tile t sits in buffer (t / tstep) % NBUF; a
   // tile goes to LDS, then the loads of the tile NBUF steps ahead are issued
   // into the freed registers
@@ -320,12 +326,14 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
   }
 }
 
-// Two resident workgroups per CU (2 waves per SIMD) where the registers allow.
-template <int D, int NRB>
-constexpr int mfma_min_blocks() { return (D >= 256 && NRB == 2) ? 1 : 2; }
+// Two resident workgroups per CU (2 waves per SIMD) where the registers allow:
+// not with two row blocks at D = 256, nor at D = 128 with a mask (which spills
+// within 256 registers).
+template <int D, int NRB, bool MASK>
+constexpr int mfma_min_blocks() { return (NRB == 2 && (D >= 256 || (D == 128 && MASK))) ? 1 : 2; }
 
 template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
-__global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB>())) void split_decode_mfma(
+__global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>())) void split_decode_mfma(
     const DecodeArgs a) {
   using L = MLay<D>;
   constexpr int NW = L::NW;

@@ -135,22 +135,27 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb) {
 }
 
 // Kv heads per workgroup.  Grouping the heads of a page slot in one
-// workgroup (one wave per head at hpb = 4) makes it read longer runs of each
-// slot, which HBM serves faster than separate D * 2-byte head slices: on
-// MI355X the VALU kernel gains 13% at D = 64 and 5% at D = 128 (B = 16,
-// 4096 keys, Hkv = 8), nothing at D = 256.  Grouping multiplies the splits
-// needed to fill the chip by hpb; it is taken only while that count stays in
-// [2, kMaxGroupedSplits]: at one split a workgroup holds hpb whole sequences
-// and ragged lengths unbalance the grid (B = 256 lognormal lengths: 1.65x
-// slower), and more splits cost more partial traffic.  The matrix-core kernel
-// measured no gain (its 16-key tiles keep fewer bytes in flight per wave),
-// so it keeps one head per workgroup.
+// workgroup (one or two waves per head) makes it read longer runs of each
+// slot, which HBM serves faster than separate D * 2-byte head slices.
+// Measured on MI355X (B = 16, 4096 keys, Hkv = 8): the VALU kernel gains 13%
+// at D = 64 and 5% at D = 128 with four heads, nothing at D = 256; the
+// matrix-core kernel gains 2-3% with two heads at D = 64 and 128 and loses
+// with four (its 16-key tiles keep fewer bytes in flight per wave) and at
+// D = 32 and 256.  Grouping multiplies the splits needed to fill the chip by
+// hpb; it is taken only while that count stays in [2, kMaxGroupedSplits]: at
+// one split a workgroup holds hpb whole sequences and ragged lengths
+// unbalance the grid (B = 256 lognormal lengths: 1.65x slower), and more
+// splits cost more partial traffic.
 constexpr int kMaxGroupedSplits = 8;
 
-int heuristic_hpb(const pkv_problem *p, int cus) {
+int max_heads_per_block(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  if (pkv::use_mfma(R) || p->head_dim > 128) return 1;
-  for (int hpb = pkv::kMaxHeadsPerBlock; hpb > 1; hpb /= 2) {
+  if (pkv::use_mfma(R)) return (p->head_dim == 64 || p->head_dim == 128) ? 2 : 1;
+  return p->head_dim <= 128 ? pkv::kMaxHeadsPerBlock : 1;
+}
+
+int heuristic_hpb(const pkv_problem *p, int cus) {
+  for (int hpb = max_heads_per_block(p); hpb > 1; hpb /= 2) {
     if (p->num_kv_heads % hpb) continue;
     const int s = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, hpb);
     if (s >= 2 && s <= kMaxGroupedSplits) return hpb;

@@ -155,13 +155,18 @@ def test_split_heuristic_shapes():
     mha = base_problem(batch=4, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=64,
                        max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
     assert plan_of(mha) == (8, 1)
-    # matrix-core rows (G=8) at D=64: two workgroups per CU; at D=128: one
-    mf64 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64, max_pages_per_seq=128,
-                        max_kv_len=4096, num_pages=2048)
-    assert plan_of(mf64) == (4, 1)
-    mf128 = base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
-                         max_kv_len=4096, num_pages=2048)
-    assert plan_of(mf128) == (2, 1)
+    # matrix-core rows (G=8) at D=64: two workgroups per CU, two heads each; at D=128: one workgroup
+    # per CU; at D=32 and 256 one head per workgroup
+    mf = {d: base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
+                          max_kv_len=4096, num_pages=2048) for d in (32, 64, 128, 256)}
+    assert plan_of(mf[32]) == (4, 1)
+    assert plan_of(mf[64]) == (8, 2)
+    assert plan_of(mf[128]) == (4, 2)
+    assert plan_of(mf[256]) == (4, 1)
+    # B=8 decode (1B model): grouping would need 16+ splits -> one head per workgroup
+    d1b = base_problem(batch=8, num_q_heads=24, num_kv_heads=4, head_dim=64, max_pages_per_seq=64,
+                       max_kv_len=2048, num_pages=512)
+    assert plan_of(d1b)[1] == 1
     # VALU kernel, B=16, Hkv=8: four heads per workgroup and 8 splits at D <= 128, one head at 256
     for d, want in ((32, (8, 4)), (64, (8, 4)), (128, (8, 4)), (256, (2, 1))):
         v = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
@@ -210,11 +215,12 @@ def test_plan_report():
     many = base_problem(batch=64, q_len=1, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
                         max_kv_len=4096, num_pages=8192, num_splits=4)
     info = pkv.plan(many, 256)
-    assert info.matrix_core == 1 and info.rows_per_block == 16 and info.units == 64 * 8
+    assert info.matrix_core == 1 and info.rows_per_block == 16 and info.heads_per_block == 2
+    assert info.units == 64 * 4
     assert info.merge_in_kernel == 0 and info.kernels == 2
     # more than PKV_MAX_FUSED_UNITS units never merge in-kernel
     lots = base_problem(batch=4096, num_q_heads=8, num_kv_heads=2, head_dim=64, max_pages_per_seq=4,
-                        max_kv_len=100, num_pages=8, num_splits=2)
+                        max_kv_len=100, num_pages=8, num_splits=2, heads_per_block=1)
     info = pkv.plan(lots, 100000)
     assert info.units > pkv.PKV_MAX_FUSED_UNITS and info.merge_in_kernel == 0 and info.kernels == 2
     empty = base_problem(batch=0)
