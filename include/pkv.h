@@ -195,7 +195,8 @@ int pkv_paged_decode_partials(const pkv_problem *p, const void *q,
 /* The combine step alone: merges `splits` partials per row with the
  * log-sum-exp rule  M = max_{l_s>0} m_s,  w_s = l_s exp(m_s - M),
  * out = sum_s w_s o_s / sum_s w_s  (0 when no partial has l_s > 0); the
- * o_part rows of partials with l_s = 0 are never read.
+ * o_part rows of partials with l_s = 0 are never read; a row with exactly one
+ * partial of l_s > 0 gets that o_s unchanged.
  *   o_part   fp32 [rows, splits, head_dim]   (16-byte aligned)
  *   ml_part  fp32 [rows, splits, 2]          (m, l), 8-byte aligned
  *   out_bf16 bf16 [rows, head_dim] (16-byte aligned), out_f32 NULL or fp32 [rows, head_dim]

@@ -407,8 +407,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   const int inner_idx = slot % a.inner;
   const int outer_idx = (slot / a.inner) * 8 + xcd;
   if (outer_idx >= a.outer) return;
-  const int b = outer_idx / a.S;
-  const int s = outer_idx - b * a.S;
+  int b, s;
+  decode_pair(a, outer_idx, b, s);
   const int hg = inner_idx / a.nrb;
   const int rb = inner_idx - hg * a.nrb;
 
@@ -441,6 +441,17 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     lim[r] = lr;
     kmax = lr > kmax ? lr : kmax;
   }
+
+  // splits past the unit's keys: no work; outside the in-kernel merge they
+  // leave (m, l) = (-inf, 0) for the combine step
+  const int nact = active_splits(a, kmax);
+  const int nrows = (a.R - r0 < RP ? a.R - r0 : RP) * a.hpb;
+  if (s >= nact) {
+    if (!a.fused) empty_partials(a, b, hg, r0, s, nrows);
+    return;
+  }
+  // the unit's only split with keys writes the output itself
+  const bool direct = !a.partials || (a.fused && nact == 1);
 
   Ctx<D, RP> c;
   c.kbase = a.k + g * D;
@@ -559,7 +570,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   }
   float *rmw = mlb + NW * RP * 2;                  // [RP * hpb][2]: merged (M, W) per row
   float *fw = rmw + RP * kMaxHeadsPerBlock * 2;    // [NW * RP]: normalised wave factors
-  const int nrows = (a.R - r0 < RP ? a.R - r0 : RP) * a.hpb;
   __syncthreads();
   if (threadIdx.x < nrows) {
     const int ri = threadIdx.x;
@@ -586,8 +596,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
       if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * D + d], o);
     return o;
   };
-  write_rows<D>(a, s, rowtab, nrows, resn, Mrow, Wrow, NW * 64);
-  fused_tail<D>(a, b * a.inner + inner_idx, rowtab, nrows, smem, NW * 64);
+  write_rows<D>(a, s, direct, rowtab, nrows, resn, Mrow, Wrow, NW * 64);
+  if (a.fused && !direct) fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrows, smem, NW * 64);
 }
 
 // Combine (the standalone pkv_combine entry point): each block merges
@@ -601,7 +611,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int64_t base = (int64_t)blockIdx.x * NR;
   const int64_t left = a.rows - base;
   const int nrows = left < NR ? (int)left : NR;
-  merge_rows<D, false>(a.o_part, a.ml_part, a.S, [&](int r) { return base + r; }, nrows, a.out, a.out_f32, 256);
+  merge_rows<D, false>(a.o_part, a.ml_part, a.S, a.S, [&](int r) { return base + r; }, nrows, a.out, a.out_f32,
+                       256);
 }
 
 // Zero-fill (workspace counters); a kernel, not a memset, so it may sit in a

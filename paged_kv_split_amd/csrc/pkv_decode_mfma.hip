@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   const int inner_idx = slot % a.inner;
   const int outer_idx = (slot / a.inner) * 8 + xcd;
   if (outer_idx >= a.outer) return;
-  const int b = outer_idx / a.S;
-  const int s = outer_idx - b * a.S;
+  int b, s;
+  decode_pair(a, outer_idx, b, s);
   const int hg = inner_idx / a.nrb;
   const int rg = inner_idx - hg * a.nrb;
 
@@ -380,6 +380,17 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   for (int rb = 0; rb < NRB; ++rb) lim[rb] = row_limit(r0 + cc + 16 * rb);
   const int rlast = (r0 + RW < a.R ? r0 + RW : a.R) - 1;
   const int kmax = row_limit(rlast);   // the last row sees the most keys
+
+  // splits past the unit's keys: no work; outside the in-kernel merge they
+  // leave (m, l) = (-inf, 0) for the combine step
+  const int nact = active_splits(a, kmax);
+  const int nrt = (a.R - r0 < RW ? a.R - r0 : RW) * a.hpb;  // output rows of the block
+  if (s >= nact) {
+    if (!a.fused) empty_partials(a, b, hg, r0, s, nrt);
+    return;
+  }
+  // the unit's only split with keys writes the output itself
+  const bool direct = !a.partials || (a.fused && nact == 1);
 
   int *bt_lds = reinterpret_cast<int *>(smem_raw);
   uint16_t *kt = reinterpret_cast<uint16_t *>(smem_raw + L::BT_BYTES + w * L::WAVE_LDS);
@@ -509,10 +520,10 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
         if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * L::OB_STRIDE + d], o);
       return o;
     };
-    write_rows<D>(a, s, rowtab + 16 * rb * a.hpb, nrows, resn, Mrow, Wrow, NW * 64);
+    write_rows<D>(a, s, direct, rowtab + 16 * rb * a.hpb, nrows, resn, Mrow, Wrow, NW * 64);
   }
-  fused_tail<D>(a, b * a.inner + inner_idx, rowtab, (a.R - r0 < RW ? a.R - r0 : RW) * a.hpb,
-                reinterpret_cast<float *>(smem_raw), NW * 64);
+  if (a.fused && !direct)
+    fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 
 template <int D, int NRB, bool C, bool M, bool U>

@@ -117,6 +117,25 @@ __device__ __forceinline__ float2 load2(const float *p) {  // p 8-byte aligned
   }
 }
 
+// The (sequence b, split s) pair of outer index p (0 <= p < B * S).  The
+// split-major order puts every sequence's first split ahead of any second
+// one, and rotating the sequences by 3s between splits gives each XCD (the
+// pairs p, p + 8, ... land on one XCD) a mix of sequences and split
+// positions, so ragged lengths and splits past a sequence's end spread over
+// the XCDs rather than piling onto some.
+__device__ __forceinline__ void decode_pair(const DecodeArgs &a, int p, int &b, int &s) {
+  s = p / a.B;
+  b = p - s * a.B + 3 * s;
+  b %= a.B;
+}
+
+// Splits of a unit that hold keys: its rows see kmax keys at most.  At least
+// one, so that a unit without keys still writes its (zero) output.
+__device__ __forceinline__ int active_splits(const DecodeArgs &a, int kmax) {
+  const int n = (kmax + a.chunk - 1) / a.chunk;
+  return n < 1 ? 1 : (n > a.S ? a.S : n);
+}
+
 // Output row (b, i, h) of packed row rr (= i * G + k) of kv head g.
 __device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, int rr) {
   const int i = rr / a.G;
@@ -125,12 +144,16 @@ __device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, in
 }
 
 // ---- log-sum-exp merge of split partials -----------------------------------
-// For each of `nrows` rows (row index rowf(r)) and each 4-element group of
-// its D outputs, one thread walks the S partials in split order 0..S-1 with
+// For each of `nrows` rows (row index rowf(r); partials of a row S apart) and
+// each 4-element group of its D outputs, one thread walks the first nsp <= S
+// partials in split order with
 // an online merge: partials with l_s = 0 are skipped (their o rows are never
 // used); otherwise, when m_s exceeds the running max M the running sums are
 // rescaled by exp(M - m_s), then w_s = l_s exp(m_s - M) is added to W and
-// w_s o_s to the accumulator.  out = acc * (1 / W), 0 when W = 0.  This is
+// w_s o_s to the accumulator.  out = acc * (1 / W), 0 when W = 0, and o_s
+// itself when s is the only partial with l_s > 0 (so a row that one split
+// covers gets the same bits whether that split wrote the output or a merge
+// of its partial did).  This is
 // the log-sum-exp rule M = max m_s, out = sum_s l_s e^(m_s - M) o_s / sum_s
 // l_s e^(m_s - M), evaluated in one pass.  Each thread loads the (m, l) of
 // the splits itself, so no LDS and no barrier are needed.  Both the in-kernel
@@ -152,8 +175,8 @@ __device__ __forceinline__ float4 load4(const float *p) {  // p 16-byte aligned
 }
 
 template <int D, bool DEV, class RowF>
-__device__ void merge_rows(const float *o_part, const float *ml_part, int S, RowF rowf, int nrows, uint16_t *out,
-                           float *out_f32, int nthreads) {
+__device__ void merge_rows(const float *o_part, const float *ml_part, int S, int nsp, RowF rowf, int nrows,
+                           uint16_t *out, float *out_f32, int nthreads) {
   constexpr int DQ = D / 4;  // 4-element groups per row (a power of two)
   constexpr int NB = kMergeBatch;
   const int tid = threadIdx.x;
@@ -161,7 +184,7 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
   // split) pairs, group-major, split order within a group
   const int ngroups = nrows * DQ;
   const int mine = tid < ngroups ? (ngroups - 1 - tid) / nthreads + 1 : 0;
-  const int items = mine * S;
+  const int items = mine * nsp;
   float4 ov[NB];
   float2 mv[NB];
   int ig = tid, isp = 0;
@@ -179,7 +202,7 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
       if (i0 + k < items) {
         ov[k] = load4<DEV>(ip);
         mv[k] = load2<DEV>(im);
-        if (++isp == S) {
+        if (++isp == nsp) {
           isp = 0;
           ig += nthreads;
           if (i0 + k + 1 < items) group_start(ig);
@@ -194,6 +217,8 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
 
   float M = -INFINITY, W = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 first = acc;  // o of the first partial with l > 0
+  int used = 0;        // partials with l > 0 so far
   int cg = tid, csp = 0;
   for (int i0 = 0; i0 < items; i0 += NB) {
     if (i0 > 0) issue(i0);
@@ -203,6 +228,7 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
         const float m = mv[k].x;
         const float l = mv[k].y;
         if (l > 0.f) {
+          if (used++ == 0) first = ov[k];
           if (m > M) {
             const float sc = fast_exp2((M - m) * kLog2e);
             W *= sc;
@@ -219,12 +245,13 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
           acc.z = fmaf(wk, ov[k].z, acc.z);
           acc.w = fmaf(wk, ov[k].w, acc.w);
         }
-        if (++csp == S) {
+        if (++csp == nsp) {
           const int r = cg / DQ;
           const int64_t row = rowf(r);
           const int d = 4 * (cg - r * DQ);
           const float inv = W > 0.f ? 1.f / W : 0.f;
-          const float4 res = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+          const float4 res =
+              used == 1 ? first : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(res.x) | ((uint32_t)f32_to_bf16_rne(res.y) << 16);
           const uint32_t hi = (uint32_t)f32_to_bf16_rne(res.z) | ((uint32_t)f32_to_bf16_rne(res.w) << 16);
           *reinterpret_cast<uint2 *>(out + row * D + d) = make_uint2(lo, hi);
@@ -232,6 +259,7 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
           M = -INFINITY;
           W = 0.f;
           acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          used = 0;
           csp = 0;
           cg += nthreads;
         }
@@ -240,23 +268,33 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, Row
   }
 }
 
+// A split with no keys of its unit, outside the in-kernel merge: its (m, l)
+// entries become (-inf, 0) (its o_part rows are left untouched, never read).
+// Block row ri = r * hpb + hh is packed row r0 + r of kv head hg * hpb + hh.
+__device__ __forceinline__ void empty_partials(const DecodeArgs &a, int b, int hg, int r0, int s, int nrows) {
+  for (int ri = threadIdx.x; ri < nrows; ri += blockDim.x) {
+    const int64_t row = out_row(a, b, hg * a.hpb + (ri & (a.hpb - 1)), r0 + (ri >> a.lhpb));
+    *reinterpret_cast<float2 *>(a.ml_part + (row * a.S + s) * 2) = make_float2(-INFINITY, 0.f);
+  }
+}
+
 // Epilogue shared by the split kernels once a block has merged its waves for
-// packed rows r0 .. r0+nrows-1: `rowtab[r]` is the output row of packed row
-// r0 + r, `resn(r, d)` the normalised result (0 when the row saw no key),
-// `Mrow(r)` the base-2 reference max and `Wrow(r)` the total weight.  One
-// split: write the output.  Several splits: write this split's partial
-// (o = resn, m in natural-log units, l = W); an empty split (W = 0) writes
-// only (m, l) = (-inf, 0).
+// its nrows output rows: `rowtab[r]` is the output row of block row r,
+// `resn(r, d)` the normalised result (0 when the row saw no key), `Mrow(r)`
+// the base-2 reference max and `Wrow(r)` the total weight.  `direct`: write
+// the output (the unit's only split with keys).  Otherwise write this split's
+// partial (o = resn, m in natural-log units, l = W); an empty split (W = 0)
+// writes only (m, l) = (-inf, 0).
 template <int D, class ResF, class MF, class WF>
-__device__ void write_rows(const DecodeArgs &a, int s, const int64_t *rowtab, int nrows, ResF resn, MF Mrow,
-                           WF Wrow, int nthreads) {
+__device__ void write_rows(const DecodeArgs &a, int s, bool direct, const int64_t *rowtab, int nrows, ResF resn,
+                           MF Mrow, WF Wrow, int nthreads) {
   constexpr int DP = D / 2;
   for (int idx = threadIdx.x; idx < nrows * DP; idx += nthreads) {
     const int r = idx / DP;
     const int d = 2 * (idx - r * DP);
     const int64_t row = rowtab[r];
     const float W = Wrow(r);
-    if (!a.partials) {
+    if (direct) {
       const float vx = resn(r, d);
       const float vy = resn(r, d + 1);
       *reinterpret_cast<uint32_t *>(a.out + row * D + d) =
@@ -298,24 +336,24 @@ __device__ __forceinline__ void wave_factors(const float (&m)[NW], const float (
   for (int ww = 0; ww < NW; ++ww) f[ww] *= inv;
 }
 
-// With a.fused (several splits, one call): every block of a unit stores its
-// partial, waits for those stores to complete and counts itself in; the block
-// that arrives last merges the unit's partials and resets the counter, so the
-// workspace is ready for the next call.  `lds` (one int) is free: all block
-// threads are past their last use of it when this is called.
+// With a.fused (several splits, one call): each of the unit's n active
+// splits (those that hold keys of it) stores its partial, waits for those
+// stores to complete and counts itself in; the block that arrives last merges
+// the n partials and resets the counter, so the workspace is ready for the
+// next call.  `lds` (one int) is free: all block threads are past their last
+// use of it when this is called.
 template <int D>
-__device__ void fused_tail(const DecodeArgs &a, int unit, const int64_t *rowtab, int nrows, float *lds,
+__device__ void fused_tail(const DecodeArgs &a, int unit, int n, const int64_t *rowtab, int nrows, float *lds,
                            int nthreads) {
-  if (!a.fused) return;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   __syncthreads();
   int *flag = reinterpret_cast<int *>(lds);
-  if (threadIdx.x == 0) flag[0] = atomicAdd(a.counters + unit, 1) == a.S - 1;
+  if (threadIdx.x == 0) flag[0] = atomicAdd(a.counters + unit, 1) == n - 1;
   __syncthreads();
   const bool last = flag[0] != 0;
   __syncthreads();
   if (!last) return;
-  merge_rows<D, true>(a.o_part, a.ml_part, a.S, [&](int r) { return rowtab[r]; }, nrows, a.out, a.out_f32,
+  merge_rows<D, true>(a.o_part, a.ml_part, a.S, n, [&](int r) { return rowtab[r]; }, nrows, a.out, a.out_f32,
                       nthreads);
   if (threadIdx.x == 0) a.counters[unit] = 0;  // ready for the next call
 }

@@ -89,12 +89,27 @@ int query_cus(int *out) {
 }
 
 // Split heuristic (keys only along the sequence axis, in the spirit of the
-// pages' compute_num_splits and ejkernel's num_splits = 0 "auto"): split each
-// sequence so that the grid has about blocks_per_cu() workgroups per CU (no
-// split when the (sequence, kv-head group, row block) units alone reach
-// that), never below kMinTilesPerWave tiles per wave and never above 64
-// splits.
+// pages' compute_num_splits and ejkernel's num_splits = 0 "auto").  Few
+// units: split each sequence so that the grid has about blocks_per_cu()
+// workgroups per CU, never below kMinTilesPerWave tiles per wave and never
+// above 64 splits.  Units that fill the chip by themselves: cap the keys of
+// one workgroup at split_cap_keys(), so that in a ragged batch the longest
+// sequences do not run alone at the end of the launch (splits past a
+// sequence's end exit at once; a sequence that fits one split writes its
+// output directly).
 constexpr int kMinTilesPerWave = 2;
+
+// Keys per workgroup in a batch that fills the chip: at least 1024, and at
+// least 64 per packed row, so that the partials of a split sequence (rows * D
+// fp32 per split, written and read back) stay within 2 / 64 of its K/V bytes.
+// Measured on MI355X for B = 256 lognormal lengths (median 1024, clipped to
+// [32, 8192], 32 rows per kv head, D = 128): 4 splits of 2048 keys in place
+// of one take a call from 425 to 377 us (8 splits of 1024: 403 us).
+int split_cap_keys(const pkv_problem *p) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  const int cap = 64 * R;
+  return cap > 1024 ? cap : 1024;
+}
 
 // Workgroups per CU to aim at, measured on MI355X over the decode shapes:
 // one where a workgroup keeps enough K/V bytes in flight to cover memory
@@ -123,7 +138,10 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb) {
   const int64_t units = units_of(p, hpb);
   if (units <= 0) return 1;
   const int64_t target = (int64_t)cus * blocks_per_cu(p);
-  if (units >= target) return 1;
+  if (units >= target) {
+    const int64_t s = ceil_div(max_len_of(p), split_cap_keys(p));
+    return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
+  }
   const int T = pkv::tile_keys(p->head_dim);
   const int64_t min_keys = (int64_t)T * (pkv::kWavesPerBlock / hpb) * kMinTilesPerWave;
   const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
@@ -141,11 +159,11 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb) {
 // at D = 64 and 5% at D = 128 with four heads, nothing at D = 256; the
 // matrix-core kernel gains 2-3% with two heads at D = 64 and 128 and loses
 // with four (its 16-key tiles keep fewer bytes in flight per wave) and at
-// D = 32 and 256.  Grouping multiplies the splits needed to fill the chip by
-// hpb; it is taken only while that count stays in [2, kMaxGroupedSplits]: at
-// one split a workgroup holds hpb whole sequences and ragged lengths
-// unbalance the grid (B = 256 lognormal lengths: 1.65x slower), and more
-// splits cost more partial traffic.
+// D = 32 and 256; in batches that fill the chip the VALU kernel gains up to
+// 13% with four heads (B = 64 and 256).  Grouping is taken only while the
+// split count stays in [2, kMaxGroupedSplits]: at one split a workgroup would
+// hold hpb whole sequences, which ragged lengths unbalance (B = 256 lognormal
+// lengths: 1.65x slower), and more splits cost more partial traffic.
 constexpr int kMaxGroupedSplits = 8;
 
 int max_heads_per_block(const pkv_problem *p) {
@@ -176,12 +194,13 @@ Plan make_plan(const pkv_problem *p, int cus) {
   pl.hpb = p->heads_per_block > 0 ? p->heads_per_block : heuristic_hpb(p, cus);
   pl.S = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, pl.hpb);
   pl.units = units_of(p, pl.hpb);
-  // In-kernel merge (a counter for every unit) when the grid has at most two
-  // workgroups per CU: the merging workgroups then hold up few others and the
-  // saved combine launch is the larger cost.  Larger grids use the combine
-  // kernel, measured faster there (the merge's device-scope traffic then runs
-  // under full HBM load and on the kernel's critical path).
-  pl.fused = pl.S > 1 && pl.units <= PKV_MAX_FUSED_UNITS && pl.units * pl.S <= 2 * (int64_t)cus;
+  // In-kernel merge (a counter for every unit) whenever the counters fit the
+  // workspace head.  Splits past a sequence's end exit at once and a unit
+  // with one split holding keys writes its output directly, so only units
+  // split for real merge, each as soon as its last split ends; on MI355X this
+  // matched or beat a separate combine launch from 24 to 8192 workgroups
+  // (B = 256 ragged: 377 against 403 us).
+  pl.fused = pl.S > 1 && pl.units <= PKV_MAX_FUSED_UNITS;
   return pl;
 }
 

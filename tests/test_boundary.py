@@ -140,13 +140,19 @@ def plan_of(p, cus=256):
 
 
 def test_split_heuristic_shapes():
-    """Heuristic: one split when units fill the chip, more for few long sequences,
-    bounded by the key count and 64; kv heads grouped per workgroup only on the
-    VALU kernel at D <= 128 and only for 2..8 splits."""
-    # B=256, Hkv=8, R=32 -> 2 row blocks of 16: 4096 units >= 2*256 -> 1 (matrix-core: one head)
+    """Heuristic: when units fill the chip, splits of at most max(1024, 64 R)
+    keys; for few long sequences, splits that fill the chip, bounded by the key
+    count and 64; kv heads grouped per workgroup only for 2..8 splits of a
+    batch that does not fill the chip by itself."""
+    # B=256, Hkv=8, R=32 (one 32-row workgroup per kv head): units fill the chip -> splits of
+    # 64 * 32 = 2048 keys over max_kv_len 8192 -> 4, two heads per workgroup
     big = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
                        max_pages_per_seq=256, max_kv_len=8192, num_pages=13000)
-    assert plan_of(big) == (1, 1) and pkv.num_splits(big, 256) == 1
+    assert plan_of(big) == (4, 2) and pkv.num_splits(big, 256) == 4
+    # the same batch with short sequences: one split
+    big_short = base_problem(batch=256, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                             max_pages_per_seq=64, max_kv_len=2048, num_pages=13000)
+    assert plan_of(big_short) == (1, 1)
     # B=4, Hkv=8, G=4 (matrix-core rows, D=128) -> 32 units, 32768 keys -> one workgroup per CU
     long = base_problem(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64,
                         max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
@@ -172,13 +178,14 @@ def test_split_heuristic_shapes():
         v = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
                          max_kv_len=4096, num_pages=2048)
         assert plan_of(v) == want, d
-    # more sequences: fewer splits; at one split the heads stay apart (ragged lengths)
+    # more sequences: fewer splits; once the units fill the chip the splits hold at most
+    # 1024 keys (one row per kv head)
     v64 = base_problem(batch=64, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
                        max_kv_len=4096, num_pages=8192)
     assert plan_of(v64) == (2, 4)
     v256 = base_problem(batch=256, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
                         max_kv_len=4096, num_pages=32768)
-    assert plan_of(v256) == (1, 1)
+    assert plan_of(v256) == (4, 4)
     # short sequences cap the split count (two tiles per wave)
     short = base_problem(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
                          max_kv_len=100)
@@ -211,13 +218,13 @@ def test_plan_report():
                        max_kv_len=4096, num_pages=2048, num_splits=1)
     info = pkv.plan(one, 256)
     assert (info.splits, info.heads_per_block, info.merge_in_kernel, info.kernels) == (1, 1, 0, 1)
-    # many workgroups: the separate combine kernel
+    # many workgroups still merge in-kernel (units within the counter head)
     many = base_problem(batch=64, q_len=1, num_q_heads=64, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,
                         max_kv_len=4096, num_pages=8192, num_splits=4)
     info = pkv.plan(many, 256)
     assert info.matrix_core == 1 and info.rows_per_block == 16 and info.heads_per_block == 2
-    assert info.units == 64 * 4
-    assert info.merge_in_kernel == 0 and info.kernels == 2
+    assert info.units == 64 * 4 and info.workgroups == 64 * 4 * 4
+    assert info.merge_in_kernel == 1 and info.kernels == 1
     # more than PKV_MAX_FUSED_UNITS units never merge in-kernel
     lots = base_problem(batch=4096, num_q_heads=8, num_kv_heads=2, head_dim=64, max_pages_per_seq=4,
                         max_kv_len=100, num_pages=8, num_splits=2, heads_per_block=1)

@@ -304,9 +304,11 @@ def test_many_units_use_the_combine_kernel():
     B = pkv.PKV_MAX_FUSED_UNITS // 8 + 9
     rng = np.random.default_rng(11)
     lens = rng.integers(0, 150, B)
-    w = workloads.build("manyunits", B=B, q_len=1, Hq=8, Hkv=8, D=32, page_size=16,
+    # matrix-core rows at D = 32: one kv head per workgroup, B * Hkv units
+    w = workloads.build("manyunits", B=B, q_len=1, Hq=64, Hkv=8, D=32, page_size=16,
                         kv_lens=lens, seed=3300)
-    assert w.B * w.Hkv > pkv.PKV_MAX_FUSED_UNITS
+    info = pkv.plan(problem(w, num_splits=3))
+    assert info.units > pkv.PKV_MAX_FUSED_UNITS and not info.merge_in_kernel and info.kernels == 2
     out16, out32 = run(w, num_splits=3)
     seqs = [0, 1, int(np.argmax(lens)), B // 2, B - 1]
     ref = oracle.decode(sub_batch(w, seqs))
@@ -319,12 +321,13 @@ def test_one_workspace_serves_calls_of_any_shape():
     counter head is zero after every call."""
     shapes = [
         dict(B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[800, 20, 0, 1400]),
-        dict(B=600, q_len=1, Hq=8, Hkv=8, D=64, page_size=16, kv_lens=[70] * 600),  # 4800 units
+        dict(B=600, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 600),  # 4800 units
         dict(B=2, q_len=3, Hq=16, Hkv=2, D=64, page_size=8, kv_lens=[300, 41], causal="last"),
         dict(B=1, q_len=1, Hq=8, Hkv=1, D=32, page_size=64, kv_lens=[5000]),
     ]
     ws = [workloads.build(f"reuse{i}", seed=3400 + i, **kw) for i, kw in enumerate(shapes)]
     plans = [(w, S) for w in ws for S in (5, 2)]
+    assert {pkv.plan(problem(w, num_splits=S)).merge_in_kernel for w, S in plans} == {0, 1}
     need_o = max(pkv.workspace_bytes(problem(w, num_splits=S), S)[0] for w, S in plans)
     need_m = max(pkv.workspace_bytes(problem(w, num_splits=S), S)[1] for w, S in plans)
     o_part = torch.empty(need_o // 4, dtype=torch.float32, device="cuda:0")
@@ -351,7 +354,10 @@ def test_one_workspace_serves_calls_of_any_shape():
 
 
 def test_both_merge_paths_are_exercised():
+    """The shapes above cover both merge paths: in-kernel up to
+    PKV_MAX_FUSED_UNITS units, the combine kernel beyond."""
     shapes = [(dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 7),
-              (dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 64)]
+              (dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 64),
+              (dict(B=600, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 600), 2)]
     flags = [pkv.merges_in_kernel(problem(workloads.build("paths", seed=1, **kw), S), S) for kw, S in shapes]
-    assert flags == [True, False]
+    assert flags == [True, True, False]
