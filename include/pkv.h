@@ -37,8 +37,9 @@
  *  - Caller contract (not checkable without a device sync): block-table
  *    entries for the pages that hold keys j < kv_lens[b] are in
  *    [0, num_pages); 0 <= kv_lens[b] <= max_kv_len; causal_offsets[b] >= -1.
- *    Entries past ceil(kv_lens[b] / page_size) are never read, nor are page
- *    slots at or past kv_lens[b].
+ *    Entries past ceil(kv_lens[b] / page_size) may hold any value: they may
+ *    be read, but are never used to address memory.  Page slots at or past
+ *    kv_lens[b] are never read.
  */
 #ifndef PKV_H
 #define PKV_H
