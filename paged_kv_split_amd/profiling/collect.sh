@@ -1,7 +1,9 @@
 #!/bin/bash
 # Collect, for each bench.py workload named, a rocprofv3 kernel trace with
-# per-kernel statistics and two counter passes (FETCH_SIZE, then WRITE_SIZE),
-# plus the same two counters for a plain 1 GiB device copy (calibration).
+# per-kernel statistics and three counter passes (FETCH_SIZE; WRITE_SIZE;
+# matrix-core busy cycles and bf16 MFMA operations, LDS bank conflicts and LDS
+# activity, GPU active cycles), plus FETCH_SIZE and WRITE_SIZE for a plain
+# 1 GiB device copy (calibration).
 # usage: bash paged_kv_split_amd/profiling/collect.sh OUTDIR WORKLOAD...
 set -u
 cd "$(dirname "$0")/../.." || exit 1
@@ -34,6 +36,9 @@ for wl in "$@"; do
   step "${wl}_fetch" 120 rocprofv3 --pmc FETCH_SIZE -d "$out/${wl}_fetch" -o fetch --output-format csv -- \
     $BENCH --workload "$wl" --steps 4
   step "${wl}_write" 120 rocprofv3 --pmc WRITE_SIZE -d "$out/${wl}_write" -o write --output-format csv -- \
+    $BENCH --workload "$wl" --steps 4
+  step "${wl}_sq" 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT \
+    SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE MfmaUtil -d "$out/${wl}_sq" -o sq --output-format csv -- \
     $BENCH --workload "$wl" --steps 4
 done
 echo "collected in $out" >&2

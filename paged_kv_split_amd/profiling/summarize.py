@@ -6,7 +6,8 @@ For each workload it writes PROFILES_DIR/<kernel>_<workload>.md: the
 rocprofv3 per-kernel statistics of the library's kernels, the bench line's
 own HIP-event timing of the same kernel (the two must agree), and the HBM
 bytes per launch from the FETCH_SIZE and WRITE_SIZE counters, each scaled by
-what the counter reads for a plain 1 GiB device copy.  It also records those
+what the counter reads for a plain 1 GiB device copy, and (when collected)
+the matrix-core busy fraction, bf16 MFMA throughput and LDS bank conflicts.  It also records those
 bytes in PROFILES_DIR/traffic.json, keyed by the kernel-source digest, for
 bench.py's roofline.traffic field.
 """
@@ -19,6 +20,8 @@ import sys
 from . import source_digest
 
 COPY_BYTES = 1 << 30
+SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
 OURS = ("split_decode", "combine_kernel")
 
 
@@ -115,12 +118,44 @@ def summarize(out, profiles, wl, cal, command):
     fb, wb = per_kernel[_short(split["Name"])]
     lines += ["", f"Split kernel: {fb + wb:,.0f} HBM bytes per launch = {(fb + wb) / algo:.3f} x the "
               f"algorithmic bytes.", ""]
+    sq = None
+    sq_files = glob.glob(f"{out}/{wl}_sq/*counter_collection.csv")
+    if sq_files:
+        rows = _csv(f"{out}/{wl}_sq/*counter_collection.csv")
+        c = {n: counter_per_dispatch(rows, n) for n in
+             ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT",
+              "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE", "MfmaUtil")}
+        name = next((k for k in c["GRBM_GUI_ACTIVE"] if _short(k) == _short(split["Name"])), None)
+        if name is not None:
+            busy = c["SQ_VALU_MFMA_BUSY_CYCLES"].get(name, 0.0)
+            gui = c["GRBM_GUI_ACTIVE"][name]
+            mops = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"].get(name, 0.0)
+            conf = c["SQ_LDS_BANK_CONFLICT"].get(name, 0.0)
+            lds = c["SQ_LDS_IDX_ACTIVE"].get(name, 0.0)
+            # the per-dispatch GRBM_GUI_ACTIVE record is the sum over the XCDs' GRBM
+            # instances; busy cycles are summed over all SIMDs
+            util = 100.0 * busy / (gui / XCDS * SIMDS) if gui > 0 else 0.0
+            derived = c["MfmaUtil"].get(name)
+            tflops = mops * 512 / (prof_us * 1e-6) / 1e12
+            sq = {"mfma_busy_pct": round(util, 2), "mfma_util_derived_pct": derived, "mfma_bf16_tflops": round(tflops, 2),
+                  "lds_bank_conflict_pct": round(100.0 * conf / lds, 2) if lds > 0 else 0.0}
+            lines += ["## Matrix cores and LDS (SQ counters, per launch of the split kernel)", "",
+                      f"- MFMA busy: {util:.2f}% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / "
+                      f"(GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs))"
+                      + (f"; rocprofv3's derived MfmaUtil: {derived:.2f}%" if derived is not None else ""),
+                      f"- bf16 MFMA work: {mops * 512:,.0f} flop per launch = {tflops:.2f} TFLOP/s over the "
+                      f"rocprofv3 average duration (dense bf16 peak 2500 TFLOP/s)",
+                      f"- LDS bank conflicts: {conf:,.0f} cycles over {lds:,.0f} LDS-active cycles "
+                      f"({sq['lds_bank_conflict_pct']:.2f}%)", ""]
     path = os.path.join(profiles, f"{fam}_{wl}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
-    return {"kernel": _short(split["Name"]), "hbm_bytes_per_call": round(fb + wb),
-            "fetch_bytes": round(fb), "write_bytes": round(wb), "algorithmic_bytes": algo,
-            "rocprof_avg_us": round(prof_us, 3), "event_avg_us": ev_us}
+    rec = {"kernel": _short(split["Name"]), "hbm_bytes_per_call": round(fb + wb),
+           "fetch_bytes": round(fb), "write_bytes": round(wb), "algorithmic_bytes": algo,
+           "rocprof_avg_us": round(prof_us, 3), "event_avg_us": ev_us}
+    if sq:
+        rec.update(sq)
+    return rec
 
 
 def main():
