@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="decode_1b")
     ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--heads-per-block", type=int, default=0, help="kv heads per workgroup; 0 = library heuristic")
+    ap.add_argument("--kv-layout", default="paged", choices=["paged", "blhd", "bhld"],
+                    help="K/V in pages (pkv_paged_decode) or contiguous per sequence (pkv_contiguous_decode)")
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
@@ -176,20 +178,34 @@ def main():
     kl = t(w.kv_lens, torch.int32)
     co = None if w.causal_offsets is None else t(w.causal_offsets, torch.int32)
     mask = None if w.mask is None else t(w.mask, torch.float32)
-    pool_bytes = 2 * w.k_cache.nbytes
+    paged = args.kv_layout == "paged"
+    if paged:
+        kc, vc = w.k_cache, w.v_cache
+    else:
+        import workloads
+        kc, vc = workloads.to_contiguous(w, args.kv_layout)
+    cap = w.max_kv_len
+    pool_bytes = 2 * kc.nbytes
     n_rep = max(2, math.ceil(args.replica_bytes / max(pool_bytes, 1)))
-    kh = torch.from_numpy(w.k_cache.view(np.int16)).view(torch.bfloat16)
-    vh = torch.from_numpy(w.v_cache.view(np.int16)).view(torch.bfloat16)
+    kh = torch.from_numpy(kc.view(np.int16)).view(torch.bfloat16)
+    vh = torch.from_numpy(vc.view(np.int16)).view(torch.bfloat16)
     ks = [kh.to(dev) for _ in range(n_rep)]
     vs = [vh.to(dev) for _ in range(n_rep)]
-    del kh, vh
+    del kh, vh, kc, vc
 
     msb, msq = w.mask_strides
-    prob = pkv.make_problem(batch=w.B, q_len=w.q_len, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
-                            page_size=w.page_size, num_pages=w.num_pages,
-                            max_pages_per_seq=w.max_pages_per_seq, max_kv_len=w.max_kv_len,
-                            scale=w.scale, causal_offset=w.causal_offset, num_splits=args.splits,
-                            mask_stride_b=msb, mask_stride_q=msq, heads_per_block=args.heads_per_block)
+    if paged:
+        prob = pkv.make_problem(batch=w.B, q_len=w.q_len, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                                page_size=w.page_size, num_pages=w.num_pages,
+                                max_pages_per_seq=w.max_pages_per_seq, max_kv_len=w.max_kv_len,
+                                scale=w.scale, causal_offset=w.causal_offset, num_splits=args.splits,
+                                mask_stride_b=msb, mask_stride_q=msq, heads_per_block=args.heads_per_block)
+    else:
+        prob = pkv.contiguous_problem(batch=w.B, q_len=w.q_len, num_q_heads=w.Hq, num_kv_heads=w.Hkv,
+                                      head_dim=w.D, kv_capacity=cap, max_kv_len=w.max_kv_len, scale=w.scale,
+                                      causal_offset=w.causal_offset, num_splits=args.splits,
+                                      mask_stride_b=msb, mask_stride_q=msq,
+                                      heads_per_block=args.heads_per_block)
     plan = pkv.plan(prob)
     S = plan.splits
     prob.num_splits = S
@@ -206,10 +222,14 @@ def main():
     po, pm = P(o_part), P(ml_part)
 
     def step(r):
-        st = pkv.paged_decode_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3], base[4],
-                                  po, ob, pm, mb, P(out), 0, sh)
+        if paged:
+            st = pkv.paged_decode_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3], base[4],
+                                      po, ob, pm, mb, P(out), 0, sh)
+        else:
+            st = pkv.contiguous_decode_raw(prob, pkv.KV_LAYOUTS[args.kv_layout], cap, base[0], P(ks[r]), P(vs[r]),
+                                           base[2], base[3], base[4], po, ob, pm, mb, P(out), 0, sh)
         if st:
-            raise pkv.PkvError(st, "pkv_paged_decode")
+            raise pkv.PkvError(st, "pkv_paged_decode" if paged else "pkv_contiguous_decode")
 
     # warmup
     for i in range(args.warmup):
@@ -286,7 +306,9 @@ def main():
     # The dominant kernel's own average duration: the whole call when it is
     # one kernel; otherwise the split kernel alone (the same kernel, run
     # through pkv_paged_decode_partials), and the combine kernel alone.
-    n_kernels = plan.kernels
+    # Contiguous K/V has no partials entry point: a two-kernel call is timed
+    # whole there.
+    n_kernels = plan.kernels if paged else 1
     rows = w.B * w.q_len * w.Hq
     pob, pmb = pkv.partials_bytes(prob, S)
     po2 = torch.empty(max(pob // 4, 4), dtype=torch.float32, device=dev)
@@ -343,7 +365,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": describe(w, S, n_rep, plan.heads_per_block),
+        "config": dict(describe(w, S, n_rep, plan.heads_per_block), kv_layout=args.kv_layout),
         "us_per_call": round(us_call, 3),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "kernels_per_call": n_kernels,
@@ -355,7 +377,7 @@ def main():
         "kv_bytes_per_call": kv_bytes,
         "roofline": {"bound": "hbm", "kernel": kernel_name(w, S, prob), "achieved": round(kern_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name if paged else f"{w.name}:{args.kv_layout}")},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

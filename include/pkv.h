@@ -58,7 +58,7 @@ extern "C" {
 enum {
   PKV_OK = 0,
   PKV_ERR_NULL = 1,        /* a required pointer is NULL */
-  PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, Hkv % heads_per_block != 0, max_kv_len too big, bad stride */
+  PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, Hkv % heads_per_block != 0, Hkv * D > 2^24, max_kv_len too big, bad stride */
   PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS, heads_per_block not in {0, 1, 2, 4} */
   PKV_ERR_WORKSPACE = 4,   /* o_part / ml_part missing or smaller than pkv_workspace_bytes */
   PKV_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
@@ -174,6 +174,34 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                      const float *mask, float *o_part, size_t o_part_bytes,
                      float *ml_part, size_t ml_part_bytes, void *out_bf16,
                      float *out_f32, hipStream_t stream);
+
+/* K/V layouts of pkv_contiguous_decode, and the largest key capacity per
+ * sequence it takes. */
+#define PKV_KV_BLHD 1                    /* k_cache, v_cache bf16 [B, kv_capacity, Hkv, D] */
+#define PKV_KV_BHLD 2                    /* k_cache, v_cache bf16 [B, Hkv, kv_capacity, D] */
+#define PKV_MAX_CONTIGUOUS_KEYS (1 << 30)
+
+/* Decode attention over contiguous (non-paged) K/V: the same operation and
+ * kernels as pkv_paged_decode, with key j of sequence b at row j of sequence
+ * b's own region of the cache instead of a page-table lookup (AstrAI
+ * paged-decode commit notes: one set of decode kernels over a contiguous and
+ * a paged K/V addressing policy, and stride-based addressing with a
+ * "bhld"/"blhd" layout switch).
+ *   kv_layout    PKV_KV_BLHD or PKV_KV_BHLD (else PKV_ERR_UNSUPPORTED)
+ *   kv_capacity  keys per sequence in the cache, 1 .. PKV_MAX_CONTIGUOUS_KEYS
+ *                (else PKV_ERR_SHAPE); p->max_kv_len <= kv_capacity (0 means
+ *                kv_capacity)
+ *   k_cache, v_cache  bf16 in the chosen layout, contiguous, 16-byte aligned;
+ *                rows at or past kv_lens[b] are never read
+ * p->page_size, p->num_pages and p->max_pages_per_seq are ignored; every other
+ * field, argument, the workspace (pkv_workspace_bytes, pkv_plan with
+ * p->max_kv_len set) and the status codes are as for pkv_paged_decode. */
+int pkv_contiguous_decode(const pkv_problem *p, int kv_layout, int64_t kv_capacity,
+                          const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *kv_lens, const int32_t *causal_offsets,
+                          const float *mask, float *o_part, size_t o_part_bytes,
+                          float *ml_part, size_t ml_part_bytes, void *out_bf16,
+                          float *out_f32, hipStream_t stream);
 
 /* The split step alone: the same split kernel as pkv_paged_decode, always
  * writing the split partials and never launching the combine.  For callers

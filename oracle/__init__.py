@@ -129,6 +129,26 @@ def combine(o_part: np.ndarray, m_part: np.ndarray, l_part: np.ndarray) -> np.nd
     return out
 
 
+def decode_contiguous(w, k: np.ndarray, v: np.ndarray, layout: str = "blhd", threads: int = 0) -> np.ndarray:
+    """fp64 output for contiguous K/V (AstrAI paged-decode commit notes: a
+    contiguous and a paged K/V addressing policy for the same decode, and the
+    "bhld"/"blhd" layouts): key j of sequence b is row j of sequence b's
+    region, k / v [B, cap, Hkv, D] ("blhd") or [B, Hkv, cap, D] ("bhld").
+    That is the paged definition with one page of cap keys per sequence and
+    page b holding sequence b, which is how it is evaluated here; the other
+    fields of `w` (q, kv_lens, mask, causal offsets, scale) are used as given."""
+    if layout == "bhld":
+        k = k.transpose(0, 2, 1, 3)
+        v = v.transpose(0, 2, 1, 3)
+    elif layout != "blhd":
+        raise ValueError(layout)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    B, cap = k.shape[0], k.shape[1]
+    bt = np.arange(B, dtype=np.int32).reshape(B, 1)
+    return decode(w.replace(k_cache=k, v_cache=v, block_table=bt, page_size=cap), threads)
+
+
 def max_threads() -> int:
     return int(_load().pkv_oracle_max_threads())
 

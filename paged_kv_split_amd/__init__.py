@@ -27,9 +27,14 @@ PKV_ERR_DEVICE = 7
 PKV_MAX_SPLITS = 256
 PKV_COUNTER_BYTES = 16384
 PKV_MAX_FUSED_UNITS = PKV_COUNTER_BYTES // 4
+PKV_KV_BLHD = 1
+PKV_KV_BHLD = 2
+PKV_MAX_CONTIGUOUS_KEYS = 1 << 30
+KV_LAYOUTS = {"blhd": PKV_KV_BLHD, "bhld": PKV_KV_BHLD}
 
 EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
-            "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus", "pkv_status_string")
+            "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
+            "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -94,11 +99,14 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, P, P, P]
         L.pkv_paged_decode_partials.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                                 ctypes.c_size_t, P]
+        L.pkv_contiguous_decode.argtypes = [PP, ctypes.c_int, ctypes.c_int64, P, P, P, P, P, P, P,
+                                            ctypes.c_size_t, P, ctypes.c_size_t, P, P, P]
         L.pkv_combine.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         L.pkv_device_cus.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
         for name in ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+                     "pkv_contiguous_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -182,6 +190,16 @@ def paged_decode_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block
                                   block_table or None, kv_lens or None, causal_offsets or None,
                                   mask or None, o_part or None, o_part_bytes, ml_part or None,
                                   ml_part_bytes, out_bf16 or None, out_f32 or None, stream or None)
+
+
+def contiguous_decode_raw(problem: Problem, kv_layout: int, kv_capacity: int, q: int, k_cache: int, v_cache: int,
+                          kv_lens: int, causal_offsets: int, mask: int, o_part: int, o_part_bytes: int,
+                          ml_part: int, ml_part_bytes: int, out_bf16: int, out_f32: int, stream: int) -> int:
+    """pkv_contiguous_decode on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_contiguous_decode(ctypes.byref(problem), int(kv_layout), int(kv_capacity), q or None,
+                                       k_cache or None, v_cache or None, kv_lens or None, causal_offsets or None,
+                                       mask or None, o_part or None, o_part_bytes, ml_part or None,
+                                       ml_part_bytes, out_bf16 or None, out_f32 or None, stream or None)
 
 
 def paged_decode_partials_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block_table: int,
@@ -287,6 +305,70 @@ def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
                           _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
                           _ptr(out), _ptr(out_f32), _stream_handle(stream))
     _check(st, "pkv_paged_decode")
+    return out
+
+
+def contiguous_problem(*, batch: int, q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       kv_capacity: int, max_kv_len: int = 0, scale: float = 1.0, causal_offset: int = -1,
+                       num_splits: int = 0, mask_stride_b: int = 0, mask_stride_q: int = 0,
+                       heads_per_block: int = 0) -> Problem:
+    """The problem pkv_contiguous_decode plans with (its paged fields describe
+    one page of kv_capacity keys per sequence), so that ``plan``,
+    ``num_splits`` and ``workspace_bytes`` report what a contiguous call does."""
+    return make_problem(batch=batch, q_len=q_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, page_size=1, num_pages=0, max_pages_per_seq=kv_capacity,
+                        max_kv_len=max_kv_len if max_kv_len > 0 else kv_capacity, scale=scale,
+                        causal_offset=causal_offset, num_splits=num_splits, mask_stride_b=mask_stride_b,
+                        mask_stride_q=mask_stride_q, heads_per_block=heads_per_block)
+
+
+def contiguous_decode(q, k_cache, v_cache, kv_lens, *, layout: str = "blhd", scale: float,
+                      causal_offset: int = -1, causal_offsets=None, mask=None, num_splits: int = 0,
+                      max_kv_len: int = 0, heads_per_block: int = 0, out=None, out_f32=None, o_part=None,
+                      ml_part=None, stream=None):
+    """Decode over contiguous K/V on torch device tensors.  Returns ``out`` (bf16).
+
+    layout "blhd": k_cache, v_cache bf16 [B, kv_capacity, Hkv, D]; "bhld":
+    [B, Hkv, kv_capacity, D].  Other arguments as for ``paged_decode``.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(kv_lens, "kv_lens", torch.int32, 1)
+    if layout not in KV_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(KV_LAYOUTS)}")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, q_len, Hq, D = q.shape
+    if layout == "blhd":
+        Bk, cap, Hkv, Dk = k_cache.shape
+    else:
+        Bk, Hkv, cap, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError("k_cache does not match q in batch or head dim")
+    if causal_offsets is not None:
+        _require(causal_offsets, "causal_offsets", torch.int32, 1)
+    msb = msq = 0
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_cuda or mask.stride(-1) != 1:
+            raise ValueError("mask must be a device float32 tensor with a contiguous last dim")
+        msb = mask.stride(0)
+        msq = mask.stride(1) if mask.dim() == 3 else 0
+    p = contiguous_problem(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, kv_capacity=cap,
+                           max_kv_len=max_kv_len, scale=scale, causal_offset=causal_offset, num_splits=num_splits,
+                           mask_stride_b=msb, mask_stride_q=msq, heads_per_block=heads_per_block)
+    S = num_splits_for(p)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if S > 1 and (o_part is None or ml_part is None):
+        o_part, ml_part = alloc_workspace(p, S, q.device)
+    st = contiguous_decode_raw(p, KV_LAYOUTS[layout], cap, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+                               _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
+                               0 if o_part is None else o_part.numel() * o_part.element_size(),
+                               _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
+                               _ptr(out), _ptr(out_f32), _stream_handle(stream))
+    _check(st, "pkv_contiguous_decode")
     return out
 
 

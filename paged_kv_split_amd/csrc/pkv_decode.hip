@@ -190,14 +190,15 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
     // a tile past the window end (an unconditional prefetch) reads the last key's page
     const int bj = base < jlast ? base : jlast;
     const int page = __builtin_amdgcn_readfirstlane(c.bt[(bj >> c.page_shift) - c.p0]);
-    const int64_t pofs = (int64_t)page * c.page_stride;
+    // the tile's first key in the scalar offset; keys j of the tile are j - bj < T rows further
+    const int64_t pofs = (int64_t)page * c.page_stride + (int64_t)(bj & c.pmask) * c.row_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
 #pragma unroll
     for (int st = 0; st < Lay::NSTEP; ++st) {
       int j = base + st * Lay::KPV + c.kg;
       j = j < jlast ? j : jlast;
-      const uint32_t off = (uint32_t)((j & c.pmask) * c.row_stride);
+      const uint32_t off = (uint32_t)((j - bj) * c.row_stride);
       t.k[st] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + c.ds);
       t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + c.ds);
     }
@@ -454,8 +455,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   const bool direct = !a.partials || (a.fused && nact == 1);
 
   Ctx<D, RP> c;
-  c.kbase = a.k + g * D;
-  c.vbase = a.v + g * D;
+  c.kbase = a.k + g * a.head_stride;
+  c.vbase = a.v + g * a.head_stride;
   c.bt = reinterpret_cast<const int *>(smem);
   c.page_shift = a.page_shift;
   c.pmask = (1 << a.page_shift) - 1;
@@ -503,10 +504,13 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   // ---- key windows whose pages fit the LDS page-table slice (one window
   // unless the split spans more than kBtCap pages).  The first window's slice
   // does not depend on kv_lens, so its load is issued with the q load.
-  const int win_keys = (kBtCap << a.page_shift) >= NW * T ? ((kBtCap << a.page_shift) / (NW * T)) * (NW * T)
-                                                         : NW * T;
+  const int win_keys = window_keys(kBtCap, a.page_shift, NW * T);
   const int cap_keys = a.max_pages << a.page_shift;
   auto load_bt = [&](int from) {
+    if (a.contig) {  // contiguous K/V: sequence b is page b
+      if (threadIdx.x == 0) bt_lds[0] = b;
+      return;
+    }
     int to = from + win_keys;
     if (to > c.kb + a.chunk) to = c.kb + a.chunk;
     if (to > cap_keys) to = cap_keys;

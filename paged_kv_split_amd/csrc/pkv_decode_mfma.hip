@@ -95,14 +95,15 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
     // a tile past the window end (an unconditional prefetch) reads the last key's page
     const int bj = base < jlast ? base : jlast;
     const int page = __builtin_amdgcn_readfirstlane(c.bt[(bj >> c.page_shift) - c.p0]);
-    const int64_t pofs = (int64_t)page * c.page_stride;
+    // the tile's first key in the scalar offset; keys j of the tile are j - bj < T rows further
+    const int64_t pofs = (int64_t)page * c.page_stride + (int64_t)(bj & c.pmask) * c.row_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
 #pragma unroll
     for (int ii = 0; ii < L::NLD; ++ii) {
       int j = base + ii * L::RPI + lane / L::LPR;
       j = j < jlast ? j : jlast;
-      const uint32_t off = (uint32_t)((j & c.pmask) * c.row_stride);
+      const uint32_t off = (uint32_t)((j - bj) * c.row_stride);
       t.k[ii] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + ch);
       __builtin_amdgcn_sched_barrier(0);  // fixed issue order (see mtile_loop)
       t.v[ii] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + ch);
@@ -397,8 +398,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   uint16_t *vt = kt + L::TILE_ELEMS;
 
   MCtx c;
-  c.kbase = a.k + g * D;
-  c.vbase = a.v + g * D;
+  c.kbase = a.k + g * a.head_stride;
+  c.vbase = a.v + g * a.head_stride;
   c.bt = bt_lds;
   c.page_shift = a.page_shift;
   c.pmask = (1 << a.page_shift) - 1;
@@ -426,9 +427,13 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   }
 
   const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
-  const int win_keys = ((kBtCap << a.page_shift) / (NW * KT)) * (NW * KT);
+  const int win_keys = window_keys(kBtCap, a.page_shift, NW * KT);
   const int cap_keys = a.max_pages << a.page_shift;
   auto load_bt = [&](int from) {
+    if (a.contig) {  // contiguous K/V: sequence b is page b
+      if (threadIdx.x == 0) bt_lds[0] = b;
+      return;
+    }
     int to = from + win_keys;
     if (to > kb + a.chunk) to = kb + a.chunk;
     if (to > cap_keys) to = cap_keys;

@@ -136,6 +136,15 @@ __device__ __forceinline__ int active_splits(const DecodeArgs &a, int kmax) {
   return n < 1 ? 1 : (n > a.S ? a.S : n);
 }
 
+// Keys per page-table window: `cap` pages, a multiple of `step` keys, at
+// least `step` and at most 2^30 (contiguous K/V has one page of up to 2^30
+// keys per sequence).
+__device__ __forceinline__ int window_keys(int cap, int page_shift, int step) {
+  const int64_t w = ((int64_t)cap << page_shift) / step * step;
+  if (w < step) return step;
+  return w > ((int64_t)1 << 30) ? ((1 << 30) / step) * step : (int)w;
+}
+
 // Output row (b, i, h) of packed row rr (= i * G + k) of kv head g.
 __device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, int rr) {
   const int i = rr / a.G;

@@ -46,6 +46,8 @@ int check_problem(const pkv_problem *p) {
     return PKV_ERR_SHAPE;
   if (p->num_q_heads % p->num_kv_heads) return PKV_ERR_SHAPE;
   if (!supported_dim(p->head_dim)) return PKV_ERR_UNSUPPORTED;
+  // a key row of all kv heads (Hkv * D elements) times a tile of keys must fit 32 bits
+  if ((int64_t)p->num_kv_heads * p->head_dim > (1 << 24)) return PKV_ERR_SHAPE;
   if (!is_pow2(p->page_size) || p->page_size > 4096) return PKV_ERR_UNSUPPORTED;
   if (p->num_pages < 0 || p->max_pages_per_seq < 1) return PKV_ERR_SHAPE;
   if (p->max_kv_len < 0) return PKV_ERR_SHAPE;
@@ -297,15 +299,24 @@ namespace {
 // Checks and launch plan shared by pkv_paged_decode (partials_only = false)
 // and pkv_paged_decode_partials (true).  Returns a status; on PKV_OK `a`
 // holds the split-kernel arguments (a->S is the split count).
-int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const void *v_cache,
-                const int32_t *block_table, const int32_t *kv_lens, const int32_t *causal_offsets,
-                const float *mask, float *o_part, size_t o_part_bytes, float *ml_part,
-                size_t ml_part_bytes, void *out_bf16, float *out_f32, bool partials_only,
+// Where the keys live: paged (block table) or contiguous per sequence.
+struct KvSource {
+  const void *k, *v;
+  const int32_t *block_table;  // paged only
+  int layout;                  // 0 paged, PKV_KV_BLHD or PKV_KV_BHLD
+  int64_t capacity;            // contiguous: keys per sequence in the cache
+};
+
+int plan_decode(const pkv_problem *p, const void *q, const KvSource &src, const int32_t *kv_lens,
+                const int32_t *causal_offsets, const float *mask, float *o_part, size_t o_part_bytes,
+                float *ml_part, size_t ml_part_bytes, void *out_bf16, float *out_f32, bool partials_only,
                 pkv::DecodeArgs *a) {
-  if (!q || !k_cache || !v_cache || !block_table || !kv_lens) return PKV_ERR_NULL;
+  const bool paged = src.layout == 0;
+  const int32_t *block_table = src.block_table;
+  if (!q || !src.k || !src.v || (paged && !block_table) || !kv_lens) return PKV_ERR_NULL;
   if (!partials_only && !out_bf16) return PKV_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      (out_bf16 && !aligned(out_bf16, 16)) || !aligned(block_table, 4) || !aligned(kv_lens, 4) ||
+  if (!aligned(q, 16) || !aligned(src.k, 16) || !aligned(src.v, 16) ||
+      (out_bf16 && !aligned(out_bf16, 16)) || (paged && !aligned(block_table, 4)) || !aligned(kv_lens, 4) ||
       (causal_offsets && !aligned(causal_offsets, 4)) || (mask && !aligned(mask, 4)) ||
       (out_f32 && !aligned(out_f32, 16)))
     return PKV_ERR_ALIGN;
@@ -351,9 +362,9 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
 
   *a = pkv::DecodeArgs{};
   a->q = static_cast<const uint16_t *>(q);
-  a->k = static_cast<const uint16_t *>(k_cache);
-  a->v = static_cast<const uint16_t *>(v_cache);
-  a->block_table = block_table;
+  a->k = static_cast<const uint16_t *>(src.k);
+  a->v = static_cast<const uint16_t *>(src.v);
+  a->block_table = paged ? block_table : nullptr;
   a->kv_lens = kv_lens;
   a->causal_offsets = causal_offsets;
   a->mask = mask;
@@ -364,16 +375,26 @@ int plan_decode(const pkv_problem *p, const void *q, const void *k_cache, const 
   a->out_f32 = out_f32;
   a->mask_sb = p->mask_stride_b;
   a->mask_sq = p->mask_stride_q;
-  a->page_stride = (int64_t)p->page_size * p->num_kv_heads * p->head_dim;
-  a->row_stride = p->num_kv_heads * p->head_dim;
+  if (paged) {
+    a->page_stride = (int64_t)p->page_size * p->num_kv_heads * p->head_dim;
+    a->row_stride = p->num_kv_heads * p->head_dim;
+    a->head_stride = p->head_dim;
+    a->page_shift = ilog2(p->page_size);
+    a->max_pages = p->max_pages_per_seq;
+  } else {  // one page of 2^30 key slots per sequence, addressed with the cache's strides
+    a->page_stride = src.capacity * p->num_kv_heads * p->head_dim;
+    a->row_stride = src.layout == PKV_KV_BLHD ? p->num_kv_heads * p->head_dim : p->head_dim;
+    a->head_stride = src.layout == PKV_KV_BLHD ? (int64_t)p->head_dim : src.capacity * p->head_dim;
+    a->page_shift = 30;
+    a->max_pages = 1;
+    a->contig = 1;
+  }
   a->B = p->batch;
   a->q_len = p->q_len;
   a->Hq = p->num_q_heads;
   a->Hkv = p->num_kv_heads;
   a->G = G;
   a->R = R;
-  a->page_shift = ilog2(p->page_size);
-  a->max_pages = p->max_pages_per_seq;
   a->S = S;
   a->chunk = (int32_t)chunk;
   a->nrb = (R + rp - 1) / rp;
@@ -405,24 +426,11 @@ int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stre
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
-                     const void *v_cache, const int32_t *block_table,
-                     const int32_t *kv_lens, const int32_t *causal_offsets,
-                     const float *mask, float *o_part, size_t o_part_bytes,
-                     float *ml_part, size_t ml_part_bytes, void *out_bf16,
-                     float *out_f32, hipStream_t stream) {
-  int rc = check_problem(p);
-  if (rc) return rc;
-  if (p->batch == 0) return PKV_OK;
-  pkv::DecodeArgs a;
-  rc = plan_decode(p, q, k_cache, v_cache, block_table, kv_lens, causal_offsets, mask, o_part,
-                   o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
-  if (rc) return rc;
-  rc = launch_plan(a, p, stream);
+// The split kernel, then (several splits without the in-kernel merge) the
+// combine kernel.
+int launch_all(const pkv::DecodeArgs &a, const pkv_problem *p, float *o_part, void *out_bf16, float *out_f32,
+               hipStream_t stream) {
+  int rc = launch_plan(a, p, stream);
   if (rc) return rc;
   if (a.S > 1 && !a.fused) {
     pkv::CombineArgs c = {};
@@ -437,6 +445,53 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
   return PKV_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
+                     const void *v_cache, const int32_t *block_table,
+                     const int32_t *kv_lens, const int32_t *causal_offsets,
+                     const float *mask, float *o_part, size_t o_part_bytes,
+                     float *ml_part, size_t ml_part_bytes, void *out_bf16,
+                     float *out_f32, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->batch == 0) return PKV_OK;
+  pkv::DecodeArgs a;
+  rc = plan_decode(p, q, KvSource{k_cache, v_cache, block_table, 0, 0}, kv_lens, causal_offsets, mask, o_part,
+                   o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
+  if (rc) return rc;
+  return launch_all(a, p, o_part, out_bf16, out_f32, stream);
+}
+
+int pkv_contiguous_decode(const pkv_problem *p, int kv_layout, int64_t kv_capacity, const void *q,
+                          const void *k_cache, const void *v_cache, const int32_t *kv_lens,
+                          const int32_t *causal_offsets, const float *mask, float *o_part,
+                          size_t o_part_bytes, float *ml_part, size_t ml_part_bytes, void *out_bf16,
+                          float *out_f32, hipStream_t stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (kv_layout != PKV_KV_BLHD && kv_layout != PKV_KV_BHLD) return PKV_ERR_UNSUPPORTED;
+  if (kv_capacity < 1 || kv_capacity > PKV_MAX_CONTIGUOUS_KEYS) return PKV_ERR_SHAPE;
+  // the paged fields do not apply: check the rest as a problem whose single
+  // page per sequence holds kv_capacity keys
+  pkv_problem pc = *p;
+  pc.page_size = 1;
+  pc.num_pages = 0;
+  pc.max_pages_per_seq = (int32_t)kv_capacity;
+  int rc = check_problem(&pc);
+  if (rc) return rc;
+  if (pc.batch == 0) return PKV_OK;
+  if (pc.max_kv_len == 0) pc.max_kv_len = (int32_t)kv_capacity;
+  // K/V element offsets must fit the 64-bit arithmetic of the kernels
+  if ((double)pc.batch * (double)kv_capacity * pc.num_kv_heads * pc.head_dim > 9.0e18) return PKV_ERR_SHAPE;
+  pkv::DecodeArgs a;
+  rc = plan_decode(&pc, q, KvSource{k_cache, v_cache, nullptr, kv_layout, kv_capacity}, kv_lens, causal_offsets,
+                   mask, o_part, o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
+  if (rc) return rc;
+  return launch_all(a, &pc, o_part, out_bf16, out_f32, stream);
+}
+
 int pkv_paged_decode_partials(const pkv_problem *p, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *block_table,
                               const int32_t *kv_lens, const int32_t *causal_offsets,
@@ -446,7 +501,7 @@ int pkv_paged_decode_partials(const pkv_problem *p, const void *q, const void *k
   if (rc) return rc;
   if (p->batch == 0) return PKV_OK;
   pkv::DecodeArgs a;
-  rc = plan_decode(p, q, k_cache, v_cache, block_table, kv_lens, causal_offsets, mask, o_part,
+  rc = plan_decode(p, q, KvSource{k_cache, v_cache, block_table, 0, 0}, kv_lens, causal_offsets, mask, o_part,
                    o_part_bytes, ml_part, ml_part_bytes, nullptr, nullptr, true, &a);
   if (rc) return rc;
   return launch_plan(a, p, stream);

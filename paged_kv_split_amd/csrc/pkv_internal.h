@@ -22,10 +22,12 @@ struct DecodeArgs {
   uint16_t *out;                  // bf16 [rows, D] (S == 1)
   float *out_f32;                 // nullable       (S == 1)
   int64_t mask_sb, mask_sq;
-  int64_t page_stride;            // elements per physical page: P * Hkv * D
-  int32_t row_stride;             // elements per page slot: Hkv * D
+  int64_t page_stride;            // elements per physical page: P * Hkv * D (contiguous K/V: one sequence)
+  int64_t head_stride;            // elements between kv heads: D (paged, blhd) or capacity * D (bhld)
+  int32_t row_stride;             // elements between consecutive keys: Hkv * D (paged, blhd) or D (bhld)
+  int32_t contig;                 // 1: contiguous K/V, sequence b is page b (no block table)
   int32_t B, q_len, Hq, Hkv, G, R;  // R = G * q_len rows per kv head
-  int32_t page_shift;             // log2(page_size)
+  int32_t page_shift;             // log2(page_size); 30 for contiguous K/V
   int32_t max_pages;              // block_table row stride
   int32_t S;                      // splits
   int32_t chunk;                  // keys per split (multiple of the tile)

@@ -60,6 +60,25 @@ def run(w, d=None, num_splits=0, stream=None, sync=True, heads_per_block=0):
     return out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy()
 
 
+def run_contiguous(w, layout, num_splits=0, heads_per_block=0, capacity=None, sync=True):
+    """pkv_contiguous_decode on the workload's keys laid out contiguously
+    (workloads.to_contiguous); returns (out_bf16 bits, out_f32, k, v) with the
+    host K/V arrays used."""
+    k, v = __import__("workloads").to_contiguous(w, layout, capacity)
+    d = dev_tensors(w)
+    dev = d["q"].device
+    kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).to(dev)
+    vt = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+    out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device=dev)
+    out = pkv.contiguous_decode(d["q"], kt, vt, d["kl"], layout=layout, scale=w.scale,
+                                causal_offset=w.causal_offset, causal_offsets=d["co"], mask=d["mask"],
+                                num_splits=num_splits, max_kv_len=w.max_kv_len,
+                                heads_per_block=heads_per_block, out_f32=out32)
+    if sync:
+        torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), k, v
+
+
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

@@ -282,3 +282,42 @@ def test_grid_beyond_32bit_work_items_is_rejected():
     # 2^23 sequences x 2 kv heads = 2^24 workgroups of 256 threads: 2^32 work-items
     assert call(base_problem(batch=1 << 23, num_splits=1, heads_per_block=1)) == pkv.PKV_ERR_SHAPE
     assert pkv.combine_raw((1 << 25) * 2 + 8, 2, 64, FAKE, FAKE, FAKE, 0, 0) == pkv.PKV_ERR_SHAPE
+
+
+def ccall(p, layout=pkv.PKV_KV_BLHD, capacity=128, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kl=FAKE, co=0, mask=0, o=0, ob=0, ml=0, mb=0, out=FAKE, out32=0)
+    a.update(ptrs)
+    return pkv.contiguous_decode_raw(p, layout, capacity, a["q"], a["k"], a["v"], a["kl"], a["co"], a["mask"],
+                                     a["o"], a["ob"], a["ml"], a["mb"], a["out"], a["out32"], 0)
+
+
+def test_contiguous_decode_checks():
+    p = base_problem(num_splits=1, heads_per_block=1, max_kv_len=100)
+    assert ccall(p, layout=0) == pkv.PKV_ERR_UNSUPPORTED
+    assert ccall(p, layout=3) == pkv.PKV_ERR_UNSUPPORTED
+    assert ccall(p, capacity=0) == pkv.PKV_ERR_SHAPE
+    assert ccall(p, capacity=pkv.PKV_MAX_CONTIGUOUS_KEYS + 1) == pkv.PKV_ERR_SHAPE
+    assert ccall(p, capacity=99) == pkv.PKV_ERR_SHAPE                     # max_kv_len > capacity
+    for which in ("q", "k", "v", "kl", "out"):
+        assert ccall(p, **{which: 0}) == pkv.PKV_ERR_NULL
+    assert ccall(p, k=FAKE + 2) == pkv.PKV_ERR_ALIGN
+    assert ccall(base_problem(batch=0)) == pkv.PKV_OK
+    # the paged fields are ignored: a page size that pkv_paged_decode rejects is fine here
+    odd = base_problem(num_splits=1, heads_per_block=1, page_size=48, num_pages=-1, max_kv_len=100)
+    assert ccall(odd) == pkv.PKV_ERR_LAUNCH                              # passes every host check
+    assert ccall(p, layout=pkv.PKV_KV_BHLD) == pkv.PKV_ERR_LAUNCH
+    # several splits need the workspace, as for the paged entry point
+    ps = base_problem(num_splits=4, heads_per_block=1, max_kv_len=100)
+    assert ccall(ps) == pkv.PKV_ERR_WORKSPACE
+
+
+def test_contiguous_problem_plans_like_the_entry_point():
+    cp = pkv.contiguous_problem(batch=16, q_len=1, num_q_heads=8, num_kv_heads=8, head_dim=64, kv_capacity=4096)
+    info = pkv.plan(cp, 256)
+    assert (info.splits, info.heads_per_block) == (8, 4)
+    assert pkv.workspace_bytes(cp, 8)[0] == 16 * 8 * 8 * 64 * 4
+
+
+def test_kv_row_too_wide_is_rejected():
+    assert call(base_problem(num_splits=1, num_q_heads=1 << 17, num_kv_heads=1 << 17, head_dim=256)) == \
+        pkv.PKV_ERR_SHAPE

@@ -294,3 +294,38 @@ def test_workload_shapes_and_page_tables():
     assert r.num_pages == int(((r.kv_lens + 31) // 32).sum())
     s = workloads.sweep(32, 64, B=2, L=256)
     assert s.mask.shape == (2, 256) and 0.02 < np.isinf(s.mask).mean() < 0.25
+
+
+@pytest.mark.parametrize("i", range(len(BRUTE)))
+def test_contiguous_kv_matches_bruteforce_and_paged(i):
+    """Contiguous K/V (both layouts, a capacity beyond the longest sequence
+    whose extra rows are NaN): the same values as the brute-force path over
+    the paged copy, and the same bits as the paged oracle."""
+    w = small(200 + i, **dict(BRUTE[i]))
+    paged = oracle.decode(w)
+    brute = oracle.bruteforce_decode(w)
+    for layout in ("blhd", "bhld"):
+        k, v = workloads.to_contiguous(w, layout, capacity=max(1, w.max_kv_len) + 5)
+        got = oracle.decode_contiguous(w, k, v, layout)
+        assert np.isfinite(got).all()
+        assert np.array_equal(got, paged)
+        np.testing.assert_allclose(got, brute, rtol=0, atol=1e-12)
+
+
+def test_contiguous_layouts_place_keys_as_documented():
+    """to_contiguous puts key j of sequence b, kv head g at [b, j, g] (blhd)
+    and [b, g, j] (bhld), and NaN past kv_lens[b]."""
+    w = small(300, lens=[5, 0, 17], Hkv=2, Hq=4)
+    kb, vb = workloads.to_contiguous(w, "blhd", capacity=20)
+    kh, vh = workloads.to_contiguous(w, "bhld", capacity=20)
+    P = w.page_size
+    for b in range(w.B):
+        L = int(w.kv_lens[b])
+        for j in range(20):
+            for g in range(w.Hkv):
+                if j < L:
+                    pg = int(w.block_table[b, j // P])
+                    assert np.array_equal(kb[b, j, g], w.k_cache[pg, j % P, g])
+                    assert np.array_equal(vh[b, g, j], w.v_cache[pg, j % P, g])
+                else:
+                    assert (kb[b, j, g] == workloads.BF16_NAN).all() and (vh[b, g, j] == workloads.BF16_NAN).all()

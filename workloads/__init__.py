@@ -82,6 +82,31 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
+def to_contiguous(w: Workload, layout: str = "blhd", capacity: Optional[int] = None):
+    """The workload's K/V as contiguous caches (no page table): key j of
+    sequence b at row j of sequence b's region.  layout "blhd": [B, capacity,
+    Hkv, D]; "bhld": [B, Hkv, capacity, D].  capacity defaults to the longest
+    sequence; rows at or past kv_lens[b] hold bf16 NaN (never to be read).
+    Returns (k, v) as uint16 bf16 bits."""
+    cap = int(capacity) if capacity is not None else max(1, w.max_kv_len)
+    P = w.page_size
+    k = np.full((w.B, cap, w.Hkv, w.D), BF16_NAN, dtype=np.uint16)
+    v = np.full((w.B, cap, w.Hkv, w.D), BF16_NAN, dtype=np.uint16)
+    for b in range(w.B):
+        L = int(w.kv_lens[b])
+        for j0 in range(0, L, P):
+            n = min(P, L - j0)
+            pg = int(w.block_table[b, j0 // P])
+            k[b, j0:j0 + n] = w.k_cache[pg, :n]
+            v[b, j0:j0 + n] = w.v_cache[pg, :n]
+    if layout == "bhld":
+        k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+        v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    elif layout != "blhd":
+        raise ValueError(layout)
+    return k, v
+
+
 def _bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
