@@ -123,8 +123,8 @@ struct Layout {
   static constexpr int SW_SHIFT = LPK >= 4 ? 0 : (LPK == 2 ? 1 : 2);
   static constexpr int SW_MASK = LPK >= 8 ? 1 : 3;
   __device__ static int kslot(int ch, int row) { return ch ^ (SW_MUL * ((row >> SW_SHIFT) & SW_MASK)); }
-  // merge phase: per-wave O rows, per-wave (m, l), per-row (M, W), wave factors
-  static constexpr int MERGE = NW * RP * D + NW * RP * 2 + RP * kMaxHeadsPerBlock * 2 + NW * RP;
+  // merge phase: per-wave O rows and (m, l)
+  static constexpr int MERGE = NW * RP * D + NW * RP * 2;
   static constexpr int MAIN = kBtCap + 4 + PBUF + KBUF;  // page-table slice (+1 page when a window
                                                          // starts mid-page), p and K slices
   static constexpr int SMEM = MAIN > MERGE ? MAIN : MERGE;
@@ -568,39 +568,14 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
       const int u = wk * HR + r * a.hpb + hw;
-      mlb[u * 2] = st.m[r];
-      mlb[u * 2 + 1] = l_tot[r];
+      *reinterpret_cast<float2 *>(mlb + u * 2) = make_float2(st.m[r], l_tot[r]);
     }
   }
-  float *rmw = mlb + NW * RP * 2;                  // [RP * hpb][2]: merged (M, W) per row
-  float *fw = rmw + RP * kMaxHeadsPerBlock * 2;    // [NW * RP]: normalised wave factors
   __syncthreads();
-  if (threadIdx.x < nrows) {
-    const int ri = threadIdx.x;
-    float mw[NW], lw[NW], f[NW], M, W;
-#pragma unroll
-    for (int kk = 0; kk < NW; ++kk) {
-      mw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2] : -INFINITY;
-      lw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2 + 1] : 0.f;
-    }
-    wave_factors<NW>(mw, lw, M, W, f);
-    rmw[2 * ri] = M;
-    rmw[2 * ri + 1] = W;
-#pragma unroll
-    for (int kk = 0; kk < NW; ++kk)
-      if (kk < wph) fw[kk * HR + ri] = f[kk];
-  }
-  __syncthreads();
-  auto Mrow = [&](int ri) { return rmw[2 * ri]; };
-  auto Wrow = [&](int ri) { return rmw[2 * ri + 1]; };
-  auto resn = [&](int ri, int d) {
-    float o = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NW; ++kk)
-      if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * D + d], o);
-    return o;
+  auto item = [&](int ri, int d, float &M, float &W, float &vx, float &vy) {
+    merge_waves<NW, D>(mlb, ob, HR, wph, ri, d, M, W, vx, vy);
   };
-  write_rows<D>(a, s, direct, rowtab, nrows, resn, Mrow, Wrow, NW * 64);
+  write_rows<D>(a, s, direct, rowtab, nrows, item, NW * 64);
   if (a.fused && !direct) fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrows, smem, NW * 64);
 }
 

@@ -56,9 +56,8 @@ struct MLay {
   static constexpr int WAVE_LDS = 2 * TILE_ELEMS * 2 + MASK_BYTES;  // bytes: K + V tile, mask
   static constexpr int BT_BYTES = (kBtCap + 4) * 4;
   static constexpr int OB_STRIDE = D + 4;    // merge-buffer row stride (floats), padded against bank conflicts
-  // merge phase: per-wave O rows, per-wave (m, l), per-row (M, W), wave factors
-  static constexpr int MERGE_BYTES =
-      NW * 16 * OB_STRIDE * 4 + NW * 16 * 2 * 4 + 16 * kMaxHeadsPerBlock * 2 * 4 + NW * 16 * 4;
+  // merge phase: per-wave O rows and (m, l)
+  static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 16 * 2 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
   static constexpr int SMEM_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   // swizzles (16-byte chunk index within a row)
@@ -481,8 +480,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   const int HR = 16 * a.hpb;
   float *ob = reinterpret_cast<float *>(smem_raw);        // [NW * 16][OB_STRIDE]
   float *mlb = ob + NW * 16 * L::OB_STRIDE;               // [NW * 16][2]
-  float *rmw = mlb + NW * 16 * 2;                         // [16 * hpb][2]: merged (M, W) per row
-  float *fw = rmw + 16 * kMaxHeadsPerBlock * 2;           // [NW * 16]: normalised wave factors
   const int u = wk * HR + cc * a.hpb + hw;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -493,39 +490,14 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
       float4 *dst = reinterpret_cast<float4 *>(ob + u * L::OB_STRIDE + 16 * nb + 4 * q);
       dst[0] = make_float4(st.o[rb][nb][0], st.o[rb][nb][1], st.o[rb][nb][2], st.o[rb][nb][3]);
     }
-    if (q == 0) {
-      mlb[u * 2] = st.m[rb];
-      mlb[u * 2 + 1] = ltot[rb];
-    }
+    if (q == 0) *reinterpret_cast<float2 *>(mlb + u * 2) = make_float2(st.m[rb], ltot[rb]);
     const int rs = r0 + 16 * rb;
     const int nrows = (a.R - rs < 16 ? a.R - rs : 16) * a.hpb;
     __syncthreads();
-    if (threadIdx.x < nrows) {
-      const int ri = threadIdx.x;
-      float mw[NW], lw[NW], f[NW], M, W;
-#pragma unroll
-      for (int kk = 0; kk < NW; ++kk) {
-        mw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2] : -INFINITY;
-        lw[kk] = kk < wph ? mlb[(kk * HR + ri) * 2 + 1] : 0.f;
-      }
-      wave_factors<NW>(mw, lw, M, W, f);
-      rmw[2 * ri] = M;
-      rmw[2 * ri + 1] = W;
-#pragma unroll
-      for (int kk = 0; kk < NW; ++kk)
-        if (kk < wph) fw[kk * HR + ri] = f[kk];
-    }
-    __syncthreads();
-    auto Mrow = [&](int ri) { return rmw[2 * ri]; };
-    auto Wrow = [&](int ri) { return rmw[2 * ri + 1]; };
-    auto resn = [&](int ri, int d) {
-      float o = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NW; ++kk)
-        if (kk < wph) o = fmaf(fw[kk * HR + ri], ob[(kk * HR + ri) * L::OB_STRIDE + d], o);
-      return o;
+    auto item = [&](int ri, int d, float &M, float &W, float &vx, float &vy) {
+      merge_waves<NW, L::OB_STRIDE>(mlb, ob, HR, wph, ri, d, M, W, vx, vy);
     };
-    write_rows<D>(a, s, direct, rowtab + 16 * rb * a.hpb, nrows, resn, Mrow, Wrow, NW * 64);
+    write_rows<D>(a, s, direct, rowtab + 16 * rb * a.hpb, nrows, item, NW * 64);
   }
   if (a.fused && !direct)
     fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);

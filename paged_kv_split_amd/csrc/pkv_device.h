@@ -287,37 +287,37 @@ __device__ __forceinline__ void empty_partials(const DecodeArgs &a, int b, int h
   }
 }
 
-// Epilogue shared by the split kernels once a block has merged its waves for
-// its nrows output rows: `rowtab[r]` is the output row of block row r,
-// `resn(r, d)` the normalised result (0 when the row saw no key), `Mrow(r)`
-// the base-2 reference max and `Wrow(r)` the total weight.  `direct`: write
-// the output (the unit's only split with keys).  Otherwise write this split's
-// partial (o = resn, m in natural-log units, l = W); an empty split (W = 0)
-// writes only (m, l) = (-inf, 0).
-template <int D, class ResF, class MF, class WF>
-__device__ void write_rows(const DecodeArgs &a, int s, bool direct, const int64_t *rowtab, int nrows, ResF resn,
-                           MF Mrow, WF Wrow, int nthreads) {
+// Epilogue shared by the split kernels once a block's waves have left their
+// results in LDS, for its nrows output rows: `rowtab[r]` is the output row of
+// block row r; `item(r, d, M, W, vx, vy)` gives the row's base-2 reference
+// max M, its total weight W and the normalised results at columns d, d + 1
+// (0 when the row saw no key).  `direct`: write the output (the unit's only
+// split with keys).  Otherwise write this split's partial (o, m in
+// natural-log units, l = W); an empty split (W = 0) writes only
+// (m, l) = (-inf, 0).
+template <int D, class ItemF>
+__device__ void write_rows(const DecodeArgs &a, int s, bool direct, const int64_t *rowtab, int nrows, ItemF item,
+                           int nthreads) {
   constexpr int DP = D / 2;
   for (int idx = threadIdx.x; idx < nrows * DP; idx += nthreads) {
     const int r = idx / DP;
     const int d = 2 * (idx - r * DP);
     const int64_t row = rowtab[r];
-    const float W = Wrow(r);
+    float M, W, vx, vy;
+    item(r, d, M, W, vx, vy);
     if (direct) {
-      const float vx = resn(r, d);
-      const float vy = resn(r, d + 1);
       *reinterpret_cast<uint32_t *>(a.out + row * D + d) =
           (uint32_t)f32_to_bf16_rne(vx) | ((uint32_t)f32_to_bf16_rne(vy) << 16);
       if (a.out_f32) *reinterpret_cast<float2 *>(a.out_f32 + row * D + d) = make_float2(vx, vy);
     } else {
       float *po = a.o_part + (row * a.S + s) * D + d;
       float *pm = a.ml_part + (row * a.S + s) * 2;
-      const float mx = W > 0.f ? Mrow(r) * kLn2 : -INFINITY;
+      const float mx = W > 0.f ? M * kLn2 : -INFINITY;
       if (a.fused) {  // merged by another workgroup of this launch
-        if (W > 0.f) store_dev2(po, resn(r, d), resn(r, d + 1));
+        if (W > 0.f) store_dev2(po, vx, vy);
         if (d == 0) store_dev2(pm, mx, W);
       } else {        // read after this kernel has ended
-        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(resn(r, d), resn(r, d + 1));
+        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(vx, vy);
         if (d == 0) *reinterpret_cast<float2 *>(pm) = make_float2(mx, W);
       }
     }
@@ -343,6 +343,34 @@ __device__ __forceinline__ void wave_factors(const float (&m)[NW], const float (
   const float inv = W > 0.f ? 1.f / W : 0.f;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) f[ww] *= inv;
+}
+
+// The merged result of block row ri at columns d, d + 1 from the per-wave
+// results in LDS: wave slot kk*HR + ri holds wave kk's (m, l) in mlb and its
+// unnormalised O row in ob (row stride OBS floats); waves kk >= wph hold no
+// row of this head.  All loads are issued together, from clamped slots, and
+// unused waves are masked after loading, so no branch separates them.
+template <int NW, int OBS>
+__device__ __forceinline__ void merge_waves(const float *mlb, const float *ob, int HR, int wph, int ri, int d,
+                                            float &M, float &W, float &vx, float &vy) {
+  float mw[NW], lw[NW], f[NW];
+  float2 o[NW];
+#pragma unroll
+  for (int kk = 0; kk < NW; ++kk) {
+    const int slot = (kk < wph ? kk : wph - 1) * HR + ri;
+    const float2 ml = *reinterpret_cast<const float2 *>(mlb + 2 * slot);
+    o[kk] = *reinterpret_cast<const float2 *>(ob + slot * OBS + d);
+    mw[kk] = kk < wph ? ml.x : -INFINITY;
+    lw[kk] = kk < wph ? ml.y : 0.f;
+  }
+  wave_factors<NW>(mw, lw, M, W, f);
+  vx = 0.f;
+  vy = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NW; ++kk) {
+    vx = fmaf(f[kk], o[kk].x, vx);   // f = 0 for unused waves (their loads are finite rows of wave wph - 1)
+    vy = fmaf(f[kk], o[kk].y, vy);
+  }
 }
 
 // With a.fused (several splits, one call): each of the unit's n active
