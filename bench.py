@@ -6,7 +6,8 @@ merges the splits for small grids, or the split kernel then the combine
 kernel) over one batch of synthetic, seeded input that is already resident in
 HBM.  The default workload is the 1B-model decode shape (B=8, Hq=24, Hkv=4,
 D=64, page 32, kv_lens uniform on [128, 2048]); ``--workload`` selects the
-other decode shapes.
+other decode shapes, and ``mixed`` a batch of chunked-prefill and decode
+sequences with different query-token counts (pkv_paged_decode_varlen).
 
 Protocol: W untimed warmup steps; then K timed eager steps back to back on
 one stream, bracketed by two HIP events (median of --runs repetitions), each
@@ -64,12 +65,13 @@ def algorithmic_bytes(w) -> int:
     the pages in use and, when present, the mask entries of those keys."""
     import numpy as np
     L = w.kv_lens.astype(np.int64)
+    n = w.q_lens.astype(np.int64) if w.q_lens is not None else np.full(w.B, w.q_len, dtype=np.int64)
     kv = int(L.sum()) * w.Hkv * w.D * 2 * 2
-    qo = w.B * w.q_len * w.Hq * w.D * 2 * 2
+    qo = w.total_tokens * w.Hq * w.D * 2 * 2
     bt = int(((L + w.page_size - 1) // w.page_size).sum()) * 4
     mask = 0
     if w.mask is not None:
-        mask = int(L.sum()) * 4 * (w.q_len if w.mask.ndim == 3 else 1)
+        mask = int((L * (n if w.mask.ndim == 3 else 1)).sum()) * 4
     return kv + qo + bt + mask
 
 
@@ -85,10 +87,14 @@ def make_workload(name: str):
 
 def describe(w, splits, replicas, heads_per_block):
     L = w.kv_lens
-    return {"workload": w.name, "B": w.B, "q_len": w.q_len, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+    extra = {}
+    if w.q_lens is not None:
+        extra = {"q_tokens": w.total_tokens, "prefill_seqs": int((w.q_lens > 1).sum()),
+                 "causal_last": w.causal_offset == -2}
+    return {"workload": w.name, "B": w.B, "q_len": w.q_len, **extra, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "page_size": w.page_size, "kv_len_min": int(L.min()), "kv_len_max": int(L.max()),
             "kv_len_mean": round(float(L.mean()), 1), "mask": None if w.mask is None else list(w.mask.shape),
-            "causal": w.causal_offsets is not None or w.causal_offset >= 0, "splits": splits,
+            "causal": w.causal_offsets is not None or w.causal_offset != -1, "splits": splits,
             "heads_per_block": heads_per_block,
             "replicas": replicas, "seed": w.seed}
 
@@ -102,12 +108,14 @@ def cpu_baseline(w, budget_s: float):
     def head(n):
         return w.replace(B=n, q=w.q[:n], block_table=w.block_table[:n], kv_lens=w.kv_lens[:n],
                          causal_offsets=None if w.causal_offsets is None else w.causal_offsets[:n],
-                         mask=None if w.mask is None else w.mask[:n])
+                         mask=None if w.mask is None else w.mask[:n],
+                         q_lens=None if w.q_lens is None else w.q_lens[:n])
 
+    run = oracle.decode_varlen if w.q_lens is not None or w.causal_offset < -1 else oracle.decode
     threads = oracle.max_threads()
     probe = head(1)
     t0 = time.perf_counter()
-    oracle.decode(probe)
+    run(probe)
     sec_per_byte = max(time.perf_counter() - t0, 1e-5) / max(probe.kv_bytes(), 1)
     n = 1
     while n < w.B and head(n + 1).kv_bytes() * sec_per_byte * 3 <= budget_s:
@@ -116,7 +124,7 @@ def cpu_baseline(w, budget_s: float):
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        oracle.decode(sub)
+        run(sub)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": round(sub.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -173,7 +181,15 @@ def main():
     def t(a, dtype):
         return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).to(dev)
 
-    q = t(w.q.view(np.int16), torch.bfloat16)
+    varlen = w.q_lens is not None
+    if varlen:
+        qp, cu = w.packed_q()
+        q = t(qp.view(np.int16), torch.bfloat16)
+        cu_t = t(cu, torch.int32)
+        if args.kv_layout != "paged":
+            raise SystemExit("varlen batches are paged only")
+    else:
+        q = t(w.q.view(np.int16), torch.bfloat16)
     bt = t(w.block_table, torch.int32)
     kl = t(w.kv_lens, torch.int32)
     co = None if w.causal_offsets is None else t(w.causal_offsets, torch.int32)
@@ -222,7 +238,10 @@ def main():
     po, pm = P(o_part), P(ml_part)
 
     def step(r):
-        if paged:
+        if varlen:
+            st = pkv.paged_decode_varlen_raw(prob, P(cu_t), w.total_tokens, base[0], P(ks[r]), P(vs[r]), base[1],
+                                             base[2], base[3], base[4], po, ob, pm, mb, P(out), 0, sh)
+        elif paged:
             st = pkv.paged_decode_raw(prob, base[0], P(ks[r]), P(vs[r]), base[1], base[2], base[3], base[4],
                                       po, ob, pm, mb, P(out), 0, sh)
         else:
@@ -306,10 +325,10 @@ def main():
     # The dominant kernel's own average duration: the whole call when it is
     # one kernel; otherwise the split kernel alone (the same kernel, run
     # through pkv_paged_decode_partials), and the combine kernel alone.
-    # Contiguous K/V has no partials entry point: a two-kernel call is timed
-    # whole there.
-    n_kernels = plan.kernels if paged else 1
-    rows = w.B * w.q_len * w.Hq
+    # Contiguous K/V and varlen batches have no partials entry point: a
+    # two-kernel call is timed whole there.
+    n_kernels = plan.kernels if paged and not varlen else 1
+    rows = w.total_tokens * w.Hq
     pob, pmb = pkv.partials_bytes(prob, S)
     po2 = torch.empty(max(pob // 4, 4), dtype=torch.float32, device=dev)
     pm2 = torch.empty(max(pmb // 4, 4), dtype=torch.float32, device=dev)
@@ -368,9 +387,9 @@ def main():
         "config": dict(describe(w, S, n_rep, plan.heads_per_block), kv_layout=args.kv_layout),
         "us_per_call": round(us_call, 3),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "kernels_per_call": n_kernels,
+        "kernels_per_call": plan.kernels,
         "kernel_us": {"split": round(split_ms * 1e3, 3), "combine": round(comb_ms * 1e3, 3),
-                      "timing": timing},
+                      "timing": timing if n_kernels == plan.kernels else timing + ", split = whole call"},
         "algorithmic_bytes_per_call": algo,
         "warm_us_per_call": round(warm_ms * 1e3, 3),
         "graph_us_per_call": None if graph_call_ms is None else round(graph_call_ms * 1e3, 3),

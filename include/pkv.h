@@ -68,6 +68,11 @@ enum {
 
 #define PKV_MAX_SPLITS 256
 
+/* causal_offset value: the query tokens of each sequence are its last keys,
+ * token i of a sequence with n query tokens sits at position kv_lens[b] - n + i
+ * (the chunked-prefill / decode convention; requires kv_lens[b] >= n). */
+#define PKV_CAUSAL_LAST (-2)
+
 /* Head of the pkv_paged_decode ml_part workspace holding the per-unit arrival
  * counters of the in-kernel merge (one int32 per (sequence, kv-head group,
  * row block) unit, see pkv_plan), and the largest unit count merged
@@ -92,7 +97,8 @@ typedef struct pkv_problem {
   int32_t max_pages_per_seq; /* block_table row stride, >= 1 */
   int32_t max_kv_len;        /* host-known bound on kv_lens; 0 => max_pages_per_seq * page_size */
   float scale;               /* finite score scale, usually 1/sqrt(D) */
-  int32_t causal_offset;     /* -1 off; >= 0 position of query token 0 (all sequences) */
+  int32_t causal_offset;     /* -1 off; >= 0 position of query token 0 (all sequences);
+                                PKV_CAUSAL_LAST: each sequence's query tokens are its last keys */
   int32_t num_splits;        /* 0 heuristic; 1..PKV_MAX_SPLITS forced */
   int64_t mask_stride_b;     /* mask element stride between sequences (>= 0) */
   int64_t mask_stride_q;     /* mask element stride between query tokens; 0 => 2D [B, kv] mask */
@@ -174,6 +180,32 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                      const float *mask, float *o_part, size_t o_part_bytes,
                      float *ml_part, size_t ml_part_bytes, void *out_bf16,
                      float *out_f32, hipStream_t stream);
+
+/* Decode over a batch whose sequences have different numbers of query
+ * tokens ("varlen": chunked prefill and single-token decode in one call, as
+ * in the AstrAI paged-decode commit notes on prefill and decode kernels over
+ * the same paged cache).  Sequence b has n_b = cu_q_lens[b+1] - cu_q_lens[b]
+ * query tokens, 0 <= n_b <= p->q_len (the bound the launch is sized for).
+ *   cu_q_lens    device int32 [B + 1], cu_q_lens[0] = 0, non-decreasing,
+ *                cu_q_lens[B] = total_tokens (4-byte aligned)
+ *   total_tokens 0 .. B * q_len (else PKV_ERR_SHAPE); host copy of cu_q_lens[B]
+ *   q, out_bf16, out_f32   [total_tokens, Hq, D], token t of sequence b at
+ *                cu_q_lens[b] + t
+ *   mask         element (b, t, j) at mask[b * mask_stride_b + t * mask_stride_q + j]
+ *   causal       p->causal_offset PKV_CAUSAL_LAST (the usual choice), -1, a
+ *                position >= 0, or causal_offsets[B] as for pkv_paged_decode
+ * The workspace is the one pkv_workspace_bytes gives for p (B * q_len * Hq
+ * rows bound the token rows); other arguments and statuses as for
+ * pkv_paged_decode.  The offsets in cu_q_lens are device data the host cannot
+ * check: the kernels clamp each sequence's count to 0 .. q_len but trust the
+ * offsets to stay within total_tokens.  With every count equal to q_len the
+ * results are bit for bit those of pkv_paged_decode on the same problem. */
+int pkv_paged_decode_varlen(const pkv_problem *p, const int32_t *cu_q_lens, int64_t total_tokens,
+                            const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, const int32_t *kv_lens,
+                            const int32_t *causal_offsets, const float *mask, float *o_part,
+                            size_t o_part_bytes, float *ml_part, size_t ml_part_bytes,
+                            void *out_bf16, float *out_f32, hipStream_t stream);
 
 /* K/V layouts of pkv_contiguous_decode, and the largest key capacity per
  * sequence it takes. */

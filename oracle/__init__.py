@@ -20,6 +20,12 @@ attends over the keys of sequence b addressed through its page table; GQA
 head sharing; optional additive mask; unified causal_offset (-1 = off, c >= 0
 = absolute position of query token 0, so token i sees keys j <= c + i);
 split-KV partials merged by a log-sum-exp combine.
+
+``decode_varlen`` covers batches whose sequences carry different numbers of
+query tokens (chunked prefill and decode together, as in the same commit
+notes: prefill and decode kernels over one paged cache), one sequence at a
+time by the definition above, and the causal mode in which each sequence's
+tokens are its last keys.
 """
 from __future__ import annotations
 
@@ -72,7 +78,12 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data
 
 
+CAUSAL_LAST = -2
+
+
 def _common_args(w):
+    if getattr(w, "q_lens", None) is not None or w.causal_offset < -1:
+        raise ValueError("varlen batches and causal_offset CAUSAL_LAST go through decode_varlen")
     q = np.ascontiguousarray(w.q, dtype=np.uint16)
     k = np.ascontiguousarray(w.k_cache, dtype=np.uint16)
     v = np.ascontiguousarray(w.v_cache, dtype=np.uint16)
@@ -149,6 +160,50 @@ def decode_contiguous(w, k: np.ndarray, v: np.ndarray, layout: str = "blhd", thr
     return decode(w.replace(k_cache=k, v_cache=v, block_table=bt, page_size=cap), threads)
 
 
+def decode_varlen(w, threads: int = 0) -> np.ndarray:
+    """fp64 output [T, Hq, D] of a batch whose sequence b carries n_b query
+    tokens (w.q_lens, or q_len each when None; its tokens are w.q[b, :n_b]),
+    rows in sequence order (T = sum n_b).
+
+    Reading: each sequence is an independent decode problem with q_len = n_b,
+    evaluated here by the fixed-length definition one sequence at a time.
+    With causal_offset CAUSAL_LAST token i of sequence b sits at position
+    L_b - n_b + i and sees keys j <= L_b - n_b + i; a token at a negative
+    position (only when n_b > L_b) sees no key and its row is zero, as for
+    any row with no visible key.  A per-sequence causal_offsets[b] or a fixed
+    causal_offset >= 0 is the position of the sequence's token 0, as for the
+    fixed-length batch."""
+    n_all = w.q_lens if w.q_lens is not None else np.full(w.B, w.q_len, dtype=np.int32)
+    outs = []
+    for b in range(w.B):
+        n = int(n_all[b])
+        if n == 0:
+            continue
+        L = int(w.kv_lens[b])
+        lead = 0
+        if w.causal_offsets is not None:
+            co = int(w.causal_offsets[b])
+        elif w.causal_offset == CAUSAL_LAST:
+            co = L - n
+            if co < 0:
+                lead, co = -co, 0
+        else:
+            co = int(w.causal_offset)
+        out = np.zeros((n, w.Hq, w.D), dtype=np.float64)
+        if lead < n:
+            m = None
+            if w.mask is not None:
+                m = w.mask[b:b + 1] if w.mask.ndim == 2 else w.mask[b:b + 1, lead:n]
+            sub = w.replace(B=1, q_len=n - lead, q=w.q[b:b + 1, lead:n], block_table=w.block_table[b:b + 1],
+                            kv_lens=w.kv_lens[b:b + 1], causal_offset=co, causal_offsets=None, mask=m,
+                            q_lens=None)
+            out[lead:] = decode(sub, threads)[0]
+        outs.append(out)
+    if not outs:
+        return np.zeros((0, w.Hq, w.D), dtype=np.float64)
+    return np.concatenate(outs, axis=0)
+
+
 def max_threads() -> int:
     return int(_load().pkv_oracle_max_threads())
 
@@ -158,6 +213,45 @@ def max_threads() -> int:
 
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bruteforce_varlen(w) -> np.ndarray:
+    """Varlen brute force, token by token: [T, Hq, D].  Each query token is
+    given its absolute position explicitly (CAUSAL_LAST: L_b - n_b + i), its
+    visible keys are listed, and a naive softmax over them weights V."""
+    G = w.Hq // w.Hkv
+    P = w.page_size
+    n_all = w.q_lens if w.q_lens is not None else np.full(w.B, w.q_len, dtype=np.int32)
+    q = bf16_bits_to_f64(w.q)
+    rows = []
+    for b in range(w.B):
+        n, L = int(n_all[b]), int(w.kv_lens[b])
+        keys = [(int(w.block_table[b, j // P]), j % P) for j in range(L)]
+        for i in range(n):
+            if w.causal_offsets is not None:
+                pos = int(w.causal_offsets[b]) + i if w.causal_offsets[b] >= 0 else None
+            elif w.causal_offset == CAUSAL_LAST:
+                pos = L - n + i
+            else:
+                pos = w.causal_offset + i if w.causal_offset >= 0 else None
+            row = np.zeros((w.Hq, w.D))
+            for h in range(w.Hq):
+                kh = h // G
+                s, vs = [], []
+                for j, (pg, sl) in enumerate(keys):
+                    if pos is not None and j > pos:
+                        continue
+                    sc = float(np.dot(q[b, i, h], bf16_bits_to_f64(w.k_cache[pg, sl, kh]))) * float(np.float32(w.scale))
+                    if w.mask is not None:
+                        sc += float(w.mask[b, j] if w.mask.ndim == 2 else w.mask[b, i, j])
+                    if np.isfinite(sc):
+                        s.append(sc)
+                        vs.append(bf16_bits_to_f64(w.v_cache[pg, sl, kh]))
+                if s:
+                    e = np.exp(np.array(s) - max(s))
+                    row[h] = (e / e.sum()) @ np.array(vs)
+            rows.append(row)
+    return np.array(rows).reshape(-1, w.Hq, w.D)
 
 
 def bruteforce_decode(w) -> np.ndarray:

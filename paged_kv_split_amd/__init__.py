@@ -30,10 +30,11 @@ PKV_MAX_FUSED_UNITS = PKV_COUNTER_BYTES // 4
 PKV_KV_BLHD = 1
 PKV_KV_BHLD = 2
 PKV_MAX_CONTIGUOUS_KEYS = 1 << 30
+PKV_CAUSAL_LAST = -2
 KV_LAYOUTS = {"blhd": PKV_KV_BLHD, "bhld": PKV_KV_BHLD}
 
 EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
-            "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
+            "pkv_paged_decode_varlen", "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
             "pkv_status_string")
 
 
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, P, P, P]
         L.pkv_paged_decode_partials.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                                 ctypes.c_size_t, P]
+        L.pkv_paged_decode_varlen.argtypes = [PP, P, ctypes.c_int64, P, P, P, P, P, P, P, P,
+                                              ctypes.c_size_t, P, ctypes.c_size_t, P, P, P]
         L.pkv_contiguous_decode.argtypes = [PP, ctypes.c_int, ctypes.c_int64, P, P, P, P, P, P, P,
                                             ctypes.c_size_t, P, ctypes.c_size_t, P, P, P]
         L.pkv_combine.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
@@ -106,7 +109,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
         for name in ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
-                     "pkv_contiguous_decode",
+                     "pkv_paged_decode_varlen", "pkv_contiguous_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -190,6 +193,18 @@ def paged_decode_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block
                                   block_table or None, kv_lens or None, causal_offsets or None,
                                   mask or None, o_part or None, o_part_bytes, ml_part or None,
                                   ml_part_bytes, out_bf16 or None, out_f32 or None, stream or None)
+
+
+def paged_decode_varlen_raw(problem: Problem, cu_q_lens: int, total_tokens: int, q: int, k_cache: int,
+                            v_cache: int, block_table: int, kv_lens: int, causal_offsets: int, mask: int,
+                            o_part: int, o_part_bytes: int, ml_part: int, ml_part_bytes: int, out_bf16: int,
+                            out_f32: int, stream: int) -> int:
+    """pkv_paged_decode_varlen on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_paged_decode_varlen(ctypes.byref(problem), cu_q_lens or None, int(total_tokens), q or None,
+                                         k_cache or None, v_cache or None, block_table or None, kv_lens or None,
+                                         causal_offsets or None, mask or None, o_part or None, o_part_bytes,
+                                         ml_part or None, ml_part_bytes, out_bf16 or None, out_f32 or None,
+                                         stream or None)
 
 
 def contiguous_decode_raw(problem: Problem, kv_layout: int, kv_capacity: int, q: int, k_cache: int, v_cache: int,
@@ -305,6 +320,60 @@ def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
                           _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
                           _ptr(out), _ptr(out_f32), _stream_handle(stream))
     _check(st, "pkv_paged_decode")
+    return out
+
+
+def paged_decode_varlen(q, k_cache, v_cache, block_table, kv_lens, cu_q_lens, *, max_q_len: int,
+                        scale: float, causal_offset: int = PKV_CAUSAL_LAST, causal_offsets=None, mask=None,
+                        num_splits: int = 0, max_kv_len: int = 0, heads_per_block: int = 0, out=None,
+                        out_f32=None, o_part=None, ml_part=None, stream=None):
+    """Paged decode over sequences with different query-token counts.
+    Returns ``out`` (bf16 [T, Hq, D]).
+
+    q bf16 [T, Hq, D], the tokens of sequence b at rows cu_q_lens[b] ..
+    cu_q_lens[b+1] - 1; cu_q_lens int32 [B + 1] on the device with
+    cu_q_lens[B] = T; max_q_len bounds every sequence's token count (the
+    launch is sized for it); causal_offset defaults to PKV_CAUSAL_LAST (each
+    sequence's tokens are its last keys); mask optional fp32 [B, kv] or
+    [B, max_q_len, kv].  Other arguments as for ``paged_decode``.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(kv_lens, "kv_lens", torch.int32, 1)
+    _require(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B = kv_lens.shape[0]
+    if cu_q_lens.shape[0] != B + 1:
+        raise ValueError("cu_q_lens must have batch + 1 entries")
+    if causal_offsets is not None:
+        _require(causal_offsets, "causal_offsets", torch.int32, 1)
+    msb = msq = 0
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_cuda or mask.stride(-1) != 1:
+            raise ValueError("mask must be a device float32 tensor with a contiguous last dim")
+        msb = mask.stride(0)
+        msq = mask.stride(1) if mask.dim() == 3 else 0
+    T, Hq, D = q.shape
+    num_pages, P, Hkv, _ = k_cache.shape
+    p = make_problem(batch=B, q_len=max_q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+                     num_pages=num_pages, max_pages_per_seq=block_table.shape[1], max_kv_len=max_kv_len,
+                     scale=scale, causal_offset=causal_offset, num_splits=num_splits, mask_stride_b=msb,
+                     mask_stride_q=msq, heads_per_block=heads_per_block)
+    S = num_splits_for(p)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if S > 1 and (o_part is None or ml_part is None):
+        o_part, ml_part = alloc_workspace(p, S, q.device)
+    st = paged_decode_varlen_raw(p, _ptr(cu_q_lens), T, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                 _ptr(kv_lens), _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
+                                 0 if o_part is None else o_part.numel() * o_part.element_size(), _ptr(ml_part),
+                                 0 if ml_part is None else ml_part.numel() * ml_part.element_size(), _ptr(out),
+                                 _ptr(out_f32), _stream_handle(stream))
+    _check(st, "pkv_paged_decode_varlen")
     return out
 
 

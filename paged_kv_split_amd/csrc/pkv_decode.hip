@@ -141,6 +141,7 @@ struct Ctx {
   int row_stride;
   int kb;                // first key of the split
   int ke;                // end of the keys this block may see
+  int R;                 // packed rows of the sequence per kv head
   int jq, qq, kg, ds;
 };
 
@@ -181,7 +182,7 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
       // would make the compiler wait for all loads at the loop header
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        const int rr = r0 + r < a.R ? r0 + r : a.R - 1;
+        const int rr = r0 + r < c.R ? r0 + r : c.R - 1;
         t.mk[pp][r] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
       }
     }
@@ -422,33 +423,24 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 
   const int r0 = rb * RP;
   const int L = a.kv_lens[b];
-  int cofs = -1;
-  if (CAUSAL) cofs = a.causal_offsets ? a.causal_offsets[b] : a.causal_offset;
+  const SeqRows sr = seq_rows<CAUSAL>(a, b, L);
+  if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
 
   // per-row visible key limit and the block's key range
   int lim[RP];
   int kmax = 0;
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    const int rr = r0 + r;
-    int lr = 0;
-    if (rr < a.R) {
-      lr = L;
-      if (CAUSAL && cofs >= 0) {
-        const int64_t cl = (int64_t)cofs + rr / a.G + 1;
-        if (cl < lr) lr = (int)cl;
-      }
-    }
-    lim[r] = lr;
-    kmax = lr > kmax ? lr : kmax;
+    lim[r] = row_keys(a, sr, L, r0 + r);
+    kmax = lim[r] > kmax ? lim[r] : kmax;
   }
 
   // splits past the unit's keys: no work; outside the in-kernel merge they
   // leave (m, l) = (-inf, 0) for the combine step
   const int nact = active_splits(a, kmax);
-  const int nrows = (a.R - r0 < RP ? a.R - r0 : RP) * a.hpb;
+  const int nrows = (sr.R - r0 < RP ? sr.R - r0 : RP) * a.hpb;
   if (s >= nact) {
-    if (!a.fused) empty_partials(a, b, hg, r0, s, nrows);
+    if (!a.fused) empty_partials(a, sr.tok0, hg, r0, s, nrows);
     return;
   }
   // the unit's only split with keys writes the output itself
@@ -462,6 +454,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   c.pmask = (1 << a.page_shift) - 1;
   c.page_stride = a.page_stride;
   c.row_stride = a.row_stride;
+  c.R = sr.R;
   c.kb = s * a.chunk;
   int kend = c.kb + a.chunk;
   if (kend > kmax) kend = kmax;
@@ -475,10 +468,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     const int rr = r0 + r;
-    if (rr < a.R) {
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
+    if (rr < sr.R) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr.tok0, g, rr) * D);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
     } else {
@@ -520,7 +511,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   };
   if (threadIdx.x < RP * a.hpb) {
     const int rr = r0 + (threadIdx.x >> a.lhpb);
-    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
+    rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
   load_bt(c.kb);
   __syncthreads();

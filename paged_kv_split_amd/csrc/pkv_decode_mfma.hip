@@ -79,6 +79,7 @@ struct MCtx {
   int64_t page_stride;
   int row_stride;
   int ke;
+  int R;  // packed rows of the sequence per kv head
 };
 
 // Loads of one 16-key tile: full K/V rows, 128 bits per lane.  Rows past the
@@ -134,7 +135,7 @@ __device__ __forceinline__ void mload(const DecodeArgs &a, const MCtx &c, int b,
       // all loads at the loop header
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const int rr = r0 + cc + 16 * rb < a.R ? r0 + cc + 16 * rb : a.R - 1;
+        const int rr = r0 + cc + 16 * rb < c.R ? r0 + cc + 16 * rb : c.R - 1;
         t.mk[rb][i] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
       }
     }
@@ -364,29 +365,20 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   const int r0 = rg * RW;
 
   const int kvlen = a.kv_lens[b];
-  int cofs = -1;
-  if (CAUSAL) cofs = a.causal_offsets ? a.causal_offsets[b] : a.causal_offset;
-  auto row_limit = [&](int rr) -> int {
-    if (rr >= a.R) return 0;
-    int lr = kvlen;
-    if (CAUSAL && cofs >= 0) {
-      const int64_t cl = (int64_t)cofs + rr / a.G + 1;
-      if (cl < lr) lr = (int)cl;
-    }
-    return lr;
-  };
+  const SeqRows sr = seq_rows<CAUSAL>(a, b, kvlen);
+  if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
   int lim[NRB];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) lim[rb] = row_limit(r0 + cc + 16 * rb);
-  const int rlast = (r0 + RW < a.R ? r0 + RW : a.R) - 1;
-  const int kmax = row_limit(rlast);   // the last row sees the most keys
+  for (int rb = 0; rb < NRB; ++rb) lim[rb] = row_keys(a, sr, kvlen, r0 + cc + 16 * rb);
+  const int rlast = (r0 + RW < sr.R ? r0 + RW : sr.R) - 1;
+  const int kmax = row_keys(a, sr, kvlen, rlast);   // the last row sees the most keys
 
   // splits past the unit's keys: no work; outside the in-kernel merge they
   // leave (m, l) = (-inf, 0) for the combine step
   const int nact = active_splits(a, kmax);
-  const int nrt = (a.R - r0 < RW ? a.R - r0 : RW) * a.hpb;  // output rows of the block
+  const int nrt = (sr.R - r0 < RW ? sr.R - r0 : RW) * a.hpb;  // output rows of the block
   if (s >= nact) {
-    if (!a.fused) empty_partials(a, b, hg, r0, s, nrt);
+    if (!a.fused) empty_partials(a, sr.tok0, hg, r0, s, nrt);
     return;
   }
   // the unit's only split with keys writes the output itself
@@ -404,6 +396,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   c.pmask = (1 << a.page_shift) - 1;
   c.page_stride = a.page_stride;
   c.row_stride = a.row_stride;
+  c.R = sr.R;
   const int kb = s * a.chunk;
   int kend = kb + a.chunk;
   if (kend > kmax) kend = kmax;
@@ -413,10 +406,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int rr = r0 + cc + 16 * rb;
-    if (rr < a.R) {
-      const int i = rr / a.G;
-      const int h = g * a.G + (rr - i * a.G);
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (((int64_t)b * a.q_len + i) * a.Hq + h) * D);
+    if (rr < sr.R) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr.tok0, g, rr) * D);
 #pragma unroll
       for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
     } else {
@@ -452,7 +443,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
 
   if (threadIdx.x < RW * a.hpb) {
     const int rr = r0 + (threadIdx.x >> a.lhpb);
-    rowtab[threadIdx.x] = rr < a.R ? out_row(a, b, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
+    rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
   load_bt(kb);
   __syncthreads();
@@ -492,7 +483,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     }
     if (q == 0) *reinterpret_cast<float2 *>(mlb + u * 2) = make_float2(st.m[rb], ltot[rb]);
     const int rs = r0 + 16 * rb;
-    const int nrows = (a.R - rs < 16 ? a.R - rs : 16) * a.hpb;
+    const int nrows = (sr.R - rs < 16 ? sr.R - rs : 16) * a.hpb;
     __syncthreads();
     auto item = [&](int ri, int d, float &M, float &W, float &vx, float &vy) {
       merge_waves<NW, L::OB_STRIDE>(mlb, ob, HR, wph, ri, d, M, W, vx, vy);

@@ -145,11 +145,64 @@ __device__ __forceinline__ int window_keys(int cap, int page_shift, int step) {
   return w > ((int64_t)1 << 30) ? ((1 << 30) / step) * step : (int)w;
 }
 
-// Output row (b, i, h) of packed row rr (= i * G + k) of kv head g.
-__device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int b, int g, int rr) {
+// The query rows of sequence b: its first token in q / out, its packed rows
+// per kv head (G per query token) and its causal offset.  A varlen batch
+// (a.cu_q) gives each sequence its own token count, at most a.q_len.
+struct SeqRows {
+  int64_t tok0;  // first token of the sequence in q and out
+  int R;         // packed rows per kv head
+  int cofs;      // causal offset (position of the sequence's first query token)
+  bool causal;
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ SeqRows seq_rows(const DecodeArgs &a, int b, int L) {
+  SeqRows r;
+  if (a.cu_q) {
+    const int c0 = a.cu_q[b];
+    int n = a.cu_q[b + 1] - c0;
+    n = n < 0 ? 0 : (n > a.q_len ? a.q_len : n);
+    r.tok0 = c0;
+    r.R = n * a.G;
+  } else {
+    r.tok0 = (int64_t)b * a.q_len;
+    r.R = a.R;
+  }
+  r.cofs = -1;
+  r.causal = false;
+  if constexpr (CAUSAL) {
+    if (a.causal_offsets) {
+      r.cofs = a.causal_offsets[b];
+      r.causal = r.cofs >= 0;
+    } else if (a.causal_offset == kCausalLast) {  // tokens at positions L - n .. L - 1
+      r.cofs = L - r.R / a.G;
+      r.causal = true;
+    } else {
+      r.cofs = a.causal_offset;
+      r.causal = r.cofs >= 0;
+    }
+  }
+  return r;
+}
+
+// Keys packed row rr of the sequence may see: none past its rows; else its L
+// keys, or with a causal offset those up to its token's position.
+__device__ __forceinline__ int row_keys(const DecodeArgs &a, const SeqRows &sr, int L, int rr) {
+  if (rr >= sr.R) return 0;
+  int lr = L;
+  if (sr.causal) {
+    const int64_t cl = (int64_t)sr.cofs + rr / a.G + 1;
+    if (cl < lr) lr = cl < 0 ? 0 : (int)cl;
+  }
+  return lr;
+}
+
+// Output row (token, query head) of packed row rr (= i * G + k) of kv head g
+// of the sequence whose first token is tok0.
+__device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int64_t tok0, int g, int rr) {
   const int i = rr / a.G;
   const int h = g * a.G + (rr - i * a.G);
-  return ((int64_t)b * a.q_len + i) * a.Hq + h;
+  return (tok0 + i) * a.Hq + h;
 }
 
 // ---- log-sum-exp merge of split partials -----------------------------------
@@ -280,9 +333,9 @@ __device__ void merge_rows(const float *o_part, const float *ml_part, int S, int
 // A split with no keys of its unit, outside the in-kernel merge: its (m, l)
 // entries become (-inf, 0) (its o_part rows are left untouched, never read).
 // Block row ri = r * hpb + hh is packed row r0 + r of kv head hg * hpb + hh.
-__device__ __forceinline__ void empty_partials(const DecodeArgs &a, int b, int hg, int r0, int s, int nrows) {
+__device__ __forceinline__ void empty_partials(const DecodeArgs &a, int64_t tok0, int hg, int r0, int s, int nrows) {
   for (int ri = threadIdx.x; ri < nrows; ri += blockDim.x) {
-    const int64_t row = out_row(a, b, hg * a.hpb + (ri & (a.hpb - 1)), r0 + (ri >> a.lhpb));
+    const int64_t row = out_row(a, tok0, hg * a.hpb + (ri & (a.hpb - 1)), r0 + (ri >> a.lhpb));
     *reinterpret_cast<float2 *>(a.ml_part + (row * a.S + s) * 2) = make_float2(-INFINITY, 0.f);
   }
 }

@@ -55,7 +55,7 @@ int check_problem(const pkv_problem *p) {
   if (cap > INT32_MAX) return PKV_ERR_SHAPE;
   if ((int64_t)p->max_kv_len > cap) return PKV_ERR_SHAPE;
   if (!isfinite(p->scale)) return PKV_ERR_SHAPE;
-  if (p->causal_offset < -1) return PKV_ERR_SHAPE;
+  if (p->causal_offset < PKV_CAUSAL_LAST) return PKV_ERR_SHAPE;
   if (p->num_splits < 0) return PKV_ERR_SHAPE;
   if (p->num_splits > PKV_MAX_SPLITS) return PKV_ERR_UNSUPPORTED;
   if (p->heads_per_block < 0) return PKV_ERR_SHAPE;
@@ -307,10 +307,17 @@ struct KvSource {
   int64_t capacity;            // contiguous: keys per sequence in the cache
 };
 
-int plan_decode(const pkv_problem *p, const void *q, const KvSource &src, const int32_t *kv_lens,
-                const int32_t *causal_offsets, const float *mask, float *o_part, size_t o_part_bytes,
-                float *ml_part, size_t ml_part_bytes, void *out_bf16, float *out_f32, bool partials_only,
-                pkv::DecodeArgs *a) {
+// Query tokens: q_len per sequence, or (cu_q) a varlen batch of
+// total_tokens tokens packed by sequence, at most q_len each.
+struct QSource {
+  const int32_t *cu_q;
+  int64_t total_tokens;
+};
+
+int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const KvSource &src,
+                const int32_t *kv_lens, const int32_t *causal_offsets, const float *mask, float *o_part,
+                size_t o_part_bytes, float *ml_part, size_t ml_part_bytes, void *out_bf16, float *out_f32,
+                bool partials_only, pkv::DecodeArgs *a) {
   const bool paged = src.layout == 0;
   const int32_t *block_table = src.block_table;
   if (!q || !src.k || !src.v || (paged && !block_table) || !kv_lens) return PKV_ERR_NULL;
@@ -365,6 +372,8 @@ int plan_decode(const pkv_problem *p, const void *q, const KvSource &src, const 
   a->k = static_cast<const uint16_t *>(src.k);
   a->v = static_cast<const uint16_t *>(src.v);
   a->block_table = paged ? block_table : nullptr;
+  a->cu_q = qs.cu_q;
+  a->rows = qs.total_tokens * p->num_q_heads;
   a->kv_lens = kv_lens;
   a->causal_offsets = causal_offsets;
   a->mask = mask;
@@ -417,7 +426,7 @@ int plan_decode(const pkv_problem *p, const void *q, const KvSource &src, const 
 }
 
 int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stream) {
-  const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0;
+  const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0 || p->causal_offset == PKV_CAUSAL_LAST;
   (void)hipGetLastError();
   const int rows = pkv::rows_per_block(a.R);
   int err = pkv::use_mfma(a.R)
@@ -438,7 +447,7 @@ int launch_all(const pkv::DecodeArgs &a, const pkv_problem *p, float *o_part, vo
     c.ml_part = a.ml_part;
     c.out = static_cast<uint16_t *>(out_bf16);
     c.out_f32 = out_f32;
-    c.rows = (int64_t)p->batch * p->q_len * p->num_q_heads;
+    c.rows = a.rows;
     c.S = a.S;
     if (pkv::launch_combine(c, p->head_dim, stream) != hipSuccess) return PKV_ERR_LAUNCH;
   }
@@ -459,8 +468,28 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
   if (rc) return rc;
   if (p->batch == 0) return PKV_OK;
   pkv::DecodeArgs a;
-  rc = plan_decode(p, q, KvSource{k_cache, v_cache, block_table, 0, 0}, kv_lens, causal_offsets, mask, o_part,
-                   o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
+  rc = plan_decode(p, q, QSource{nullptr, (int64_t)p->batch * p->q_len}, KvSource{k_cache, v_cache, block_table, 0, 0},
+                   kv_lens, causal_offsets, mask, o_part, o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32,
+                   false, &a);
+  if (rc) return rc;
+  return launch_all(a, p, o_part, out_bf16, out_f32, stream);
+}
+
+int pkv_paged_decode_varlen(const pkv_problem *p, const int32_t *cu_q_lens, int64_t total_tokens, const void *q,
+                            const void *k_cache, const void *v_cache, const int32_t *block_table,
+                            const int32_t *kv_lens, const int32_t *causal_offsets, const float *mask,
+                            float *o_part, size_t o_part_bytes, float *ml_part, size_t ml_part_bytes,
+                            void *out_bf16, float *out_f32, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (total_tokens < 0 || total_tokens > (int64_t)p->batch * p->q_len) return PKV_ERR_SHAPE;
+  if (p->batch == 0 || total_tokens == 0) return PKV_OK;
+  if (!cu_q_lens) return PKV_ERR_NULL;
+  if (!aligned(cu_q_lens, 4)) return PKV_ERR_ALIGN;
+  pkv::DecodeArgs a;
+  rc = plan_decode(p, q, QSource{cu_q_lens, total_tokens}, KvSource{k_cache, v_cache, block_table, 0, 0}, kv_lens,
+                   causal_offsets, mask, o_part, o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false,
+                   &a);
   if (rc) return rc;
   return launch_all(a, p, o_part, out_bf16, out_f32, stream);
 }
@@ -486,8 +515,9 @@ int pkv_contiguous_decode(const pkv_problem *p, int kv_layout, int64_t kv_capaci
   // K/V element offsets must fit the 64-bit arithmetic of the kernels
   if ((double)pc.batch * (double)kv_capacity * pc.num_kv_heads * pc.head_dim > 9.0e18) return PKV_ERR_SHAPE;
   pkv::DecodeArgs a;
-  rc = plan_decode(&pc, q, KvSource{k_cache, v_cache, nullptr, kv_layout, kv_capacity}, kv_lens, causal_offsets,
-                   mask, o_part, o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
+  rc = plan_decode(&pc, q, QSource{nullptr, (int64_t)pc.batch * pc.q_len},
+                   KvSource{k_cache, v_cache, nullptr, kv_layout, kv_capacity}, kv_lens, causal_offsets, mask, o_part,
+                   o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32, false, &a);
   if (rc) return rc;
   return launch_all(a, &pc, o_part, out_bf16, out_f32, stream);
 }
@@ -501,8 +531,9 @@ int pkv_paged_decode_partials(const pkv_problem *p, const void *q, const void *k
   if (rc) return rc;
   if (p->batch == 0) return PKV_OK;
   pkv::DecodeArgs a;
-  rc = plan_decode(p, q, KvSource{k_cache, v_cache, block_table, 0, 0}, kv_lens, causal_offsets, mask, o_part,
-                   o_part_bytes, ml_part, ml_part_bytes, nullptr, nullptr, true, &a);
+  rc = plan_decode(p, q, QSource{nullptr, (int64_t)p->batch * p->q_len}, KvSource{k_cache, v_cache, block_table, 0, 0},
+                   kv_lens, causal_offsets, mask, o_part, o_part_bytes, ml_part, ml_part_bytes, nullptr, nullptr, true,
+                   &a);
   if (rc) return rc;
   return launch_plan(a, p, stream);
 }

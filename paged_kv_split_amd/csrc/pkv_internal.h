@@ -16,6 +16,7 @@ struct DecodeArgs {
   const int32_t *block_table;
   const int32_t *kv_lens;
   const int32_t *causal_offsets;  // nullable
+  const int32_t *cu_q;            // nullable: [B + 1] token starts of a varlen batch (q, out packed by token)
   const float *mask;              // nullable
   float *o_part;                  // [rows, S, D]   (S > 1)
   float *ml_part;                 // [rows, S, 2]   (S > 1)
@@ -33,13 +34,14 @@ struct DecodeArgs {
   int32_t chunk;                  // keys per split (multiple of the tile)
   int32_t nrb;                    // row blocks per kv head
   int32_t hpb, lhpb;              // kv heads per workgroup (1, 2 or 4) and its log2
-  int32_t causal_offset;          // -1 off (overridden by causal_offsets)
+  int32_t causal_offset;          // -1 off, kCausalLast, >= 0 (overridden by causal_offsets)
   float scale_log2;               // scale * log2(e)
   int32_t outer;                  // B * S
   int32_t inner;                  // (Hkv / hpb) * nrb: unit (kv-head group, row block) slots per (b, split)
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
   int32_t *counters;              // [units] arrival counters (fused), zero between calls
+  int64_t rows;                   // output rows: tokens * Hq
 };
 
 struct CombineArgs {
@@ -60,6 +62,7 @@ inline bool use_mfma(int R) { return R > 2; }
 int rows_per_block(int R);         // rows per workgroup: RP (VALU, 1 or 2) or 16/32 (MFMA)
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
+constexpr int kCausalLast = -2;    // causal_offset: the query tokens are the sequence's last keys
 constexpr int kMaxHeadsPerBlock = 4;  // kv heads one split workgroup may cover (one wave or more each)
 
 // Launchers (return a hipError_t value).

@@ -128,3 +128,21 @@ def sub_batch(w, seqs):
         kv_lens=w.kv_lens[seqs].copy(),
         causal_offsets=None if w.causal_offsets is None else w.causal_offsets[seqs].copy(),
         mask=None if w.mask is None else w.mask[seqs].copy())
+
+
+def run_varlen(w, num_splits=0, heads_per_block=0, sync=True):
+    """pkv_paged_decode_varlen on the workload's packed tokens (w.q_lens, or
+    q_len per sequence); returns (out_bf16 bits [T, Hq, D], out_f32)."""
+    d = dev_tensors(w)
+    dev = d["q"].device
+    qp, cu = w.packed_q()
+    q = torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16).to(dev)
+    cu_t = torch.from_numpy(cu).to(dev)
+    out32 = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+    out = pkv.paged_decode_varlen(q, d["k"], d["v"], d["bt"], d["kl"], cu_t, max_q_len=w.q_len, scale=w.scale,
+                                  causal_offset=w.causal_offset, causal_offsets=d["co"], mask=d["mask"],
+                                  num_splits=num_splits, max_kv_len=w.max_kv_len,
+                                  heads_per_block=heads_per_block, out_f32=out32)
+    if sync:
+        torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy()

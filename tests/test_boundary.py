@@ -78,7 +78,7 @@ def call(p, **ptrs):
     ("max_kv_len", 129, pkv.PKV_ERR_SHAPE),           # > 4 pages * 32
     ("max_kv_len", -1, pkv.PKV_ERR_SHAPE),
     ("batch", -1, pkv.PKV_ERR_SHAPE),
-    ("causal_offset", -2, pkv.PKV_ERR_SHAPE),
+    ("causal_offset", -3, pkv.PKV_ERR_SHAPE),
     ("num_splits", -1, pkv.PKV_ERR_SHAPE),
     ("num_splits", 257, pkv.PKV_ERR_UNSUPPORTED),
     ("scale", float("nan"), pkv.PKV_ERR_SHAPE),
@@ -321,3 +321,28 @@ def test_contiguous_problem_plans_like_the_entry_point():
 def test_kv_row_too_wide_is_rejected():
     assert call(base_problem(num_splits=1, num_q_heads=1 << 17, num_kv_heads=1 << 17, head_dim=256)) == \
         pkv.PKV_ERR_SHAPE
+
+
+def call_varlen(p, cu=FAKE, total=2, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, kl=FAKE, co=0, mask=0, o=0, ob=0, ml=0, mb=0, out=FAKE,
+             out32=0)
+    a.update(ptrs)
+    return pkv.paged_decode_varlen_raw(p, cu, total, a["q"], a["k"], a["v"], a["bt"], a["kl"], a["co"],
+                                       a["mask"], a["o"], a["ob"], a["ml"], a["mb"], a["out"], a["out32"], 0)
+
+
+def test_varlen_decode_checks():
+    """Argument checks of pkv_paged_decode_varlen, all answered before any
+    device work (no GPU here)."""
+    p = base_problem(num_splits=1, q_len=4, causal_offset=pkv.PKV_CAUSAL_LAST)
+    assert call_varlen(p, total=9) == pkv.PKV_ERR_SHAPE                 # > B * q_len = 8
+    assert call_varlen(p, total=-1) == pkv.PKV_ERR_SHAPE
+    assert call_varlen(p, total=0, cu=0, q=0, out=0) == pkv.PKV_OK      # no tokens: nothing to do
+    assert call_varlen(base_problem(batch=0), total=0, cu=0) == pkv.PKV_OK
+    assert call_varlen(p, cu=0) == pkv.PKV_ERR_NULL
+    assert call_varlen(p, cu=FAKE + 2) == pkv.PKV_ERR_ALIGN
+    assert call_varlen(p, q=0) == pkv.PKV_ERR_NULL
+    assert call_varlen(p, q=FAKE + 8) == pkv.PKV_ERR_ALIGN
+    assert call_varlen(base_problem(num_splits=1, causal_offset=-3)) == pkv.PKV_ERR_SHAPE
+    assert call_varlen(base_problem(num_splits=4, q_len=4)) == pkv.PKV_ERR_WORKSPACE
+    assert pkv.PKV_CAUSAL_LAST == -2

@@ -1,0 +1,111 @@
+"""GPU parity of pkv_paged_decode_varlen (sequences with different numbers of
+query tokens: chunked prefill and decode in one batch) against the fp64
+oracle's varlen form, and bit-identity with pkv_paged_decode where the two
+describe the same problem."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check, note, run, run_varlen  # noqa: E402
+
+LAST = workloads.CAUSAL_LAST
+
+# (q_lens, kv_lens, build args): VALU (G * max_q <= 2) and matrix-core
+# families, several tiles and row blocks, ragged tails, empty sequences,
+# sequences with fewer keys than tokens, masks, GQA groups.
+CASES = [
+    ([1, 2, 0, 2], [37, 300, 50, 2], dict(Hq=8, Hkv=8, D=64, page_size=32, causal="lastv")),
+    ([1, 1, 1], [1000, 1, 4097], dict(Hq=16, Hkv=16, D=128, page_size=16, causal="lastv", mask="2d")),
+    ([5, 1, 17, 0, 3], [600, 77, 2050, 9, 3], dict(Hq=32, Hkv=8, D=128, page_size=32, causal="lastv")),
+    ([40, 1, 1, 33], [64, 900, 5000, 40], dict(Hq=16, Hkv=2, D=64, page_size=64, causal="lastv",
+                                               mask="3d", mask_p=0.2)),
+    ([7, 2, 1], [3, 1500, 700], dict(Hq=24, Hkv=4, D=64, page_size=32, causal="lastv")),   # 7 tokens, 3 keys
+    ([3, 9, 1, 4], [129, 1030, 31, 800], dict(Hq=8, Hkv=2, D=256, page_size=16, causal="lastv")),
+    ([2, 6, 1], [200, 400, 3000], dict(Hq=4, Hkv=1, D=32, page_size=32)),                  # causal off
+    ([4, 1, 12], [500, 100, 2000], dict(Hq=32, Hkv=8, D=128, page_size=32, causal=20)),
+    ([16, 16, 1, 16], [4000, 16, 2500, 700], dict(Hq=8, Hkv=1, D=128, page_size=32, causal="lastv",
+                                                   mask="2d", mask_p=0.3)),
+]
+
+
+def compare_varlen(w, num_splits=0, heads_per_block=0):
+    note(f"varlen {w.name} B={w.B} q_lens={w.q_lens.tolist() if w.q_lens is not None else w.q_len} "
+         f"Hq={w.Hq} Hkv={w.Hkv} D={w.D} maxL={w.max_kv_len} causal={w.causal_offset} "
+         f"mask={None if w.mask is None else w.mask.ndim} splits={num_splits} hpb={heads_per_block} seed={w.seed}")
+    o16, o32 = run_varlen(w, num_splits, heads_per_block)
+    ref = oracle.decode_varlen(w)
+    assert o16.shape == ref.shape
+    return check(o16, o32, ref, f"varlen {w.name}"), o16, o32
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+@pytest.mark.parametrize("splits", [0, 1, 4])
+def test_varlen_cases(i, splits):
+    q_lens, lens, kw = CASES[i]
+    w = workloads.varlen(f"varlen{i}", q_lens=q_lens, kv_lens=lens, B=len(q_lens), seed=3000 + i,
+                         spare_pages=2, **kw)
+    compare_varlen(w, num_splits=splits)
+
+
+@pytest.mark.parametrize("hpb", [1, 2])
+def test_varlen_heads_per_block(hpb):
+    w = workloads.varlen("varlen_hpb", q_lens=[1, 3, 2], kv_lens=[1200, 90, 2600], B=3, Hq=16, Hkv=4, D=128,
+                         page_size=32, seed=3100, causal="lastv")
+    compare_varlen(w, num_splits=4, heads_per_block=hpb)
+
+
+def test_mixed_prefill_and_decode_batch():
+    """The mixed workload (a quarter of 32 sequences with prefill chunks of
+    8..64 tokens, the rest one decode token) at full size, every row."""
+    w = workloads.mixed()
+    compare_varlen(w)
+
+
+def test_equal_counts_are_the_fixed_batch_bit_for_bit():
+    """Every sequence with q_len tokens: the varlen call and pkv_paged_decode
+    give the same bits, with explicit per-sequence offsets and with
+    CAUSAL_LAST through both entry points."""
+    w = workloads.build("eq", B=5, q_len=3, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[3, 700, 2049, 64, 1300],
+                        seed=3200, causal="last", mask="3d", mask_p=0.1)
+    note("varlen equal counts: explicit offsets and CAUSAL_LAST")
+    f16, f32 = run(w, num_splits=3)
+    v16, v32 = run_varlen(w, num_splits=3)
+    assert np.array_equal(v16.reshape(f16.shape), f16)
+    assert np.array_equal(v32.reshape(f32.shape).view(np.uint32), f32.view(np.uint32))
+    last = w.replace(causal_offsets=None, causal_offset=LAST)
+    l16, l32 = run(last, num_splits=3)
+    lv16, lv32 = run_varlen(last.replace(q_lens=np.full(5, 3, np.int32)), num_splits=3)
+    assert np.array_equal(l16, f16) and np.array_equal(l32.view(np.uint32), f32.view(np.uint32))
+    assert np.array_equal(lv16, v16) and np.array_equal(lv32.view(np.uint32), v32.view(np.uint32))
+
+
+def test_causal_last_with_fewer_keys_than_tokens_fixed_entry():
+    """pkv_paged_decode with causal_offset CAUSAL_LAST where some sequence is
+    shorter than q_len: its leading rows see no key and are zero."""
+    w = workloads.build("lastshort", B=3, q_len=6, Hq=8, Hkv=2, D=64, page_size=16, kv_lens=[2, 40, 6],
+                        seed=3300).replace(causal_offset=LAST)
+    note("fixed entry, CAUSAL_LAST, kv_lens [2, 40, 6], q_len 6")
+    o16, o32 = run(w, num_splits=2)
+    ref = oracle.decode_varlen(w).reshape(o32.shape)
+    check(o16, o32, ref, "causal last fixed")
+    assert (o32[0, :4] == 0).all()
+
+
+def test_no_tokens_at_all_writes_nothing():
+    import torch
+    import paged_kv_split_amd as pkv
+    w = workloads.varlen("none", q_lens=[0, 0], kv_lens=[30, 5], B=2, Hq=4, Hkv=2, D=64, page_size=16, seed=3400)
+    note("varlen, zero tokens")
+    d = torch.device("cuda:0")
+    k = torch.from_numpy(w.k_cache.view(np.int16)).view(torch.bfloat16).to(d)
+    bt = torch.from_numpy(w.block_table).to(d)
+    kl = torch.from_numpy(w.kv_lens).to(d)
+    cu = torch.zeros(3, dtype=torch.int32, device=d)
+    q = torch.empty(0, 4, 64, dtype=torch.bfloat16, device=d)
+    out = pkv.paged_decode_varlen(q, k, k, bt, kl, cu, max_q_len=1, scale=w.scale)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4, 64)

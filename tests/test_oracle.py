@@ -329,3 +329,94 @@ def test_contiguous_layouts_place_keys_as_documented():
                     assert np.array_equal(vh[b, g, j], w.v_cache[pg, j % P, g])
                 else:
                     assert (kb[b, j, g] == workloads.BF16_NAN).all() and (vh[b, g, j] == workloads.BF16_NAN).all()
+
+
+# ---- varlen batches (per-sequence query-token counts) ----------------------
+
+VARLEN = [
+    dict(q_lens=[1, 5, 0, 3], lens=[40, 9, 20, 3], causal="lastv"),             # last: n_b = L_b
+    dict(q_lens=[4, 1, 2], lens=[2, 30, 0], causal="lastv"),                    # n > L: leading rows see nothing
+    dict(q_lens=[3, 1, 6], lens=[50, 17, 64], causal="lastv", mask="3d", mask_p=0.3),
+    dict(q_lens=[2, 2, 1], lens=[11, 64, 5], mask="2d", mask_p=0.4),            # causal off
+    dict(q_lens=[5, 0, 1], lens=[33, 8, 70], causal=3),                         # one fixed position
+    dict(q_lens=[1, 1, 1], lens=[7, 1, 40], causal="lastv", Hq=8, Hkv=1, D=32),
+]
+
+
+def varlen_small(seed, q_lens, lens, **kw):
+    args = dict(B=len(q_lens), Hq=4, Hkv=2, D=16, page_size=8)
+    args.update(kw)
+    return workloads.varlen("varlen", q_lens=q_lens, kv_lens=lens, seed=seed, spare_pages=2, **args)
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN)))
+def test_varlen_matches_token_by_token_bruteforce(i):
+    w = varlen_small(400 + i, **dict(VARLEN[i]))
+    a = oracle.decode_varlen(w)
+    b = oracle.bruteforce_varlen(w)
+    assert a.shape == (w.total_tokens, w.Hq, w.D)
+    assert np.isfinite(a).all()
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_varlen_with_explicit_offsets_equals_the_fixed_batch():
+    """Equal token counts and causal offsets L_b - q_len given per sequence:
+    the varlen form is the fixed-length batch, bit for bit; and CAUSAL_LAST
+    gives the same offsets."""
+    w = small(410, B=4, lens=[9, 30, 64, 17], q_len=3, causal="last", mask="3d", mask_p=0.2)
+    fixed = oracle.decode(w).reshape(-1, w.Hq, w.D)
+    assert np.array_equal(oracle.decode_varlen(w), fixed)
+    last = w.replace(causal_offsets=None, causal_offset=workloads.CAUSAL_LAST)
+    assert np.array_equal(oracle.decode_varlen(last), fixed)
+    assert np.array_equal(oracle.decode_varlen(last.replace(q_lens=np.full(4, 3, np.int32))), fixed)
+
+
+def _sdpa_rows(w, b, n, L, is_causal):
+    """torch's scaled_dot_product_attention in float64 on sequence b's keys
+    (gathered through its page table, kv heads repeated to the query heads)."""
+    P, G = w.page_size, w.Hq // w.Hkv
+    idx = [(int(w.block_table[b, j // P]), j % P) for j in range(L)]
+    K = np.stack([oracle.bf16_bits_to_f64(w.k_cache[pg, s]) for pg, s in idx])      # [L, Hkv, D]
+    V = np.stack([oracle.bf16_bits_to_f64(w.v_cache[pg, s]) for pg, s in idx])
+    q = torch.tensor(oracle.bf16_bits_to_f64(w.q[b, :n])).permute(1, 0, 2)          # [Hq, n, D]
+    k = torch.tensor(K).repeat_interleave(G, dim=1).permute(1, 0, 2)
+    v = torch.tensor(V).repeat_interleave(G, dim=1).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=is_causal,
+                                                         scale=float(np.float32(w.scale)))
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_causal_last_prefill_of_whole_sequence_is_textbook_causal_attention():
+    """n_b = L_b with CAUSAL_LAST is causal self-attention over the sequence,
+    which torch's scaled_dot_product_attention(is_causal=True) computes
+    independently (its causal mask is aligned at token 0)."""
+    w = varlen_small(420, q_lens=[12, 1, 7], lens=[12, 1, 7], causal="lastv", Hq=6, Hkv=2, D=32)
+    got = oracle.decode_varlen(w)
+    t = 0
+    for b in range(w.B):
+        n = int(w.q_lens[b])
+        np.testing.assert_allclose(got[t:t + n], _sdpa_rows(w, b, n, n, True), rtol=0, atol=1e-12)
+        t += n
+
+
+def test_decode_token_with_causal_last_sees_every_key():
+    """n_b = 1 with CAUSAL_LAST: the token is the last key, so it sees all L_b
+    keys: non-causal attention of one query (torch's sdpa, float64)."""
+    w = varlen_small(430, q_lens=[1, 1], lens=[37, 64], causal="lastv", Hq=4, Hkv=4, D=16)
+    got = oracle.decode_varlen(w)
+    for b in range(2):
+        np.testing.assert_allclose(got[b:b + 1], _sdpa_rows(w, b, 1, int(w.kv_lens[b]), False), rtol=0,
+                                   atol=1e-12)
+
+
+def test_packed_q_and_mixed_workload():
+    w = varlen_small(440, q_lens=[2, 0, 3], lens=[5, 6, 7])
+    q, cu = w.packed_q()
+    assert cu.tolist() == [0, 2, 2, 5] and q.shape == (5, 4, 16)
+    assert np.array_equal(q[2:5], w.q[2, :3]) and np.array_equal(q[:2], w.q[0, :2])
+    m = workloads.mixed()
+    assert m.q_lens.max() <= m.q_len == 64 and m.q_lens.min() >= 1
+    assert (m.kv_lens >= m.q_lens).all() and m.causal_offset == workloads.CAUSAL_LAST
+    assert 0 < (m.q_lens > 1).sum() < m.B
+    with pytest.raises(ValueError):
+        oracle.decode(m)

@@ -29,6 +29,7 @@ import numpy as np
 import torch
 
 BF16_NAN = 0x7FC0
+CAUSAL_LAST = -2   # causal_offset: each sequence's query tokens are its last keys
 
 
 @dataclasses.dataclass
@@ -52,6 +53,23 @@ class Workload:
     mask: Optional[np.ndarray] = None             # float32, 2D [B, S] or 3D [B, q_len, S]
     num_splits: int = 0
     seed: int = 0
+    # Varlen batches: sequence b carries q_lens[b] <= q_len query tokens, the
+    # first q_lens[b] of q[b] (the rest are padding, never read).
+    q_lens: Optional[np.ndarray] = None           # int32 [B] or None
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q_lens.sum()) if self.q_lens is not None else self.B * self.q_len
+
+    def packed_q(self) -> tuple[np.ndarray, np.ndarray]:
+        """(q [T, Hq, D] with sequence b's tokens at rows cu[b] .. cu[b+1]-1,
+        cu int32 [B + 1]) for a varlen batch."""
+        n = self.q_lens if self.q_lens is not None else np.full(self.B, self.q_len, dtype=np.int32)
+        cu = np.zeros(self.B + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(n)
+        q = np.concatenate([self.q[b, :int(n[b])] for b in range(self.B)], axis=0) if self.B else \
+            self.q.reshape(0, self.Hq, self.D)
+        return np.ascontiguousarray(q.reshape(-1, self.Hq, self.D)), cu
 
     @property
     def num_pages(self) -> int:
@@ -244,9 +262,38 @@ def ragged(seed: int = 1050, B: int = 256, hi: int = 8192) -> Workload:
                  kv_lens=lognormal_lens(B, hi=hi), seed=seed, causal="last")
 
 
+def mixed(seed: int = 1060, B: int = 32, max_q: int = 64, hi: int = 8192) -> Workload:
+    """Chunked prefill mixed with decode in one batch: B=32, Hq=32, Hkv=8,
+    D=128, page 32; kv_lens lognormal (median 2048, sigma 0.75) clipped to
+    [max_q, hi]; then (drawn last) each sequence carries a prefill chunk of
+    U[8, max_q] query tokens with probability 1/4, else one decode token; each
+    sequence's tokens are its last keys (causal_offset CAUSAL_LAST)."""
+    g = torch.Generator().manual_seed(seed)
+    w = build("mixed", B=B, q_len=max_q, Hq=32, Hkv=8, D=128, page_size=32,
+              kv_lens=lognormal_lens(B, median=2048.0, sigma=0.75, lo=max_q, hi=hi), seed=seed, gen=g)
+    chunk = torch.rand(B, generator=g) < 0.25
+    n = torch.randint(8, max_q + 1, (B,), generator=g)
+    q_lens = torch.where(chunk, n, torch.ones_like(n)).to(torch.int32).numpy()
+    return w.replace(q_lens=q_lens, causal_offset=CAUSAL_LAST)
+
+
+def varlen(name: str, *, q_lens, seed: int, **kw) -> Workload:
+    """``build`` with q_len = max(q_lens) (at least 1) and per-sequence query
+    token counts q_lens (drawn from nothing: given); causal "lastv" sets
+    causal_offset CAUSAL_LAST, the other causal modes are build's."""
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    causal = kw.pop("causal", "off")
+    ql = max(1, int(q_lens.max()) if q_lens.size else 1)
+    w = build(name, q_len=ql, seed=seed, causal="off" if causal == "lastv" else causal, **kw)
+    if causal == "lastv":
+        w = w.replace(causal_offset=CAUSAL_LAST)
+    return w.replace(q_lens=q_lens)
+
+
 CONFIGS = {
     "tiny": tiny,
     "decode_1b": decode_1b,
     "long_ctx": long_ctx,
     "ragged": ragged,
+    "mixed": mixed,
 }
