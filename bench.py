@@ -222,7 +222,7 @@ def main():
                                       causal_offset=w.causal_offset, num_splits=args.splits,
                                       mask_stride_b=msb, mask_stride_q=msq,
                                       heads_per_block=args.heads_per_block)
-    plan = pkv.plan(prob)
+    plan = pkv.plan_varlen(prob, w.total_tokens) if varlen else pkv.plan(prob)
     S = plan.splits
     prob.num_splits = S
     prob.heads_per_block = plan.heads_per_block

@@ -181,6 +181,13 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                      float *ml_part, size_t ml_part_bytes, void *out_bf16,
                      float *out_f32, hipStream_t stream);
 
+/* The launch plan of pkv_paged_decode_varlen for a batch of total_tokens
+ * query tokens (0 .. B * q_len, else PKV_ERR_SHAPE): as pkv_plan, with the
+ * split count and heads per workgroup sized for the rows the tokens fill
+ * rather than for q_len tokens in every sequence.  The workspace of a call is
+ * pkv_workspace_bytes(p, info->splits). */
+int pkv_plan_varlen(const pkv_problem *p, int64_t total_tokens, int num_cus, pkv_plan_info *info);
+
 /* Decode over a batch whose sequences have different numbers of query
  * tokens ("varlen": chunked prefill and single-token decode in one call, as
  * in the AstrAI paged-decode commit notes on prefill and decode kernels over

@@ -33,7 +33,7 @@ PKV_MAX_CONTIGUOUS_KEYS = 1 << 30
 PKV_CAUSAL_LAST = -2
 KV_LAYOUTS = {"blhd": PKV_KV_BLHD, "bhld": PKV_KV_BHLD}
 
-EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_plan_varlen", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
             "pkv_paged_decode_varlen", "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
             "pkv_status_string")
 
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(Problem)
         L.pkv_num_splits.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.pkv_plan.argtypes = [PP, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+        L.pkv_plan_varlen.argtypes = [PP, ctypes.c_int64, ctypes.c_int, ctypes.POINTER(PlanInfo)]
         L.pkv_workspace_bytes.argtypes = [PP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.pkv_workspace_clear.argtypes = [P, ctypes.c_size_t, P]
@@ -108,7 +109,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_device_cus.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
-        for name in ("pkv_num_splits", "pkv_plan", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
+        for name in ("pkv_num_splits", "pkv_plan", "pkv_plan_varlen", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
                      "pkv_paged_decode_varlen", "pkv_contiguous_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
@@ -151,6 +152,14 @@ def plan(problem: Problem, num_cus: int = 0) -> PlanInfo:
     per workgroup, kernel, units, merge path, launches per call)."""
     info = PlanInfo()
     _check(lib().pkv_plan(ctypes.byref(problem), int(num_cus), ctypes.byref(info)), "pkv_plan")
+    return info
+
+
+def plan_varlen(problem: Problem, total_tokens: int, num_cus: int = 0) -> PlanInfo:
+    """pkv_plan_varlen: the launch plan of a varlen call over total_tokens tokens."""
+    info = PlanInfo()
+    _check(lib().pkv_plan_varlen(ctypes.byref(problem), int(total_tokens), num_cus, ctypes.byref(info)),
+           "pkv_plan_varlen")
     return info
 
 
@@ -363,7 +372,7 @@ def paged_decode_varlen(q, k_cache, v_cache, block_table, kv_lens, cu_q_lens, *,
                      num_pages=num_pages, max_pages_per_seq=block_table.shape[1], max_kv_len=max_kv_len,
                      scale=scale, causal_offset=causal_offset, num_splits=num_splits, mask_stride_b=msb,
                      mask_stride_q=msq, heads_per_block=heads_per_block)
-    S = num_splits_for(p)
+    S = num_splits if num_splits > 0 else plan_varlen(p, T).splits
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if S > 1 and (o_part is None or ml_part is None):

@@ -401,18 +401,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   // output row of packed row r of head slot hh of the block, at r * hpb + hh
   __shared__ int64_t rowtab[RP * kMaxHeadsPerBlock];
 
-  // ---- unit decode (XCD-aware): siblings (kv-head group, row block) of one
-  // (b, split) pair get consecutive slots on the same XCD
-  const int x = blockIdx.x;
-  const int xcd = x & 7;
-  const int slot = x >> 3;
-  const int inner_idx = slot % a.inner;
-  const int outer_idx = (slot / a.inner) * 8 + xcd;
-  if (outer_idx >= a.outer) return;
-  int b, s;
-  decode_pair(a, outer_idx, b, s);
-  const int hg = inner_idx / a.nrb;
-  const int rb = inner_idx - hg * a.nrb;
+  Work wk0;
+  if (!work_of(a, wk0)) return;
+  const int b = wk0.b, s = wk0.s, hg = wk0.hg, rb = wk0.rg;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -567,7 +558,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     merge_waves<NW, D>(mlb, ob, HR, wph, ri, d, M, W, vx, vy);
   };
   write_rows<D>(a, s, direct, rowtab, nrows, item, NW * 64);
-  if (a.fused && !direct) fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrows, smem, NW * 64);
+  if (a.fused && !direct) fused_tail<D>(a, wk0.unit, nact, rowtab, nrows, smem, NW * 64);
 }
 
 // Combine (the standalone pkv_combine entry point): each block merges

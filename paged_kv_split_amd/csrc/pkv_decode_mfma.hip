@@ -343,16 +343,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   // output row of packed row rr of head slot hh of the block, at rr * hpb + hh
   __shared__ int64_t rowtab[RW * kMaxHeadsPerBlock];
 
-  const int x = blockIdx.x;
-  const int xcd = x & 7;
-  const int slot = x >> 3;
-  const int inner_idx = slot % a.inner;
-  const int outer_idx = (slot / a.inner) * 8 + xcd;
-  if (outer_idx >= a.outer) return;
-  int b, s;
-  decode_pair(a, outer_idx, b, s);
-  const int hg = inner_idx / a.nrb;
-  const int rg = inner_idx - hg * a.nrb;
+  Work wk0;
+  if (!work_of(a, wk0)) return;
+  const int b = wk0.b, s = wk0.s, hg = wk0.hg, rg = wk0.rg;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -491,7 +484,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     write_rows<D>(a, s, direct, rowtab + 16 * rb * a.hpb, nrows, item, NW * 64);
   }
   if (a.fused && !direct)
-    fused_tail<D>(a, b * a.inner + inner_idx, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
+    fused_tail<D>(a, wk0.unit, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 
 template <int D, int NRB, bool C, bool M, bool U>

@@ -123,10 +123,74 @@ __device__ __forceinline__ float2 load2(const float *p) {  // p 8-byte aligned
 // pairs p, p + 8, ... land on one XCD) a mix of sequences and split
 // positions, so ragged lengths and splits past a sequence's end spread over
 // the XCDs rather than piling onto some.
-__device__ __forceinline__ void decode_pair(const DecodeArgs &a, int p, int &b, int &s) {
-  s = p / a.B;
-  b = p - s * a.B + 3 * s;
-  b %= a.B;
+__device__ __forceinline__ void decode_pair(int p, int n, int &b, int &s) {
+  s = p / n;
+  b = p - s * n + 3 * s;
+  b %= n;
+}
+
+// Compact row blocks of a varlen batch: virtual row block v belongs to the
+// sequence b with V(b) <= v < V(b + 1), V(b) = floor(cu_q[b] * G / rp) + b.
+// V is strictly increasing and V(b + 1) - V(b) >= ceil(n_b * G / rp), the
+// sequence's row blocks, so blocks V(b) .. V(b) + that - 1 are b's and the
+// rest of the range (at most one block) is empty; the batch needs
+// floor(T * G / rp) + B virtual blocks instead of B * ceil(q_len * G / rp).
+__device__ __forceinline__ int vstart(const DecodeArgs &a, int b) {
+  return (int)(((int64_t)a.cu_q[b] * a.G) / a.rp) + b;
+}
+
+// The sequence of virtual row block v and its V(b): a wave-wide search, 64
+// candidates per round of loads (one round up to 64 sequences, two up to
+// 4096).  Every lane of the wave takes part.
+__device__ __forceinline__ int find_seq(const DecodeArgs &a, int v, int &vb) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = a.B;  // V(lo) <= v < V(lo + n) (V(B) taken as infinite)
+  for (;;) {
+    const int stride = (n + 63) >> 6;
+    const int off = lane * stride;
+    const int val = off < n ? vstart(a, lo + off) : INT_MAX;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(val <= v);  // lane 0 always (V(lo) <= v)
+    const int sel = 63 - __builtin_clzll(m);
+    if (stride == 1) {
+      vb = __builtin_amdgcn_readlane(val, sel);
+      return lo + sel;
+    }
+    lo += sel * stride;
+    n = a.B - lo < stride ? a.B - lo : stride;
+  }
+}
+
+// What a split workgroup covers: sequence b, split s, kv-head group hg, row
+// block rg, and the unit (its arrival counter for the in-kernel merge).
+// XCD-aware order: blocks x, x + 8, ... run on one XCD, so the siblings
+// (kv-head group, row block) of one (b, split) pair get consecutive slots
+// there.  False: a padding block past the grid's pairs.  A compact varlen
+// block may lie past its sequence's row blocks (r0 >= its rows): no work.
+struct Work {
+  int b, s, hg, rg, unit;
+};
+
+__device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int slot = x >> 3;
+  const int inner_idx = slot % a.inner;
+  const int outer_idx = (slot / a.inner) * 8 + xcd;
+  if (outer_idx >= a.outer) return false;
+  if (a.nv == 0) {
+    decode_pair(outer_idx, a.B, w.b, w.s);
+    w.hg = inner_idx / a.nrb;
+    w.rg = inner_idx - w.hg * a.nrb;
+    w.unit = w.b * a.inner + inner_idx;
+    return true;
+  }
+  int v, vb;
+  decode_pair(outer_idx, a.nv, v, w.s);
+  w.b = find_seq(a, v, vb);
+  w.hg = inner_idx;
+  w.rg = v - vb;
+  w.unit = v * a.inner + inner_idx;
+  return true;
 }
 
 // Splits of a unit that hold keys: its rows see kmax keys at most.  At least

@@ -107,9 +107,8 @@ constexpr int kMinTilesPerWave = 2;
 // Measured on MI355X for B = 256 lognormal lengths (median 1024, clipped to
 // [32, 8192], 32 rows per kv head, D = 128): 4 splits of 2048 keys in place
 // of one take a call from 425 to 377 us (8 splits of 1024: 403 us).
-int split_cap_keys(const pkv_problem *p) {
-  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  const int cap = 64 * R;
+int split_cap_keys(int rows) {
+  const int cap = 64 * rows;
   return cap > 1024 ? cap : 1024;
 }
 
@@ -136,12 +135,53 @@ int64_t units_of(const pkv_problem *p, int hpb) {
   return (int64_t)p->batch * (p->num_kv_heads / hpb) * row_blocks(p);
 }
 
-int heuristic_splits(const pkv_problem *p, int cus, int hpb) {
-  const int64_t units = units_of(p, hpb);
-  if (units <= 0) return 1;
+// The work the split heuristic sizes the grid for: (sequence, kv-head group,
+// row block) units that hold rows, and packed rows per such unit.  A batch
+// of q_len tokens per sequence (or a varlen batch that has them all): every
+// unit, R rows.  A varlen batch of `tokens` tokens: its row blocks number at most
+// ceil(tokens * G / rp) + B (each sequence may end in a partial block), and
+// the rows spread over them; the other units of the grid exit at once.
+struct Load {
+  int64_t units;
+  int rows;
+};
+
+// Compact row blocks of a varlen batch of `tokens` tokens: floor(tokens * G /
+// rp) + B slots hold every sequence's row blocks (the kernels map a slot to
+// its sequence from cu_q_lens); 0 where that saves nothing over one slot per
+// (sequence, row block) or the batch is not varlen.
+int64_t compact_row_blocks(const pkv_problem *p, int64_t tokens) {
+  if (tokens < 0) return 0;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int rp = pkv::rows_per_block(G * p->q_len);
+  const int64_t nv = tokens * G / rp + p->batch;
+  return nv < (int64_t)p->batch * row_blocks(p) ? nv : 0;
+}
+
+// Units of the grid: (sequence, kv-head group, row block) slots, or
+// (compact row block, kv-head group) slots.
+int64_t grid_units(const pkv_problem *p, int hpb, int64_t tokens) {
+  const int64_t nv = compact_row_blocks(p, tokens);
+  return nv ? nv * (p->num_kv_heads / hpb) : units_of(p, hpb);
+}
+
+Load load_of(const pkv_problem *p, int hpb, int64_t tokens) {
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int R = G * p->q_len;
+  const int64_t nv = compact_row_blocks(p, tokens);
+  if (nv == 0) return Load{units_of(p, hpb), R};
+  int64_t rows = ceil_div(tokens * G, nv);
+  if (rows < 1) rows = 1;
+  return Load{nv * (p->num_kv_heads / hpb), (int)(rows < R ? rows : R)};
+}
+
+int heuristic_splits(const pkv_problem *p, int cus, int hpb, int64_t tokens) {
+  const Load ld = load_of(p, hpb, tokens);
+  const int64_t units = ld.units;
+  if (units <= 0 || tokens == 0) return 1;
   const int64_t target = (int64_t)cus * blocks_per_cu(p);
   if (units >= target) {
-    const int64_t s = ceil_div(max_len_of(p), split_cap_keys(p));
+    const int64_t s = ceil_div(max_len_of(p), split_cap_keys(ld.rows));
     return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
   }
   const int T = pkv::tile_keys(p->head_dim);
@@ -174,10 +214,10 @@ int max_heads_per_block(const pkv_problem *p) {
   return p->head_dim <= 128 ? pkv::kMaxHeadsPerBlock : 1;
 }
 
-int heuristic_hpb(const pkv_problem *p, int cus) {
+int heuristic_hpb(const pkv_problem *p, int cus, int64_t tokens) {
   for (int hpb = max_heads_per_block(p); hpb > 1; hpb /= 2) {
     if (p->num_kv_heads % hpb) continue;
-    const int s = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, hpb);
+    const int s = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, hpb, tokens);
     if (s >= 2 && s <= kMaxGroupedSplits) return hpb;
   }
   return 1;
@@ -191,11 +231,12 @@ struct Plan {
   bool fused;     // pkv_paged_decode merges the splits inside the split kernel
 };
 
-Plan make_plan(const pkv_problem *p, int cus) {
+// tokens: -1 for q_len tokens per sequence, else a varlen batch's total.
+Plan make_plan(const pkv_problem *p, int cus, int64_t tokens = -1) {
   Plan pl;
-  pl.hpb = p->heads_per_block > 0 ? p->heads_per_block : heuristic_hpb(p, cus);
-  pl.S = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, pl.hpb);
-  pl.units = units_of(p, pl.hpb);
+  pl.hpb = p->heads_per_block > 0 ? p->heads_per_block : heuristic_hpb(p, cus, tokens);
+  pl.S = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, pl.hpb, tokens);
+  pl.units = grid_units(p, pl.hpb, tokens);
   // In-kernel merge (a counter for every unit) whenever the counters fit the
   // workspace head.  Splits past a sequence's end exit at once and a unit
   // with one split holding keys writes its output directly, so only units
@@ -248,15 +289,18 @@ int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out) {
   return PKV_OK;
 }
 
-int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info) {
+namespace {
+
+int plan_query(const pkv_problem *p, int64_t tokens, int num_cus, pkv_plan_info *info) {
   if (!info) return PKV_ERR_NULL;
   int rc = check_problem(p);
   if (rc) return rc;
+  if (tokens > (int64_t)p->batch * p->q_len) return PKV_ERR_SHAPE;
   if (num_cus <= 0) {
     rc = query_cus(&num_cus);
     if (rc) return rc;
   }
-  const Plan pl = make_plan(p, num_cus);
+  const Plan pl = make_plan(p, num_cus, tokens);
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
   *info = pkv_plan_info{};
   info->splits = pl.S;
@@ -268,6 +312,17 @@ int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info) {
   info->merge_in_kernel = pl.fused ? 1 : 0;
   info->kernels = (pl.S > 1 && !pl.fused && p->batch > 0) ? 2 : (p->batch > 0 ? 1 : 0);
   return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info) {
+  return plan_query(p, -1, num_cus, info);
+}
+
+int pkv_plan_varlen(const pkv_problem *p, int64_t total_tokens, int num_cus, pkv_plan_info *info) {
+  if (total_tokens < 0) return PKV_ERR_SHAPE;
+  return plan_query(p, total_tokens, num_cus, info);
 }
 
 int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
@@ -334,7 +389,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   if (S == 0) {
     const int rc = query_cus(&cus);
     if (rc) return rc;
-    S = make_plan(p, cus).S;
+    S = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1).S;
   }
   // pkv_paged_decode with several splits: ml_part = counter head + (m, l)
   const bool split_ws = S > 1 && !partials_only;
@@ -354,9 +409,10 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
       const int rc = query_cus(&cus);
       if (rc) return rc;
     }
-    pl = make_plan(p, cus);
+    pl = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1);
   }
-  pl.units = units_of(p, pl.hpb);
+  const int64_t nv = compact_row_blocks(p, qs.cu_q ? qs.total_tokens : -1);
+  pl.units = grid_units(p, pl.hpb, qs.cu_q ? qs.total_tokens : -1);
 
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
@@ -411,8 +467,10 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->lhpb = ilog2(pl.hpb);
   a->causal_offset = p->causal_offset;
   a->scale_log2 = p->scale * 1.4426950408889634f;
-  const int64_t outer = (int64_t)p->batch * S;
-  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * a->nrb;
+  a->nv = (int32_t)nv;
+  a->rp = rp;
+  const int64_t outer = (nv ? nv : (int64_t)p->batch) * S;
+  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * (nv ? 1 : a->nrb);
   if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
   // the combine kernel's grid (several splits without the in-kernel merge)
   const int64_t rows_all = (int64_t)p->batch * p->q_len * p->num_q_heads;

@@ -346,3 +346,24 @@ def test_varlen_decode_checks():
     assert call_varlen(base_problem(num_splits=1, causal_offset=-3)) == pkv.PKV_ERR_SHAPE
     assert call_varlen(base_problem(num_splits=4, q_len=4)) == pkv.PKV_ERR_WORKSPACE
     assert pkv.PKV_CAUSAL_LAST == -2
+
+
+def test_plan_varlen():
+    """pkv_plan_varlen sizes the grid for the rows the tokens fill: a batch of
+    32 sequences bounded at 64 tokens (G = 4, 32-row blocks) that holds 273
+    tokens has about 66 row blocks with rows, so its sequences are split
+    (8 splits of about 1024 keys at 8192 keys); holding every token, it
+    plans as pkv_plan does."""
+    p = base_problem(batch=32, q_len=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=32,
+                     num_pages=9000, max_pages_per_seq=256, max_kv_len=8192, causal_offset=pkv.PKV_CAUSAL_LAST)
+    full = pkv.plan(p, 256)
+    assert (full.splits, full.matrix_core, full.rows_per_block) == (1, 1, 32)
+    same = pkv.plan_varlen(p, 32 * 64, 256)
+    assert [getattr(same, f) for f, _ in same._fields_] == [getattr(full, f) for f, _ in full._fields_]
+    mixed = pkv.plan_varlen(p, 273, 256)
+    assert mixed.splits == 8 and mixed.merge_in_kernel == 1 and mixed.kernels == 1
+    assert pkv.plan_varlen(p, 0, 256).splits == 1
+    with pytest.raises(pkv.PkvError):
+        pkv.plan_varlen(p, 32 * 64 + 1, 256)
+    with pytest.raises(pkv.PkvError):
+        pkv.plan_varlen(p, -1, 256)

@@ -109,3 +109,46 @@ def test_no_tokens_at_all_writes_nothing():
     out = pkv.paged_decode_varlen(q, k, k, bt, kl, cu, max_q_len=1, scale=w.scale)
     torch.cuda.synchronize()
     assert out.shape == (0, 4, 64)
+
+
+def _plan(w, splits=0, hpb=0):
+    import paged_kv_split_amd as pkv
+    from gpu_util import problem
+    return pkv.plan_varlen(problem(w, splits, hpb), w.total_tokens)
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_compact_row_blocks_over_64_sequences(splits):
+    """150 sequences (the row-block search takes two rounds), most with one
+    token: the grid holds floor(T * G / 32) + B row-block slots, not
+    B * ceil(q_len * G / 32)."""
+    import torch
+    g = torch.Generator().manual_seed(3500)
+    B = 150
+    q_lens = torch.where(torch.rand(B, generator=g) < 0.2, torch.randint(0, 17, (B,), generator=g),
+                         torch.ones(B, dtype=torch.int64)).tolist()
+    lens = torch.randint(1, 600, (B,), generator=g).tolist()
+    lens = [max(L, n) for L, n in zip(lens, q_lens)]
+    w = workloads.varlen("compact150", q_lens=q_lens, kv_lens=lens, B=B, Hq=16, Hkv=2, D=64, page_size=16,
+                         seed=3500, causal="lastv")
+    pl = _plan(w, splits)
+    assert pl.units == (w.total_tokens * 8 // 32 + B) * 2 // pl.heads_per_block
+    compare_varlen(w, num_splits=splits)
+
+
+def test_compact_row_blocks_with_separate_combine():
+    """More compact units than arrival counters: the splits go through the
+    combine kernel (empty splits leave (m, l) = (-inf, 0) for it)."""
+    import torch
+    g = torch.Generator().manual_seed(3600)
+    B = 600
+    q_lens = torch.where(torch.rand(B, generator=g) < 0.1, torch.randint(2, 9, (B,), generator=g),
+                         torch.ones(B, dtype=torch.int64)).tolist()
+    lens = torch.randint(8, 200, (B,), generator=g).tolist()
+    w = workloads.varlen("compact600", q_lens=q_lens, kv_lens=lens, B=B, Hq=64, Hkv=8, D=128, page_size=32,
+                         seed=3600, causal="lastv")
+    pl = _plan(w, 2, 1)
+    nv = w.total_tokens * 8 // 32 + B
+    assert nv < B * 2 and pl.units == nv * 8
+    assert pl.merge_in_kernel == 0 and pl.kernels == 2
+    compare_varlen(w, num_splits=2, heads_per_block=1)
