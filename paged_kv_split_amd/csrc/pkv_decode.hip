@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   __shared__ int64_t rowtab[RP * kMaxHeadsPerBlock];
 
   Work wk0;
-  if (!work_of(a, wk0)) return;
+  if (!work_of<CAUSAL>(a, wk0)) return;
   const int b = wk0.b, s = wk0.s, hg = wk0.hg, rb = wk0.rg;
 
   const int lane = threadIdx.x & 63;
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   const int g = hg * a.hpb + hw;
 
   const int r0 = rb * RP;
-  const int L = a.kv_lens[b];
-  const SeqRows sr = seq_rows<CAUSAL>(a, b, L);
+  const int L = wk0.L;
+  const SeqRows sr = wk0.sr;
   if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
 
   // per-row visible key limit and the block's key range

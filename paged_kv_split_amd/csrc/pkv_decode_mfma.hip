@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   __shared__ int64_t rowtab[RW * kMaxHeadsPerBlock];
 
   Work wk0;
-  if (!work_of(a, wk0)) return;
+  if (!work_of<CAUSAL>(a, wk0)) return;
   const int b = wk0.b, s = wk0.s, hg = wk0.hg, rg = wk0.rg;
 
   const int lane = threadIdx.x & 63;
@@ -357,8 +357,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   const int q = lane >> 4;
   const int r0 = rg * RW;
 
-  const int kvlen = a.kv_lens[b];
-  const SeqRows sr = seq_rows<CAUSAL>(a, b, kvlen);
+  const int kvlen = wk0.L;
+  const SeqRows sr = wk0.sr;
   if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
   int lim[NRB];
 #pragma unroll

@@ -129,70 +129,6 @@ __device__ __forceinline__ void decode_pair(int p, int n, int &b, int &s) {
   b %= n;
 }
 
-// Compact row blocks of a varlen batch: virtual row block v belongs to the
-// sequence b with V(b) <= v < V(b + 1), V(b) = floor(cu_q[b] * G / rp) + b.
-// V is strictly increasing and V(b + 1) - V(b) >= ceil(n_b * G / rp), the
-// sequence's row blocks, so blocks V(b) .. V(b) + that - 1 are b's and the
-// rest of the range (at most one block) is empty; the batch needs
-// floor(T * G / rp) + B virtual blocks instead of B * ceil(q_len * G / rp).
-__device__ __forceinline__ int vstart(const DecodeArgs &a, int b) {
-  return (int)(((int64_t)a.cu_q[b] * a.G) / a.rp) + b;
-}
-
-// The sequence of virtual row block v and its V(b): a wave-wide search, 64
-// candidates per round of loads (one round up to 64 sequences, two up to
-// 4096).  Every lane of the wave takes part.
-__device__ __forceinline__ int find_seq(const DecodeArgs &a, int v, int &vb) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, n = a.B;  // V(lo) <= v < V(lo + n) (V(B) taken as infinite)
-  for (;;) {
-    const int stride = (n + 63) >> 6;
-    const int off = lane * stride;
-    const int val = off < n ? vstart(a, lo + off) : INT_MAX;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(val <= v);  // lane 0 always (V(lo) <= v)
-    const int sel = 63 - __builtin_clzll(m);
-    if (stride == 1) {
-      vb = __builtin_amdgcn_readlane(val, sel);
-      return lo + sel;
-    }
-    lo += sel * stride;
-    n = a.B - lo < stride ? a.B - lo : stride;
-  }
-}
-
-// What a split workgroup covers: sequence b, split s, kv-head group hg, row
-// block rg, and the unit (its arrival counter for the in-kernel merge).
-// XCD-aware order: blocks x, x + 8, ... run on one XCD, so the siblings
-// (kv-head group, row block) of one (b, split) pair get consecutive slots
-// there.  False: a padding block past the grid's pairs.  A compact varlen
-// block may lie past its sequence's row blocks (r0 >= its rows): no work.
-struct Work {
-  int b, s, hg, rg, unit;
-};
-
-__device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
-  const int x = blockIdx.x;
-  const int xcd = x & 7;
-  const int slot = x >> 3;
-  const int inner_idx = slot % a.inner;
-  const int outer_idx = (slot / a.inner) * 8 + xcd;
-  if (outer_idx >= a.outer) return false;
-  if (a.nv == 0) {
-    decode_pair(outer_idx, a.B, w.b, w.s);
-    w.hg = inner_idx / a.nrb;
-    w.rg = inner_idx - w.hg * a.nrb;
-    w.unit = w.b * a.inner + inner_idx;
-    return true;
-  }
-  int v, vb;
-  decode_pair(outer_idx, a.nv, v, w.s);
-  w.b = find_seq(a, v, vb);
-  w.hg = inner_idx;
-  w.rg = v - vb;
-  w.unit = v * a.inner + inner_idx;
-  return true;
-}
-
 // Splits of a unit that hold keys: its rows see kmax keys at most.  At least
 // one, so that a unit without keys still writes its (zero) output.
 __device__ __forceinline__ int active_splits(const DecodeArgs &a, int kmax) {
@@ -219,12 +155,13 @@ struct SeqRows {
   bool causal;
 };
 
+// From the sequence's entries: kv length L, cu_q[b], cu_q[b + 1] (varlen)
+// and causal_offsets[b] (when given).
 template <bool CAUSAL>
-__device__ __forceinline__ SeqRows seq_rows(const DecodeArgs &a, int b, int L) {
+__device__ __forceinline__ SeqRows seq_rows_of(const DecodeArgs &a, int b, int L, int c0, int c1, int co) {
   SeqRows r;
   if (a.cu_q) {
-    const int c0 = a.cu_q[b];
-    int n = a.cu_q[b + 1] - c0;
+    int n = c1 - c0;
     n = n < 0 ? 0 : (n > a.q_len ? a.q_len : n);
     r.tok0 = c0;
     r.R = n * a.G;
@@ -236,7 +173,7 @@ __device__ __forceinline__ SeqRows seq_rows(const DecodeArgs &a, int b, int L) {
   r.causal = false;
   if constexpr (CAUSAL) {
     if (a.causal_offsets) {
-      r.cofs = a.causal_offsets[b];
+      r.cofs = co;
       r.causal = r.cofs >= 0;
     } else if (a.causal_offset == kCausalLast) {  // tokens at positions L - n .. L - 1
       r.cofs = L - r.R / a.G;
@@ -249,6 +186,14 @@ __device__ __forceinline__ SeqRows seq_rows(const DecodeArgs &a, int b, int L) {
   return r;
 }
 
+template <bool CAUSAL>
+__device__ __forceinline__ SeqRows seq_rows(const DecodeArgs &a, int b, int L) {
+  const int c0 = a.cu_q ? a.cu_q[b] : 0;
+  const int c1 = a.cu_q ? a.cu_q[b + 1] : 0;
+  const int co = (CAUSAL && a.causal_offsets) ? a.causal_offsets[b] : -1;
+  return seq_rows_of<CAUSAL>(a, b, L, c0, c1, co);
+}
+
 // Keys packed row rr of the sequence may see: none past its rows; else its L
 // keys, or with a causal offset those up to its token's position.
 __device__ __forceinline__ int row_keys(const DecodeArgs &a, const SeqRows &sr, int L, int rr) {
@@ -259,6 +204,144 @@ __device__ __forceinline__ int row_keys(const DecodeArgs &a, const SeqRows &sr, 
     if (cl < lr) lr = cl < 0 ? 0 : (int)cl;
   }
   return lr;
+}
+
+// ---- the schedule: which (sequence, split, kv-head group, row block) a
+// split workgroup covers ---------------------------------------------------
+struct Work {
+  int b, s, hg, rg;  // sequence, split, kv-head group, row block
+  int unit;          // (sequence, kv-head group, row block) unit: its arrival counter
+  int L;             // the sequence's kv length
+  SeqRows sr;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    x += lane >= d ? y : 0;
+  }
+  return x;
+}
+
+constexpr int kExactPerLane = 4;  // sequences per lane of the exact schedule
+
+// Exact schedule (up to 64 * kExactPerLane = 256 sequences): the work items are
+// the (sequence, split, row block) triples that hold work -- row blocks with
+// rows, and with the in-kernel merge or a single split only the splits up to
+// the sequence's last key -- numbered sequence by sequence (split-major
+// within a sequence, so the row blocks that read one K/V chunk are
+// neighbours).  Every workgroup counts the items of all sequences (each lane
+// a run of kExactPerLane at most, one round of loads, then a wave-wide prefix
+// sum), so it knows their total N; XCD x (blocks x, x + 8, ...) takes items
+// x * ceil(N / 8) onward, in order, and the blocks past them -- the grid is
+// sized for a host-side bound -- exit at the end of the dispatch.
+template <bool CAUSAL>
+__device__ __forceinline__ bool work_exact(const DecodeArgs &a, int xcd, int slot, Work &w) {
+  const int lane = threadIdx.x & 63;
+  const int k = (a.B + 63) >> 6;
+  const int b0 = lane * k;
+  int Lq[kExactPerLane], c0q[kExactPerLane], c1q[kExactPerLane], coq[kExactPerLane];
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    const int b = b0 + j;
+    const bool ok = j < k && b < a.B;
+    Lq[j] = ok ? a.kv_lens[b] : 0;
+    c0q[j] = ok && a.cu_q ? a.cu_q[b] : 0;
+    c1q[j] = ok && a.cu_q ? a.cu_q[b + 1] : 0;
+    coq[j] = ok && CAUSAL && a.causal_offsets ? a.causal_offsets[b] : -1;
+  }
+  const bool trimmed = a.fused || a.S == 1;  // splits past the last key get no item
+  int items[kExactPerLane], rbs[kExactPerLane];
+  int isum = 0, usum = 0;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    items[j] = 0;
+    rbs[j] = 0;
+    if (j < k && b0 + j < a.B) {
+      const SeqRows sr = seq_rows_of<CAUSAL>(a, b0 + j, Lq[j], c0q[j], c1q[j], coq[j]);
+      rbs[j] = (sr.R + a.rp - 1) / a.rp;
+      const int ns = trimmed ? active_splits(a, row_keys(a, sr, Lq[j], sr.R - 1)) : a.S;
+      items[j] = rbs[j] * ns;
+    }
+    isum += items[j];
+    usum += rbs[j];
+  }
+  const int iscan = wave_scan(isum);
+  const int uscan = wave_scan(usum);
+  const int n_items = __builtin_amdgcn_readlane(iscan, 63);
+  const int per = (n_items + 7) >> 3;
+  const int kk = slot / a.inner;
+  if (kk >= per) return false;
+  const int v = xcd * per + kk;
+  if (v >= n_items) return false;
+  // the lane whose run holds item v, then the sequence within the run
+  const uint64_t m = __builtin_amdgcn_ballot_w64(iscan > v);
+  const int sel = __builtin_ctzll(m);
+  int ibase = __builtin_amdgcn_readlane(iscan - isum, sel);
+  int ubase = __builtin_amdgcn_readlane(uscan - usum, sel);
+  bool found = false;
+  int jsel = 0, nitem = 0, nrb = 1;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    const int c = __builtin_amdgcn_readlane(items[j], sel);
+    const int r = __builtin_amdgcn_readlane(rbs[j], sel);
+    if (!found) {
+      if (v < ibase + c) {
+        found = true;
+        jsel = j;
+        nitem = c;
+        nrb = r;
+      } else {
+        ibase += c;
+        ubase += r;
+      }
+    }
+  }
+  (void)nitem;
+  int L = 0, c0 = 0, c1 = 0, co = -1;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    if (j == jsel) {
+      L = __builtin_amdgcn_readlane(Lq[j], sel);
+      c0 = __builtin_amdgcn_readlane(c0q[j], sel);
+      c1 = __builtin_amdgcn_readlane(c1q[j], sel);
+      co = __builtin_amdgcn_readlane(coq[j], sel);
+    }
+  }
+  const int jj = v - ibase;
+  w.b = sel * k + jsel;
+  w.s = jj / nrb;
+  w.rg = jj - w.s * nrb;
+  w.hg = slot - kk * a.inner;
+  w.unit = (ubase + w.rg) * a.inner + w.hg;
+  w.L = L;
+  w.sr = seq_rows_of<CAUSAL>(a, w.b, L, c0, c1, co);
+  return true;
+}
+
+// The schedule of a workgroup.  Exact (above) when a.exact; otherwise one
+// block per (sequence, split) pair and unit slot (kv-head group, row block),
+// the pairs in split-major order (decode_pair), whose empty blocks exit.
+// XCD-aware: blocks x, x + 8, ... run on one XCD.  False: no work.
+template <bool CAUSAL>
+__device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
+  const int x = blockIdx.x;
+  const int xcd = x & 7;
+  const int slot = x >> 3;
+  if (a.exact) return work_exact<CAUSAL>(a, xcd, slot, w);
+  const int inner_idx = slot % a.inner;
+  const int outer_idx = (slot / a.inner) * 8 + xcd;
+  if (outer_idx >= a.outer) return false;
+  decode_pair(outer_idx, a.B, w.b, w.s);
+  w.hg = inner_idx / a.nrb;
+  w.rg = inner_idx - w.hg * a.nrb;
+  w.unit = w.b * a.inner + inner_idx;
+  w.L = a.kv_lens[w.b];
+  w.sr = seq_rows<CAUSAL>(a, w.b, w.L);
+  return true;
 }
 
 // Output row (token, query head) of packed row rr (= i * G + k) of kv head g

@@ -146,33 +146,44 @@ struct Load {
   int rows;
 };
 
-// Compact row blocks of a varlen batch of `tokens` tokens: floor(tokens * G /
-// rp) + B slots hold every sequence's row blocks (the kernels map a slot to
-// its sequence from cu_q_lens); 0 where that saves nothing over one slot per
-// (sequence, row block) or the batch is not varlen.
-int64_t compact_row_blocks(const pkv_problem *p, int64_t tokens) {
-  if (tokens < 0) return 0;
+// Varlen batches up to this size take the exact schedule (every workgroup
+// counts the work items of the whole batch, each lane a run of up to 4
+// sequences, which keeps the kernels' register counts unchanged); other
+// calls get one block per (sequence, split, row block).  Measured on MI355X:
+// a batch of 32 sequences, a quarter with prefill chunks of up to 64 tokens,
+// 240 -> 110 us.  For fixed-length batches the per-block split-major order is
+// as fast or faster (B = 256 lognormal lengths: 382 against 373 us at 4
+// splits, 401 against 433 us at 8; the 1B decode shape: 10.0 against 11.0 us),
+// so they keep it.
+constexpr int kExactMaxBatch = 64 * 4;
+
+// Row-block slots the grid holds: B * ceil(R / rp); a varlen batch of
+// `tokens` tokens under the exact schedule at most floor(tokens * G / rp) + B
+// (sequence b has ceil(n_b * G / rp) <= floor(n_b * G / rp) + 1 row blocks).
+int64_t row_block_slots(const pkv_problem *p, int64_t tokens) {
+  const int64_t all = (int64_t)p->batch * row_blocks(p);
+  if (tokens < 0 || p->batch > kExactMaxBatch) return all;
   const int G = p->num_q_heads / p->num_kv_heads;
   const int rp = pkv::rows_per_block(G * p->q_len);
   const int64_t nv = tokens * G / rp + p->batch;
-  return nv < (int64_t)p->batch * row_blocks(p) ? nv : 0;
+  return nv < all ? nv : all;
 }
 
-// Units of the grid: (sequence, kv-head group, row block) slots, or
-// (compact row block, kv-head group) slots.
+// Units of the grid: (sequence, kv-head group, row block) slots.
 int64_t grid_units(const pkv_problem *p, int hpb, int64_t tokens) {
-  const int64_t nv = compact_row_blocks(p, tokens);
-  return nv ? nv * (p->num_kv_heads / hpb) : units_of(p, hpb);
+  return row_block_slots(p, tokens) * (p->num_kv_heads / hpb);
 }
 
 Load load_of(const pkv_problem *p, int hpb, int64_t tokens) {
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
-  const int64_t nv = compact_row_blocks(p, tokens);
-  if (nv == 0) return Load{units_of(p, hpb), R};
-  int64_t rows = ceil_div(tokens * G, nv);
+  if (tokens < 0 || tokens >= (int64_t)p->batch * p->q_len) return Load{units_of(p, hpb), R};
+  int64_t rb = ceil_div(tokens * G, pkv::rows_per_block(R)) + p->batch;
+  const int64_t all = (int64_t)p->batch * row_blocks(p);
+  if (rb > all) rb = all;
+  int64_t rows = ceil_div(tokens * G, rb);
   if (rows < 1) rows = 1;
-  return Load{nv * (p->num_kv_heads / hpb), (int)(rows < R ? rows : R)};
+  return Load{rb * (p->num_kv_heads / hpb), (int)(rows < R ? rows : R)};
 }
 
 int heuristic_splits(const pkv_problem *p, int cus, int hpb, int64_t tokens) {
@@ -411,8 +422,9 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
     }
     pl = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1);
   }
-  const int64_t nv = compact_row_blocks(p, qs.cu_q ? qs.total_tokens : -1);
-  pl.units = grid_units(p, pl.hpb, qs.cu_q ? qs.total_tokens : -1);
+  const int64_t tokens = qs.cu_q ? qs.total_tokens : -1;
+  const bool exact = tokens >= 0 && p->batch <= kExactMaxBatch;
+  pl.units = grid_units(p, pl.hpb, tokens);
 
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
@@ -467,10 +479,10 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->lhpb = ilog2(pl.hpb);
   a->causal_offset = p->causal_offset;
   a->scale_log2 = p->scale * 1.4426950408889634f;
-  a->nv = (int32_t)nv;
+  a->exact = exact ? 1 : 0;
   a->rp = rp;
-  const int64_t outer = (nv ? nv : (int64_t)p->batch) * S;
-  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * (nv ? 1 : a->nrb);
+  const int64_t outer = (exact ? row_block_slots(p, tokens) : (int64_t)p->batch) * S;
+  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * (exact ? 1 : a->nrb);
   if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
   // the combine kernel's grid (several splits without the in-kernel merge)
   const int64_t rows_all = (int64_t)p->batch * p->q_len * p->num_q_heads;

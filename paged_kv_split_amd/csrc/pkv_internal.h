@@ -36,10 +36,10 @@ struct DecodeArgs {
   int32_t hpb, lhpb;              // kv heads per workgroup (1, 2 or 4) and its log2
   int32_t causal_offset;          // -1 off, kCausalLast, >= 0 (overridden by causal_offsets)
   float scale_log2;               // scale * log2(e)
-  int32_t outer;                  // B * S (nv * S with compact row blocks)
-  int32_t inner;                  // (Hkv / hpb) * nrb: unit (kv-head group, row block) slots per (b, split);
-                                  // Hkv / hpb with compact row blocks
-  int32_t nv;                     // varlen: compact row blocks (0 = one slot per (b, row block))
+  int32_t outer;                  // B * S pairs (sequence, split); exact schedule: a bound on the items
+  int32_t inner;                  // (Hkv / hpb) * nrb unit slots (kv-head group, row block) per pair;
+                                  // exact schedule: Hkv / hpb kv-head groups per item
+  int32_t exact;                  // 1: exact schedule (B <= 64 * kExactPerLane)
   int32_t rp;                     // packed rows per row block
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)

@@ -136,19 +136,37 @@ def test_compact_row_blocks_over_64_sequences(splits):
     compare_varlen(w, num_splits=splits)
 
 
-def test_compact_row_blocks_with_separate_combine():
-    """More compact units than arrival counters: the splits go through the
-    combine kernel (empty splits leave (m, l) = (-inf, 0) for it)."""
+def test_large_varlen_batch_with_separate_combine():
+    """600 sequences (past the exact schedule's 256: one slot per (sequence,
+    row block)) and more units than arrival counters: the splits go through
+    the combine kernel, empty row blocks exit."""
     import torch
     g = torch.Generator().manual_seed(3600)
     B = 600
     q_lens = torch.where(torch.rand(B, generator=g) < 0.1, torch.randint(2, 9, (B,), generator=g),
                          torch.ones(B, dtype=torch.int64)).tolist()
     lens = torch.randint(8, 200, (B,), generator=g).tolist()
-    w = workloads.varlen("compact600", q_lens=q_lens, kv_lens=lens, B=B, Hq=64, Hkv=8, D=128, page_size=32,
+    w = workloads.varlen("varlen600", q_lens=q_lens, kv_lens=lens, B=B, Hq=64, Hkv=8, D=128, page_size=32,
                          seed=3600, causal="lastv")
     pl = _plan(w, 2, 1)
-    nv = w.total_tokens * 8 // 32 + B
-    assert nv < B * 2 and pl.units == nv * 8
+    assert pl.units == B * 2 * 8
     assert pl.merge_in_kernel == 0 and pl.kernels == 2
     compare_varlen(w, num_splits=2, heads_per_block=1)
+
+
+def test_exact_schedule_with_separate_combine():
+    """256 sequences (the exact schedule) with more units than arrival
+    counters: every split of every row block gets a workgroup, and those
+    past a row block's keys leave empty partials for the combine kernel."""
+    import torch
+    g = torch.Generator().manual_seed(3700)
+    B = 256
+    q_lens = torch.randint(0, 13, (B,), generator=g).tolist()
+    lens = torch.randint(1, 100, (B,), generator=g).tolist()
+    w = workloads.varlen("exact256", q_lens=q_lens, kv_lens=lens, B=B, Hq=128, Hkv=16, D=64, page_size=16,
+                         seed=3700, causal="lastv")
+    pl = _plan(w, 3, 1)
+    nv = w.total_tokens * 8 // 32 + B
+    assert nv < B * 3 and pl.units == nv * 16
+    assert pl.merge_in_kernel == 0 and pl.kernels == 2
+    compare_varlen(w, num_splits=3, heads_per_block=1)
