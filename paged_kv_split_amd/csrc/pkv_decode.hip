@@ -584,8 +584,7 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, int64_t n) {
 
 template <int D, int RP, bool C, bool M, bool U>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
-  const int64_t outer_pad = ((int64_t)a.outer + 7) / 8 * 8;
-  const int64_t grid = outer_pad * a.inner;
+  const int64_t grid = split_grid(a);
   hipLaunchKernelGGL((split_decode_valu<D, RP, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
                      stream, a);
   return hipGetLastError();

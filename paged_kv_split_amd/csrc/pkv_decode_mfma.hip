@@ -489,8 +489,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
 
 template <int D, int NRB, bool C, bool M, bool U>
 hipError_t mlaunch_t(const DecodeArgs &a, hipStream_t stream) {
-  const int64_t outer_pad = ((int64_t)a.outer + 7) / 8 * 8;
-  const int64_t grid = outer_pad * a.inner;
+  const int64_t grid = split_grid(a);
   hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
                      stream, a);
   return hipGetLastError();

@@ -325,16 +325,30 @@ __device__ __forceinline__ bool work_exact(const DecodeArgs &a, int xcd, int slo
 // The schedule of a workgroup.  Exact (above) when a.exact; otherwise one
 // block per (sequence, split) pair and unit slot (kv-head group, row block),
 // the pairs in split-major order (decode_pair), whose empty blocks exit.
-// XCD-aware: blocks x, x + 8, ... run on one XCD.  False: no work.
+// XCD-aware: blocks x, x + 8, ... run on one XCD.  With 8 pairs or more,
+// pair p runs on XCD p mod 8 with all its unit slots back to back; with
+// fewer (a prefill-shaped call: few sequences, many row blocks) XCD x takes
+// the x-th eighth of the (pair, slot) list, so every XCD has work.  False:
+// no work.
 template <bool CAUSAL>
 __device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int slot = x >> 3;
   if (a.exact) return work_exact<CAUSAL>(a, xcd, slot, w);
-  const int inner_idx = slot % a.inner;
-  const int outer_idx = (slot / a.inner) * 8 + xcd;
-  if (outer_idx >= a.outer) return false;
+  int inner_idx, outer_idx;
+  if (a.outer >= 8) {
+    inner_idx = slot % a.inner;
+    outer_idx = (slot / a.inner) * 8 + xcd;
+    if (outer_idx >= a.outer) return false;
+  } else {
+    const int total = a.outer * a.inner;
+    const int per = (total + 7) >> 3;
+    const int i = xcd * per + slot;
+    if (slot >= per || i >= total) return false;
+    outer_idx = i / a.inner;
+    inner_idx = i - outer_idx * a.inner;
+  }
   decode_pair(outer_idx, a.B, w.b, w.s);
   w.hg = inner_idx / a.nrb;
   w.rg = inner_idx - w.hg * a.nrb;

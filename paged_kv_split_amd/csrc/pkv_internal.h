@@ -68,6 +68,13 @@ constexpr int kWavesPerBlock = 4;  // waves per split workgroup
 constexpr int kCausalLast = -2;    // causal_offset: the query tokens are the sequence's last keys
 constexpr int kMaxHeadsPerBlock = 4;  // kv heads one split workgroup may cover (one wave or more each)
 
+// Blocks of a split-kernel grid: 8 XCD queues of equal length holding every
+// (pair, unit slot), or (exact schedule) the item bound times the groups.
+inline int64_t split_grid(const DecodeArgs &a) {
+  if (a.outer < 8 && !a.exact) return ((int64_t)a.outer * a.inner + 7) / 8 * 8;
+  return ((int64_t)a.outer + 7) / 8 * 8 * a.inner;
+}
+
 // Launchers (return a hipError_t value).
 int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
                  bool has_mask, hipStream_t stream);
