@@ -121,8 +121,11 @@ typedef struct pkv_plan_info {
   int32_t splits;           /* key splits per sequence */
   int32_t heads_per_block;  /* kv heads per split workgroup (1, 2 or 4) */
   int32_t rows_per_block;   /* packed query rows (G * q_len) per kv head per workgroup:
-                               1 or 2 (vector kernel), 16 or 32 (matrix-core kernel) */
-  int32_t matrix_core;      /* 1: the matrix-core split kernel; 0: the vector one */
+                               1 or 2 (vector kernel), 16 or 32 (matrix-core kernel),
+                               128 (prefill-shaped matrix-core kernel: from 512 rows on at
+                               D <= 128 with one kv head per workgroup, four waves of 32
+                               rows sharing each K/V tile) */
+  int32_t matrix_core;      /* 1: a matrix-core split kernel; 0: the vector one */
   int64_t units;            /* (sequence, kv-head group, row block) units */
   int64_t workgroups;       /* split-kernel workgroups: units * splits */
   int32_t merge_in_kernel;  /* 1: the split kernel merges the splits itself */

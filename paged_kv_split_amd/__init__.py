@@ -477,7 +477,10 @@ def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
 
 def kernel_family(problem: Problem) -> str:
     """Which split kernel serves the problem (pkv_plan)."""
-    return "split_decode_mfma" if plan(problem).matrix_core else "split_decode_valu"
+    pl = plan(problem)
+    if pl.rows_per_block == 128:
+        return "split_prefill_mfma"
+    return "split_decode_mfma" if pl.matrix_core else "split_decode_valu"
 
 
 def num_splits_for(problem: Problem) -> int:

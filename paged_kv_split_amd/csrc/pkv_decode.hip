@@ -46,9 +46,10 @@
 
 namespace pkv {
 
-int rows_per_block(int R) {
+int rows_per_block(int R, int head_dim, int forced_hpb) {
   if (R <= 1) return 1;
   if (R <= 2) return 2;
+  if (use_prefill(R, head_dim, forced_hpb)) return kPrefillRows;
   return R <= 16 ? 16 : 32;
 }
 

@@ -487,6 +487,267 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     fused_tail<D>(a, wk0.unit, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 
+// ---- prefill-shaped workgroup ----------------------------------------------
+// Four waves of 32 rows each (128 packed rows of one kv head) over the same
+// keys.  A shared tile of 64 keys is four 16-key subtiles, wave w fetching
+// subtile w (the same loads and swizzled LDS layout as above); every wave
+// then computes all four subtiles for its own rows.  Shared tiles are
+// double-buffered in LDS with one barrier per tile: the next tile's loads
+// fly while this one computes, and go to LDS after it.  A wave's rows are
+// its own, so it writes them (or its split's partials) from registers with
+// no merge between waves.  With a mask, each wave stages its rows' mask
+// values of the next tile in its own LDS slice after computing the current
+// one (single-buffered: only that wave reads it).
+template <int D, bool MASK>
+struct PLay {
+  static constexpr int NW = kWavesPerBlock;
+  static constexpr int SUB = NW;                      // 16-key subtiles per shared tile
+  static constexpr int KTC = SUB * KT;                // keys per shared tile
+  static constexpr int SUB_ELEMS = KT * D;            // bf16 per K (or V) subtile
+  static constexpr int BUF_BYTES = 2 * SUB * SUB_ELEMS * 2;
+  static constexpr int MASK_SUB = 2 * 64 * 4;         // floats per subtile: [row block][lane] float4
+  static constexpr int MASK_WAVE = MASK ? SUB * MASK_SUB * 4 : 0;
+  static constexpr int BT_BYTES = (kBtCap + 4) * 4;
+  static constexpr int SMEM_BYTES = BT_BYTES + 2 * BUF_BYTES + NW * MASK_WAVE;
+};
+
+// Mask values of a wave's rows for the four subtiles of the shared tile at
+// key tb: lane (cc, q) takes keys tb + 16 sub + 4q + i of rows rw + cc + 16 rb
+// (keys and rows clamped into range; one load per entry on every path).
+template <int NRB>
+__device__ __forceinline__ void pmask_load(const DecodeArgs &a, const MCtx &c, int b, int rw, int tb, int lane,
+                                           float (&pm)[kWavesPerBlock][NRB][4]) {
+  const int q = lane >> 4;
+  const int cc = lane & 15;
+  const int jlast = c.ke - 1;
+#pragma unroll
+  for (int sub = 0; sub < kWavesPerBlock; ++sub) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int j = tb + KT * sub + 4 * q + i;
+      j = j < jlast ? j : jlast;
+      const float *mrow = a.mask + (int64_t)b * a.mask_sb + j;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int rr = rw + cc + 16 * rb < c.R ? rw + cc + 16 * rb : c.R - 1;
+        pm[sub][rb][i] = mrow[(int64_t)(rr / a.G) * a.mask_sq];
+      }
+    }
+  }
+}
+
+template <int NRB>
+__device__ __forceinline__ void pmask_store(const float (&pm)[kWavesPerBlock][NRB][4], float *mw, int lane) {
+#pragma unroll
+  for (int sub = 0; sub < kWavesPerBlock; ++sub)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      reinterpret_cast<float4 *>(mw + sub * 2 * 64 * 4)[rb * 64 + lane] =
+          make_float4(pm[sub][rb][0], pm[sub][rb][1], pm[sub][rb][2], pm[sub][rb][3]);
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, bool CAUSAL, bool MASK, bool UPAGE>
+__global__ __launch_bounds__(kWavesPerBlock * 64, (MASK && D == 128) ? 1 : 2) void split_prefill_mfma(
+    const DecodeArgs a) {
+  using P = PLay<D, MASK>;
+  constexpr int NW = P::NW;
+  constexpr int NRB = 2;                 // 32 rows per wave
+  constexpr int RWG = NW * 16 * NRB;     // rows per workgroup
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[P::SMEM_BYTES];
+  __shared__ int64_t rowtab[RWG];
+
+  Work wk0;
+  if (!work_of<CAUSAL>(a, wk0)) return;
+  const int b = wk0.b, s = wk0.s, g = wk0.hg, rg = wk0.rg;  // one kv head per workgroup: group = head
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int cc = lane & 15;
+  const int q = lane >> 4;
+  const int kvlen = wk0.L;
+  const SeqRows sr = wk0.sr;
+  const int r0 = rg * RWG;
+  if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
+  const int rw = r0 + 32 * w;  // this wave's first row
+  int lim[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) lim[rb] = row_keys(a, sr, kvlen, rw + cc + 16 * rb);
+  const int rlast = (r0 + RWG < sr.R ? r0 + RWG : sr.R) - 1;
+  const int kmax = row_keys(a, sr, kvlen, rlast);
+  const int wlast = (rw + 32 < sr.R ? rw + 32 : sr.R) - 1;
+  const int wkmax = wlast >= rw ? row_keys(a, sr, kvlen, wlast) : 0;  // keys this wave's rows see
+
+  const int nact = active_splits(a, kmax);
+  const int nrt = sr.R - r0 < RWG ? sr.R - r0 : RWG;
+  if (s >= nact) {
+    if (!a.fused) empty_partials(a, sr.tok0, g, r0, s, nrt);
+    return;
+  }
+  const bool direct = !a.partials || (a.fused && nact == 1);
+
+  int *bt_lds = reinterpret_cast<int *>(smem_raw);
+  unsigned char *bufs = smem_raw + P::BT_BYTES;
+  auto ktile = [&](int buf, int sub) {
+    return reinterpret_cast<uint16_t *>(bufs + buf * P::BUF_BYTES) + sub * P::SUB_ELEMS;
+  };
+  auto vtile = [&](int buf, int sub) {
+    return reinterpret_cast<uint16_t *>(bufs + buf * P::BUF_BYTES) + (P::SUB + sub) * P::SUB_ELEMS;
+  };
+  float *mw = reinterpret_cast<float *>(bufs + 2 * P::BUF_BYTES + w * P::MASK_WAVE);
+
+  MCtx c;
+  c.kbase = a.k + g * a.head_stride;
+  c.vbase = a.v + g * a.head_stride;
+  c.bt = bt_lds;
+  c.page_shift = a.page_shift;
+  c.pmask = (1 << a.page_shift) - 1;
+  c.page_stride = a.page_stride;
+  c.row_stride = a.row_stride;
+  c.R = sr.R;
+  const int kb = s * a.chunk;
+  int kend = kb + a.chunk;
+  if (kend > kmax) kend = kmax;
+
+  uint4 qb[NRB][D / 32];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int rr = rw + cc + 16 * rb;
+    if (rr < sr.R) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr.tok0, g, rr) * D);
+#pragma unroll
+      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
+    } else {
+#pragma unroll
+      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
+  const int win_keys = window_keys(kBtCap, a.page_shift, P::KTC);
+  const int cap_keys = a.max_pages << a.page_shift;
+  auto load_bt = [&](int from) {
+    if (a.contig) {  // contiguous K/V: sequence b is page b
+      if (threadIdx.x == 0) bt_lds[0] = b;
+      return;
+    }
+    int to = from + win_keys;
+    if (to > kb + a.chunk) to = kb + a.chunk;
+    if (to > cap_keys) to = cap_keys;
+    const int p0 = from >> a.page_shift;
+    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
+  };
+
+  MState<D, NRB> st;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    st.m[rb] = -INFINITY;
+    st.l[rb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if (threadIdx.x < RWG) {
+    const int rr = r0 + threadIdx.x;
+    rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, g, rr) : 0;
+  }
+  load_bt(kb);
+  __syncthreads();
+  for (int wb = kb; wb < kend; wb += win_keys) {
+    const int we = wb + win_keys < kend ? wb + win_keys : kend;
+    if (wb != kb) {
+      __syncthreads();
+      load_bt(wb);
+      __syncthreads();
+    }
+    c.p0 = wb >> a.page_shift;
+    c.ke = we;
+    const int ntiles = (we - wb + P::KTC - 1) / P::KTC;
+    MTile<D, NRB, false> tr;
+    float pm[MASK ? NW : 1][NRB][4];
+    mload<D, NRB, false, UPAGE>(a, c, b, rw, wb + KT * w, lane, tr);
+    if constexpr (MASK) pmask_load<NRB>(a, c, b, rw, wb, lane, pm);
+    mstore<D, NRB, false>(tr, ktile(0, w), vtile(0, w), nullptr, lane);
+    if constexpr (MASK) pmask_store<NRB>(pm, mw, lane);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      const int tb = wb + t * P::KTC;
+      // the next shared tile (unconditional: past the window end, mload and
+      // pmask_load clamp to its last key)
+      mload<D, NRB, false, UPAGE>(a, c, b, rw, tb + P::KTC + KT * w, lane, tr);
+      if constexpr (MASK) pmask_load<NRB>(a, c, b, rw, tb + P::KTC, lane, pm);
+#pragma unroll
+      for (int sub = 0; sub < P::SUB; ++sub) {
+        const int base = tb + KT * sub;
+        if (base < wkmax)  // wave-uniform: some row of this wave sees a key of the subtile
+          mcompute<D, NRB, CAUSAL, MASK>(a, c, base, mw + sub * P::MASK_SUB, qb, lim, b, rw, ktile(buf, sub),
+                                         vtile(buf, sub), lane, st);
+      }
+      mstore<D, NRB, false>(tr, ktile(buf ^ 1, w), vtile(buf ^ 1, w), nullptr, lane);
+      if constexpr (MASK) pmask_store<NRB>(pm, mw, lane);
+      __syncthreads();
+    }
+  }
+
+  // each wave writes its own rows: lane (cc, q) holds O^T[16nb + 4q + i][row cc]
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float W = xor32<OpSum>(xor16<OpSum>(st.l[rb]));
+    const int rr = rw + 16 * rb + cc;
+    if (rr < sr.R) {
+      const int64_t row = out_row(a, sr.tok0, g, rr);
+      const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const int d0 = 16 * nb + 4 * q;
+        const f32x4_t v = st.o[rb][nb] * inv;
+        if (direct) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2 *>(a.out + row * D + d0) = make_uint2(lo, hi);
+          if (a.out_f32) *reinterpret_cast<float4 *>(a.out_f32 + row * D + d0) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (W > 0.f) {
+          float *po = a.o_part + (row * a.S + s) * D + d0;
+          if (a.fused) {  // merged by another workgroup of this launch
+            store_dev2(po, v[0], v[1]);
+            store_dev2(po + 2, v[2], v[3]);
+          } else {
+            *reinterpret_cast<float4 *>(po) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      if (!direct && q == 0) {
+        float *pm2 = a.ml_part + (row * a.S + s) * 2;
+        const float mx = W > 0.f ? st.m[rb] * kLn2 : -INFINITY;
+        if (a.fused)
+          store_dev2(pm2, mx, W);
+        else
+          *reinterpret_cast<float2 *>(pm2) = make_float2(mx, W);
+      }
+    }
+  }
+  if (a.fused && !direct)
+    fused_tail<D>(a, wk0.unit, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
+}
+
+template <int D, bool C, bool M, bool U>
+hipError_t plaunch_t(const DecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((split_prefill_mfma<D, C, M, U>), dim3((unsigned)split_grid(a)), dim3(kWavesPerBlock * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool C, bool M>
+hipError_t plaunch_u(const DecodeArgs &a, hipStream_t s) {
+  return a.page_shift >= 4 ? plaunch_t<D, C, M, true>(a, s) : plaunch_t<D, C, M, false>(a, s);
+}
+
+template <int D>
+hipError_t plaunch_d(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
+  if (causal) return mask ? plaunch_u<D, true, true>(a, s) : plaunch_u<D, true, false>(a, s);
+  return mask ? plaunch_u<D, false, true>(a, s) : plaunch_u<D, false, false>(a, s);
+}
+
 template <int D, int NRB, bool C, bool M, bool U>
 hipError_t mlaunch_t(const DecodeArgs &a, hipStream_t stream) {
   const int64_t grid = split_grid(a);
@@ -513,6 +774,14 @@ hipError_t mlaunch_d(const DecodeArgs &a, int nrb16, bool causal, bool mask, hip
 }
 
 }  // namespace
+
+int launch_split_prefill(const DecodeArgs &a, int head_dim, bool causal, bool has_mask, hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return plaunch_d<32>(a, causal, has_mask, stream);
+    case 64: return plaunch_d<64>(a, causal, has_mask, stream);
+    default: return plaunch_d<128>(a, causal, has_mask, stream);
+  }
+}
 
 int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
                       hipStream_t stream) {

@@ -119,14 +119,21 @@ int split_cap_keys(int rows) {
 // D <= 64) or has a single register tile (matrix-core kernel at D = 256).
 int blocks_per_cu(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 2;
   if (pkv::use_mfma(R)) return p->head_dim == 128 ? 1 : 2;
   return 1;
+}
+
+// Packed rows per workgroup (the kernel family follows from it).
+int rows_per_block_of(const pkv_problem *p) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  return pkv::rows_per_block(R, p->head_dim, p->heads_per_block);
 }
 
 // Row blocks per kv head.
 int64_t row_blocks(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  return ceil_div(R, pkv::rows_per_block(R));
+  return ceil_div(R, rows_per_block_of(p));
 }
 
 // (sequence, kv-head group, row block) units with hpb kv heads per group:
@@ -164,7 +171,7 @@ int64_t row_block_slots(const pkv_problem *p, int64_t tokens) {
   const int64_t all = (int64_t)p->batch * row_blocks(p);
   if (tokens < 0 || p->batch > kExactMaxBatch) return all;
   const int G = p->num_q_heads / p->num_kv_heads;
-  const int rp = pkv::rows_per_block(G * p->q_len);
+  const int rp = rows_per_block_of(p);
   const int64_t nv = tokens * G / rp + p->batch;
   return nv < all ? nv : all;
 }
@@ -178,7 +185,7 @@ Load load_of(const pkv_problem *p, int hpb, int64_t tokens) {
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
   if (tokens < 0 || tokens >= (int64_t)p->batch * p->q_len) return Load{units_of(p, hpb), R};
-  int64_t rb = ceil_div(tokens * G, pkv::rows_per_block(R)) + p->batch;
+  int64_t rb = ceil_div(tokens * G, rows_per_block_of(p)) + p->batch;
   const int64_t all = (int64_t)p->batch * row_blocks(p);
   if (rb > all) rb = all;
   int64_t rows = ceil_div(tokens * G, rb);
@@ -200,6 +207,12 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb, int64_t tokens) {
   const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
   int64_t s = target / units;
   if (s > max_by_len) s = max_by_len;
+  // a varlen batch mixes sequences of few rows (decode tokens) with long
+  // key ranges: cap the keys per workgroup as for a full chip
+  if (tokens >= 0) {
+    const int64_t sc = ceil_div(max_len_of(p), split_cap_keys(ld.rows));
+    if (sc > s) s = sc;
+  }
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;
@@ -221,6 +234,7 @@ constexpr int kMaxGroupedSplits = 8;
 
 int max_heads_per_block(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 1;
   if (pkv::use_mfma(R)) return (p->head_dim == 64 || p->head_dim == 128) ? 2 : 1;
   return p->head_dim <= 128 ? pkv::kMaxHeadsPerBlock : 1;
 }
@@ -316,7 +330,7 @@ int plan_query(const pkv_problem *p, int64_t tokens, int num_cus, pkv_plan_info 
   *info = pkv_plan_info{};
   info->splits = pl.S;
   info->heads_per_block = pl.hpb;
-  info->rows_per_block = pkv::rows_per_block(R);
+  info->rows_per_block = rows_per_block_of(p);
   info->matrix_core = pkv::use_mfma(R) ? 1 : 0;
   info->units = pl.units;
   info->workgroups = pl.units * pl.S;
@@ -428,7 +442,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
 
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
-  const int rp = pkv::rows_per_block(R);
+  const int rp = rows_per_block_of(p);
   const int T = pkv::tile_keys(p->head_dim);
   const int64_t L = max_len_of(p);
   int64_t chunk = ceil_div(ceil_div(L, S), T) * T;
@@ -498,8 +512,10 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
 int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stream) {
   const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0 || p->causal_offset == PKV_CAUSAL_LAST;
   (void)hipGetLastError();
-  const int rows = pkv::rows_per_block(a.R);
-  int err = pkv::use_mfma(a.R)
+  const int rows = a.rp;
+  int err = rows == pkv::kPrefillRows
+                ? pkv::launch_split_prefill(a, p->head_dim, causal, a.mask != nullptr, stream)
+            : pkv::use_mfma(a.R)
                 ? pkv::launch_split_mfma(a, p->head_dim, rows / 16, causal, a.mask != nullptr, stream)
                 : pkv::launch_split(a, p->head_dim, rows, causal, a.mask != nullptr, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;

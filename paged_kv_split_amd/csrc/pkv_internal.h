@@ -62,7 +62,23 @@ struct CombineArgs {
 // was measured as fast or faster on gfx950 even with most of a tile padded
 // (R = 3, 4, 6, 8), so it takes over there.
 inline bool use_mfma(int R) { return R > 2; }
-int rows_per_block(int R);         // rows per workgroup: RP (VALU, 1 or 2) or 16/32 (MFMA)
+// The prefill-shaped matrix-core kernel: four waves of 32 rows each share
+// every K/V tile (128 rows per workgroup), so a key is read once per 128 rows
+// rather than once per 32.  Taken at D <= 128 with one kv head per workgroup
+// from 512 rows on (a chunk of 512 / G tokens: four of its row blocks).
+// Measured on MI355X (Hq = 32, Hkv = 8, D = 128, causal at the sequence end):
+// 4 x 512 tokens over 4096 keys 455 -> 387 us, 8 x 128 over 8192 keys
+// 467 -> 418 us, 1 x 512 over 8192 keys unchanged, 1 x 2048 over 2048 keys
+// 164 -> 177 us; below 512 rows, in a varlen batch of 32 sequences of which a
+// quarter hold prefill chunks of up to 64 tokens (256 rows), 105 -> 174 us,
+// so smaller row counts keep the 32-row kernel.
+constexpr int kPrefillRows = 128;      // rows per prefill-shaped workgroup
+constexpr int kPrefillMinRows = 512;   // packed rows per kv head from which it is taken
+inline bool use_prefill(int R, int head_dim, int forced_hpb) {
+  return R >= kPrefillMinRows && head_dim <= 128 && forced_hpb <= 1;
+}
+// rows per workgroup: RP (VALU, 1 or 2), 16/32 (MFMA) or 128 (prefill-shaped)
+int rows_per_block(int R, int head_dim, int forced_hpb);
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
 constexpr int kCausalLast = -2;    // causal_offset: the query tokens are the sequence's last keys
@@ -80,6 +96,7 @@ int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
                  bool has_mask, hipStream_t stream);
 int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
                       hipStream_t stream);
+int launch_split_prefill(const DecodeArgs &a, int head_dim, bool causal, bool has_mask, hipStream_t stream);
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
 int launch_zero(void *p, int64_t words, hipStream_t stream);
 

@@ -132,6 +132,7 @@ def test_compact_row_blocks_over_64_sequences(splits):
     w = workloads.varlen("compact150", q_lens=q_lens, kv_lens=lens, B=B, Hq=16, Hkv=2, D=64, page_size=16,
                          seed=3500, causal="lastv")
     pl = _plan(w, splits)
+    assert pl.rows_per_block == 32
     assert pl.units == (w.total_tokens * 8 // 32 + B) * 2 // pl.heads_per_block
     compare_varlen(w, num_splits=splits)
 
