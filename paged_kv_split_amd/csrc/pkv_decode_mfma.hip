@@ -269,6 +269,120 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
   __builtin_amdgcn_wave_barrier();
 }
 
+// Two 16-key tiles at once (keys base .. base + 31, the second tile at
+// kt1 / vt1): the same scores, mask, visibility and online softmax as
+// mcompute over eight keys per lane, and O^T += V^T P^T as one
+// v_mfma_f32_16x16x32_bf16 per 16 columns (per P half) instead of two
+// 16x16x16 ones.  The k index of that product runs over the lane's own keys:
+// k slots 8q .. 8q + 3 are keys 4q + i of the first tile and slots 8q + 4 ..
+// 8q + 7 keys 16 + 4q + i of the second, in the P operand (the lane's
+// probabilities) and in the V^T operand (two transposing reads, one per
+// tile) alike.
+template <int D, int NRB, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void mcompute2(const DecodeArgs &a, const MCtx &c, int base, const float *mkt0,
+                                          const float *mkt1, const uint4 (&qb)[NRB][D / 32], const int (&lim)[NRB],
+                                          const uint16_t *kt0, const uint16_t *vt0, const uint16_t *kt1,
+                                          const uint16_t *vt1, int lane, MState<D, NRB> &st) {
+  using L = MLay<D>;
+  const int cc = lane & 15;
+  const int q = lane >> 4;
+  f32x4_t s4[2][NRB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) s4[h][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int stp = 0; stp < D / 32; ++stp) {
+    const bf16x8_t ka0 =
+        __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4 *>(kt0 + cc * D)[L::swk(4 * stp + q, cc)]);
+    const bf16x8_t ka1 =
+        __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4 *>(kt1 + cc * D)[L::swk(4 * stp + q, cc)]);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, qb[rb][stp]);
+      s4[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qv, s4[0][rb], 0, 0, 0);
+      s4[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qv, s4[1][rb], 0, 0, 0);
+    }
+  }
+
+  float sv[NRB][8];
+  float dmax = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float mk[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (MASK) {
+        const float4 m4 = reinterpret_cast<const float4 *>(h ? mkt1 : mkt0)[rb * 64 + lane];
+        mk[0] = m4.x;
+        mk[1] = m4.y;
+        mk[2] = m4.z;
+        mk[3] = m4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = base + 16 * h + 4 * q + i;
+        const float v = MASK ? fmaf(s4[h][rb][i], a.scale_log2, mk[i] * kLog2e) : s4[h][rb][i] * a.scale_log2;
+        sv[rb][4 * h + i] = (j < c.ke && j < lim[rb]) ? v : -INFINITY;
+        dmax = fmaxf(dmax, sv[rb][4 * h + i] - st.m[rb]);
+      }
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(dmax > kRescaleLog2) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float mt = sv[rb][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[rb][i]);
+      mt = xor32<OpMax>(xor16<OpMax>(mt));
+      const float mnew = fmaxf(st.m[rb], mt);
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(st.m[rb] - mnew);
+      st.m[rb] = mnew;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] *= alpha;
+    }
+  }
+  bf16x8_t ph[NRB], pl[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float use = st.m[rb] == -INFINITY ? 0.f : st.m[rb];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = fast_exp2(sv[rb][i] - use);
+      lsum += p;
+      const uint16_t hb = f32_to_bf16_rne(p);
+      const float rem = p - bf16_bits_to_f32(hb);
+      ph[rb][i] = __builtin_bit_cast(__bf16, hb);
+      pl[rb][i] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(rem));
+    }
+    st.l[rb] += lsum;
+  }
+
+  const int srow = 4 * q + (cc >> 2);
+  const int sd = 4 * (cc & 3);
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    const int d0 = 16 * nb + sd;
+    const int ch = d0 >> 3;
+    const int half = (d0 >> 2) & 1;
+    const int ofs = srow * D * 2 + L::swv(ch, srow) * 16 + half * 8;
+    // vt0 / vt1 point into LDS: the C casts are address-space casts to LDS offsets
+    const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(reinterpret_cast<const char *>(vt0) + ofs));
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(reinterpret_cast<const char *>(vt1) + ofs));
+    const bf16x4_t va0 = __builtin_bit_cast(bf16x4_t, v0);
+    const bf16x4_t va1 = __builtin_bit_cast(bf16x4_t, v1);
+    const bf16x8_t va = bf16x8_t{va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      st.o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[rb], st.o[rb][nb], 0, 0, 0);
+      st.o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb], st.o[rb][nb], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // One pipeline step: tile tt (in registers tr) -> LDS; issue the loads of
 // tile tnext into tr; compute tile tt from LDS.
 template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
@@ -677,11 +791,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (MASK && D == 128) ? 1 : 2) vo
       mload<D, NRB, false, UPAGE>(a, c, b, rw, tb + P::KTC + KT * w, lane, tr);
       if constexpr (MASK) pmask_load<NRB>(a, c, b, rw, tb + P::KTC, lane, pm);
 #pragma unroll
-      for (int sub = 0; sub < P::SUB; ++sub) {
+      for (int sub = 0; sub < P::SUB; sub += 2) {
         const int base = tb + KT * sub;
-        if (base < wkmax)  // wave-uniform: some row of this wave sees a key of the subtile
-          mcompute<D, NRB, CAUSAL, MASK>(a, c, base, mw + sub * P::MASK_SUB, qb, lim, b, rw, ktile(buf, sub),
-                                         vtile(buf, sub), lane, st);
+        if (base < wkmax)  // wave-uniform: some row of this wave sees a key of the subtile pair
+          mcompute2<D, NRB, CAUSAL, MASK>(a, c, base, mw + sub * P::MASK_SUB, mw + (sub + 1) * P::MASK_SUB, qb, lim,
+                                          ktile(buf, sub), vtile(buf, sub), ktile(buf, sub + 1),
+                                          vtile(buf, sub + 1), lane, st);
       }
       mstore<D, NRB, false>(tr, ktile(buf ^ 1, w), vtile(buf ^ 1, w), nullptr, lane);
       if constexpr (MASK) pmask_store<NRB>(pm, mw, lane);
