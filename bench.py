@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E peak
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 matrix-core peak
 METRIC = "paged-decode attention µs/call and achieved HBM GB/s (% of peak), B=8..256"
 
 
@@ -73,6 +74,28 @@ def algorithmic_bytes(w) -> int:
     if w.mask is not None:
         mask = int((L * (n if w.mask.ndim == 3 else 1)).sum()) * 4
     return kv + qo + bt + mask
+
+
+def algorithmic_flops(w) -> int:
+    """Matrix flops one call must do at minimum: 4 * D per (query row, visible
+    key) (q.k and p.v, a multiply and an add each), over every query head."""
+    import numpy as np
+    L = w.kv_lens.astype(np.int64)
+    n = w.q_lens.astype(np.int64) if w.q_lens is not None else np.full(w.B, w.q_len, dtype=np.int64)
+    pairs = 0
+    for b in range(w.B):
+        i = np.arange(int(n[b]), dtype=np.int64)
+        if w.causal_offsets is not None:
+            c = int(w.causal_offsets[b])
+            vis = np.minimum(L[b], c + i + 1) if c >= 0 else np.full_like(i, L[b])
+        elif w.causal_offset == -2:
+            vis = np.minimum(L[b], L[b] - n[b] + i + 1)
+        elif w.causal_offset >= 0:
+            vis = np.minimum(L[b], w.causal_offset + i + 1)
+        else:
+            vis = np.full_like(i, L[b])
+        pairs += int(np.maximum(vis, 0).sum())
+    return pairs * w.Hq * w.D * 4
 
 
 def make_workload(name: str):
@@ -371,6 +394,10 @@ def main():
     gbs = kv_bytes / (us_call * 1e-6) / 1e9
     algo = algorithmic_bytes(w)
     kern_gbs = algo / (split_ms * 1e-3) / 1e9
+    flops = algorithmic_flops(w)
+    # the bound: matrix cores when the call's flops per byte exceed the
+    # machine balance (dense bf16 peak / HBM peak), else HBM
+    mfma_bound = flops / max(algo, 1) > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -394,9 +421,15 @@ def main():
         "warm_us_per_call": round(warm_ms * 1e3, 3),
         "graph_us_per_call": None if graph_call_ms is None else round(graph_call_ms * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
-        "roofline": {"bound": "hbm", "kernel": kernel_name(w, S, prob), "achieved": round(kern_gbs, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(w.name if paged else f"{w.name}:{args.kv_layout}")},
+        "algorithmic_flops_per_call": flops,
+        "roofline": ({"bound": "mfma", "kernel": kernel_name(w, S, prob),
+                      "achieved": round(flops / (split_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(flops / (split_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "traffic": measured_traffic(w.name if paged else f"{w.name}:{args.kv_layout}")}
+                     if mfma_bound else
+                     {"bound": "hbm", "kernel": kernel_name(w, S, prob), "achieved": round(kern_gbs, 2),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
+                      "traffic": measured_traffic(w.name if paged else f"{w.name}:{args.kv_layout}")}),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

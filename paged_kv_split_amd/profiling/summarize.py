@@ -22,7 +22,7 @@ from . import source_digest
 COPY_BYTES = 1 << 30
 SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8
-OURS = ("split_decode", "combine_kernel")
+OURS = ("split_decode", "split_prefill", "combine_kernel")
 
 
 def _csv(pattern):
@@ -78,7 +78,7 @@ def summarize(out, profiles, wl, cal, command):
         bench = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
     fetch = counter_per_dispatch(_csv(f"{out}/{wl}_fetch/*counter_collection.csv"), "FETCH_SIZE")
     write = counter_per_dispatch(_csv(f"{out}/{wl}_write/*counter_collection.csv"), "WRITE_SIZE")
-    split = max((r for r in ours if "split_decode" in r["Name"]), key=lambda r: float(r["TotalDurationNs"]))
+    split = max((r for r in ours if "split_" in r["Name"]), key=lambda r: float(r["TotalDurationNs"]))
     fam = _family(split["Name"])
     algo = bench["algorithmic_bytes_per_call"]
     ev_us = bench["kernel_us"]["split"]
@@ -99,8 +99,11 @@ def summarize(out, profiles, wl, cal, command):
               f"{prof_us:.2f} µs, ratio {ev_us / prof_us:.3f})",
               f"- whole call: {bench['us_per_call']:.2f} µs/call, {bench['value']:.1f} GB/s of K/V "
               f"({bench['kernels_per_call']} kernel(s) per call)",
-              f"- algorithmic bytes per call: {algo:,}; roofline achieved {bench['roofline']['achieved']:.1f} GB/s "
-              f"= {100 * bench['roofline']['frac']:.1f}% of 8000 GB/s", "",
+              f"- algorithmic bytes per call: {algo:,}; algorithmic matrix flops per call: "
+              f"{bench.get('algorithmic_flops_per_call', 0):,}",
+              f"- roofline ({bench['roofline']['bound']} bound): achieved {bench['roofline']['achieved']:.1f} "
+              f"{bench['roofline']['unit']} = {100 * bench['roofline']['frac']:.1f}% of "
+              f"{bench['roofline']['peak']:.0f} {bench['roofline']['unit']}", "",
               "## HBM bytes per launch (FETCH_SIZE, WRITE_SIZE)", "",
               f"Calibration on a 1 GiB device copy: FETCH_SIZE reads {cal['fetch_kib']:.0f} KiB "
               f"(scale {cal['fetch_scale']:.4f}), WRITE_SIZE reads {cal['write_kib']:.0f} KiB "

@@ -277,6 +277,14 @@ def mixed(seed: int = 1060, B: int = 32, max_q: int = 64, hi: int = 8192) -> Wor
     return w.replace(q_lens=q_lens, causal_offset=CAUSAL_LAST)
 
 
+def prefill(seed: int = 1070, B: int = 4, chunk: int = 512, L: int = 4096) -> Workload:
+    """Chunked prefill: B=4 sequences of L=4096 keys whose last 512 are a new
+    chunk of query tokens (causal_offset CAUSAL_LAST), Hq=32, Hkv=8, D=128,
+    page 32."""
+    w = build("prefill", B=B, q_len=chunk, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[L] * B, seed=seed)
+    return w.replace(causal_offset=CAUSAL_LAST)
+
+
 def varlen(name: str, *, q_lens, seed: int, **kw) -> Workload:
     """``build`` with q_len = max(q_lens) (at least 1) and per-sequence query
     token counts q_lens (drawn from nothing: given); causal "lastv" sets
@@ -296,4 +304,5 @@ CONFIGS = {
     "long_ctx": long_ctx,
     "ragged": ragged,
     "mixed": mixed,
+    "prefill": prefill,
 }
