@@ -229,8 +229,13 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb, int64_t tokens) {
 // 13% with four heads (B = 64 and 256).  Grouping is taken only while the
 // split count stays in [2, kMaxGroupedSplits]: at one split a workgroup would
 // hold hpb whole sequences, which ragged lengths unbalance (B = 256 lognormal
-// lengths: 1.65x slower), and more splits cost more partial traffic.
+// lengths: 1.65x slower), and more splits cost more partial traffic; and only
+// while a split holds at most kMaxGroupedChunk keys: grouping halves the
+// units, and a grid of few long splits leaves the chip idle behind the
+// longest sequences (B = 32 lognormal lengths up to 8192 keys, D = 128:
+// two heads at 2 splits 108 us, one head at 8 splits 61 us).
 constexpr int kMaxGroupedSplits = 8;
+constexpr int64_t kMaxGroupedChunk = 2048;
 
 int max_heads_per_block(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
@@ -243,7 +248,7 @@ int heuristic_hpb(const pkv_problem *p, int cus, int64_t tokens) {
   for (int hpb = max_heads_per_block(p); hpb > 1; hpb /= 2) {
     if (p->num_kv_heads % hpb) continue;
     const int s = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, hpb, tokens);
-    if (s >= 2 && s <= kMaxGroupedSplits) return hpb;
+    if (s >= 2 && s <= kMaxGroupedSplits && ceil_div(max_len_of(p), s) <= kMaxGroupedChunk) return hpb;
   }
   return 1;
 }

@@ -367,3 +367,15 @@ def test_plan_varlen():
         pkv.plan_varlen(p, 32 * 64 + 1, 256)
     with pytest.raises(pkv.PkvError):
         pkv.plan_varlen(p, -1, 256)
+
+
+def test_grouping_needs_short_splits():
+    """Two kv heads per workgroup would give 2 splits of 4096 keys for 32
+    sequences of up to 8192 keys (D = 128, G = 4): the plan keeps one head per
+    workgroup, which fills the chip with 8 splits of 1024 keys."""
+    p = base_problem(batch=32, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=32,
+                     num_pages=9000, max_pages_per_seq=256, max_kv_len=8192)
+    pl = pkv.plan(p, 256)
+    assert (pl.splits, pl.heads_per_block, pl.rows_per_block) == (8, 1, 16)
+    p.heads_per_block = 2
+    assert pkv.plan(p, 256).splits == 2
