@@ -171,3 +171,121 @@ def test_exact_schedule_with_separate_combine():
     assert nv < B * 3 and pl.units == nv * 16
     assert pl.merge_in_kernel == 0 and pl.kernels == 2
     compare_varlen(w, num_splits=3, heads_per_block=1)
+
+
+def _dev_varlen(w):
+    import torch
+    from gpu_util import dev_tensors
+    d = dev_tensors(w)
+    qp, cu = w.packed_q()
+    d["qp"] = torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    d["cu"] = torch.from_numpy(cu).to("cuda:0")
+    return d
+
+
+def test_varlen_graph_capture_with_changing_token_counts():
+    """A captured varlen call (exact schedule, in-kernel merge) replayed after
+    q, kv_lens and the token counts change in place (same total): every
+    replay equals an eager call on the same inputs, and the oracle."""
+    import torch
+    import paged_kv_split_amd as pkv
+    w = workloads.varlen("vgraph", q_lens=[1, 9, 1, 6], kv_lens=[1500, 900, 3000, 400], B=4, Hq=32, Hkv=8, D=128,
+                         page_size=32, seed=3800, causal="lastv")
+    d = _dev_varlen(w)
+    T = w.total_tokens
+    p = problem_for_varlen(w, 4)
+    o_part, ml_part = pkv.alloc_workspace(p, 4, "cuda:0")
+    out = torch.empty(tuple(d["qp"].shape), dtype=torch.bfloat16, device="cuda:0")
+    out32 = torch.empty(tuple(d["qp"].shape), dtype=torch.float32, device="cuda:0")
+
+    def call(stream=None):
+        pkv.paged_decode_varlen(d["qp"], d["k"], d["v"], d["bt"], d["kl"], d["cu"], max_q_len=w.q_len,
+                                scale=w.scale, num_splits=4, max_kv_len=w.max_kv_len, out=out, out_f32=out32,
+                                o_part=o_part, ml_part=ml_part, stream=stream)
+
+    note("varlen graph capture")
+    call()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    counts = [[1, 9, 1, 6], [4, 4, 4, 5], [9, 0, 8, 0], [1, 1, 6, 9]]   # each at most the 9 the launch is sized for
+    rng = np.random.default_rng(7)
+    for rep, ql in enumerate(counts):
+        assert sum(ql) == T
+        lens = np.maximum(rng.integers(1, w.kv_lens + 1), np.array(ql)).astype(np.int32)
+        wr = w.replace(q_lens=np.array(ql, np.int32), kv_lens=lens)
+        qp, cu = wr.packed_q()
+        d["qp"].copy_(torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16).to("cuda:0"))
+        d["cu"].copy_(torch.from_numpy(cu).to("cuda:0"))
+        d["kl"].copy_(torch.from_numpy(lens).to("cuda:0"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        r32, r16 = out32.clone(), out.clone()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(r32.view(torch.int32), out32.view(torch.int32)), f"replay {rep}"
+        assert torch.equal(r16.view(torch.int16), out.view(torch.int16)), f"replay {rep}"
+        check(r16.view(torch.int16).cpu().numpy().view(np.uint16), r32.cpu().numpy(), oracle.decode_varlen(wr),
+              f"graph replay {rep}")
+
+
+def problem_for_varlen(w, splits):
+    from gpu_util import problem
+    return problem(w, splits)
+
+
+def test_one_workspace_across_varlen_fixed_and_prefill_calls():
+    """The arrival counters of every call are left zero: varlen (exact
+    schedule), fixed-length and prefill-shaped calls share one workspace in
+    turn, each checked against the oracle."""
+    import torch
+    import paged_kv_split_amd as pkv
+    from gpu_util import dev_tensors, problem
+    wv = workloads.varlen("wsv", q_lens=[3, 1, 12, 1], kv_lens=[700, 2000, 900, 50], B=4, Hq=32, Hkv=8, D=128,
+                          page_size=32, seed=3900, causal="lastv")
+    wf = workloads.build("wsf", B=6, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                         kv_lens=[3000, 100, 2000, 5, 900, 4096], seed=3901)
+    wp = workloads.build("wsp", B=2, q_len=160, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[2000, 700],
+                         seed=3902).replace(causal_offset=LAST)
+    big = max(pkv.workspace_bytes(problem(x, 4), 4)[0] for x in (wv, wf, wp)), \
+        max(pkv.workspace_bytes(problem(x, 4), 4)[1] for x in (wv, wf, wp))
+    o_part = torch.empty(big[0] // 4, dtype=torch.float32, device="cuda:0")
+    ml_part = torch.zeros(big[1] // 4, dtype=torch.float32, device="cuda:0")
+    for rnd in range(2):
+        note(f"shared workspace round {rnd}")
+        d = _dev_varlen(wv)
+        out32 = torch.empty(tuple(d["qp"].shape), dtype=torch.float32, device="cuda:0")
+        o16 = pkv.paged_decode_varlen(d["qp"], d["k"], d["v"], d["bt"], d["kl"], d["cu"], max_q_len=wv.q_len,
+                                      scale=wv.scale, num_splits=4, max_kv_len=wv.max_kv_len, out_f32=out32,
+                                      o_part=o_part, ml_part=ml_part)
+        torch.cuda.synchronize()
+        check(o16.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), oracle.decode_varlen(wv),
+              "shared workspace varlen")
+        for x in (wf, wp):
+            d = dev_tensors(x)
+            p = problem(x, 4)
+            out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
+            o16 = pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=x.scale,
+                                   causal_offset=x.causal_offset, out_f32=out32, o_part=o_part, ml_part=ml_part,
+                                   problem=p)
+            torch.cuda.synchronize()
+            ref = oracle.decode_varlen(x).reshape(out32.shape) if x.causal_offset == LAST else oracle.decode(x)
+            check(o16.view(torch.int16).cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref,
+                  f"shared workspace {x.name}")
+    head = ml_part[: pkv.PKV_COUNTER_BYTES // 4].view(torch.int32)
+    assert int(head.abs().sum()) == 0
+
+
+def test_varlen_calls_are_deterministic():
+    w = workloads.mixed()
+    note("varlen determinism")
+    a16, a32 = run_varlen(w)
+    b16, b32 = run_varlen(w)
+    assert np.array_equal(a16, b16) and np.array_equal(a32.view(np.uint32), b32.view(np.uint32))
