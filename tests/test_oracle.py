@@ -420,3 +420,43 @@ def test_packed_q_and_mixed_workload():
     assert 0 < (m.q_lens > 1).sum() < m.B
     with pytest.raises(ValueError):
         oracle.decode(m)
+
+
+def test_varlen_closed_forms():
+    """Hand-checkable varlen cases (causal "last"): a token that sees one key
+    returns that key's V row exactly; tokens whose visible keys are all equal
+    return the exact mean of the visible V rows; a sequence with no tokens
+    adds no rows; a token with no visible key (more tokens than keys) is 0."""
+    P, D, Hkv, Hq = 4, 8, 1, 2
+    rng = np.random.default_rng(11)
+    kv = lambda n: f32_to_bf16_bits(np.round(rng.normal(size=(n, D)) * 4) / 4)
+    # sequence 0: 2 keys, 2 tokens; sequence 1: no tokens; sequence 2: 3 keys, 1 token;
+    # sequence 3: 1 key, 2 tokens (the first sees nothing)
+    L = [2, 5, 3, 1]
+    q_lens = [2, 0, 1, 2]
+    pages = [[0], [1, 2], [3], [4]]
+    k = np.zeros((5, P, Hkv, D), np.uint16)
+    v = np.zeros((5, P, Hkv, D), np.uint16)
+    same_key = kv(1)[0]
+    for b, pg in enumerate(pages):
+        for j in range(L[b]):
+            k[pg[j // P], j % P, 0] = same_key
+            v[pg[j // P], j % P, 0] = kv(1)[0]
+    q = np.zeros((4, 2, Hq, D), np.uint16)
+    q[:] = kv(1)[0]
+    bt = np.full((4, 2), -1, np.int32)
+    for b, pg in enumerate(pages):
+        bt[b, :len(pg)] = pg
+    w = Workload(name="closed", B=4, q_len=2, Hq=Hq, Hkv=Hkv, D=D, page_size=P, q=q, k_cache=k, v_cache=v,
+                 block_table=bt, kv_lens=np.array(L, np.int32), scale=0.5, causal_offset=workloads.CAUSAL_LAST,
+                 q_lens=np.array(q_lens, np.int32))
+    out = oracle.decode_varlen(w)
+    assert out.shape == (5, Hq, D)
+    vrow = lambda b, j: oracle.bf16_bits_to_f64(v[pages[b][j // P], j % P, 0])
+    for h in range(Hq):
+        assert np.array_equal(out[0, h], vrow(0, 0))                           # token 0 of seq 0: key 0 only
+        assert np.allclose(out[1, h], (vrow(0, 0) + vrow(0, 1)) / 2, atol=1e-15)  # token 1: keys 0, 1
+        assert np.allclose(out[2, h], (vrow(2, 0) + vrow(2, 1) + vrow(2, 2)) / 3, atol=1e-15)
+        assert (out[3, h] == 0).all()                                          # seq 3, token 0: position -1
+        assert np.array_equal(out[4, h], vrow(3, 0))                           # seq 3, token 1: key 0
+    np.testing.assert_allclose(oracle.bruteforce_varlen(w), out, rtol=0, atol=1e-15)
