@@ -281,6 +281,7 @@ def _partials_then_combine(w, d, S):
     dict(B=3, q_len=1, Hq=16, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]),              # VALU, R=2
     dict(B=2, q_len=2, Hq=16, Hkv=2, D=64, page_size=16, kv_lens=[900, 77], causal="last"),      # MFMA, R=16
     dict(B=2, q_len=1, Hq=48, Hkv=1, D=256, page_size=64, kv_lens=[700, 1000], mask="2d"),        # MFMA, R=48
+    dict(B=2, q_len=160, Hq=32, Hkv=8, D=64, page_size=32, kv_lens=[800, 300], causal="last"),   # prefill, R=640
 ])
 @pytest.mark.parametrize("S", [2, 7, 64])
 def test_in_kernel_merge_equals_separate_combine(shape, S):
