@@ -20,8 +20,9 @@
 //  * O^T = V^T P^T with v_mfma_f32_16x16x16_bf16: V^T comes straight from
 //    the row-major V tile through ds_read_b64_tr_b16 (the gfx950 transposing
 //    LDS read), P^T is the S^T register layout itself; P is split into a bf16
-//    high part and a bf16 remainder (two MFMAs) so the probabilities keep
-//    about 16 significant bits, and the row sums l use the fp32 values;
+//    high part and a bf16 remainder (two MFMAs, both converted with the
+//    gfx950 v_cvt_pk_bf16_f32) so the probabilities keep about 16
+//    significant bits, and the row sums l use the fp32 values;
 //  * exclusion (tail, causal, -inf mask) is a select; scores are in base 2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -239,10 +240,10 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
     for (int i = 0; i < 4; ++i) {
       const float p = fast_exp2(sv[rb][i] - use);
       lsum += p;
-      const uint16_t hb = f32_to_bf16_rne(p);
-      const float rem = p - bf16_bits_to_f32(hb);
-      ph[rb][i] = __builtin_bit_cast(__bf16, hb);
-      pl[rb][i] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(rem));
+      // the gfx950 conversion (v_cvt_pk_bf16_f32, round to nearest even)
+      const __bf16 hi = (__bf16)p;
+      ph[rb][i] = hi;
+      pl[rb][i] = (__bf16)(p - (float)hi);
     }
     st.l[rb] += lsum;
   }
@@ -352,10 +353,10 @@ __device__ __forceinline__ void mcompute2(const DecodeArgs &a, const MCtx &c, in
     for (int i = 0; i < 8; ++i) {
       const float p = fast_exp2(sv[rb][i] - use);
       lsum += p;
-      const uint16_t hb = f32_to_bf16_rne(p);
-      const float rem = p - bf16_bits_to_f32(hb);
-      ph[rb][i] = __builtin_bit_cast(__bf16, hb);
-      pl[rb][i] = __builtin_bit_cast(__bf16, f32_to_bf16_rne(rem));
+      // the gfx950 conversion (v_cvt_pk_bf16_f32, round to nearest even)
+      const __bf16 hi = (__bf16)p;
+      ph[rb][i] = hi;
+      pl[rb][i] = (__bf16)(p - (float)hi);
     }
     st.l[rb] += lsum;
   }
