@@ -80,8 +80,25 @@ struct MCtx {
   int64_t page_stride;
   int row_stride;
   int ke;
-  int R;  // packed rows of the sequence per kv head
+  int R;     // packed rows of the sequence per kv head
+  int kvis;  // keys every row of this wave that exists sees (a tile below it needs no visibility select)
 };
+
+// The smallest key limit over a wave's rows that exist (rows past the
+// sequence's rows see nothing and are never written, so they do not count).
+template <int NRB>
+__device__ __forceinline__ int wave_min_limit(const int (&lim)[NRB], int r0, int R, int lane) {
+  int v = INT_MAX;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+    if (r0 + (lane & 15) + 16 * rb < R) v = lim[rb] < v ? lim[rb] : v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_xor(v, d, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
 
 // Loads of one 16-key tile: full K/V rows, 128 bits per lane.  Rows past the
 // end are clamped to the last valid key (finite data, zero weight); when a
@@ -209,13 +226,22 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
       mk[3] = m4.w;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = base + 4 * q + i;
-      const float v = MASK ? fmaf(s4[rb][i], a.scale_log2, mk[i] * kLog2e) : s4[rb][i] * a.scale_log2;
-      sv[rb][i] = (j < c.ke && j < lim[rb]) ? v : -INFINITY;
-      dmax = fmaxf(dmax, sv[rb][i] - st.m[rb]);
-    }
+    for (int i = 0; i < 4; ++i)
+      sv[rb][i] = MASK ? fmaf(s4[rb][i], a.scale_log2, mk[i] * kLog2e) : s4[rb][i] * a.scale_log2;
   }
+  // a tile inside every row's window (wave-uniform) needs no visibility select
+  if (!(base + KT <= c.ke && base + KT <= c.kvis)) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = base + 4 * q + i;
+        sv[rb][i] = (j < c.ke && j < lim[rb]) ? sv[rb][i] : -INFINITY;
+      }
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+    dmax = fmaxf(dmax, fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3])) - st.m[rb]);
   // lazy reference max: move it (and rescale O, l) only when a score exceeds
   // it by more than kRescaleLog2; the branch is wave-uniform
   if (__builtin_amdgcn_ballot_w64(dmax > kRescaleLog2) != 0) {
@@ -321,13 +347,27 @@ __device__ __forceinline__ void mcompute2(const DecodeArgs &a, const MCtx &c, in
         mk[3] = m4.w;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = base + 16 * h + 4 * q + i;
-        const float v = MASK ? fmaf(s4[h][rb][i], a.scale_log2, mk[i] * kLog2e) : s4[h][rb][i] * a.scale_log2;
-        sv[rb][4 * h + i] = (j < c.ke && j < lim[rb]) ? v : -INFINITY;
-        dmax = fmaxf(dmax, sv[rb][4 * h + i] - st.m[rb]);
-      }
+      for (int i = 0; i < 4; ++i)
+        sv[rb][4 * h + i] = MASK ? fmaf(s4[h][rb][i], a.scale_log2, mk[i] * kLog2e) : s4[h][rb][i] * a.scale_log2;
     }
+  }
+  if (!(base + 2 * KT <= c.ke && base + 2 * KT <= c.kvis)) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = base + 16 * h + 4 * q + i;
+          sv[rb][4 * h + i] = (j < c.ke && j < lim[rb]) ? sv[rb][4 * h + i] : -INFINITY;
+        }
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float mt = sv[rb][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[rb][i]);
+    dmax = fmaxf(dmax, mt - st.m[rb]);
   }
   if (__builtin_amdgcn_ballot_w64(dmax > kRescaleLog2) != 0) {
 #pragma unroll
@@ -505,6 +545,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   c.page_stride = a.page_stride;
   c.row_stride = a.row_stride;
   c.R = sr.R;
+  c.kvis = wave_min_limit<NRB>(lim, r0, sr.R, lane);
   const int kb = s * a.chunk;
   int kend = kb + a.chunk;
   if (kend > kmax) kend = kmax;
@@ -719,6 +760,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (MASK && D == 128) ? 1 : 2) vo
   c.page_stride = a.page_stride;
   c.row_stride = a.row_stride;
   c.R = sr.R;
+  c.kvis = wave_min_limit<NRB>(lim, rw, sr.R, lane);
   const int kb = s * a.chunk;
   int kend = kb + a.chunk;
   if (kend > kmax) kend = kmax;
