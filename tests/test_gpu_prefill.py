@@ -97,3 +97,24 @@ def test_varlen_prefill_chunks():
         note(f"varlen prefill splits={splits}")
         o16, o32 = run_varlen(w, num_splits=splits)
         check(o16, o32, oracle.decode_varlen(w), "varlen prefill")
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_varlen_prefill_with_3d_mask_and_single_sequence(splits):
+    """Varlen through the prefill-shaped kernel with a 3D mask (indexed by
+    the token within its sequence), and a batch of one sequence whose chunk
+    is shorter than the bound."""
+    w = workloads.varlen("vpmask", q_lens=[70, 1, 128, 0], kv_lens=[700, 64, 1500, 9], B=4, Hq=32, Hkv=8, D=64,
+                         page_size=16, seed=4300, causal="lastv", mask="3d", mask_p=0.15)
+    import paged_kv_split_amd as pkv
+    assert pkv.plan_varlen(problem(w, splits), w.total_tokens).rows_per_block == 128
+    note(f"varlen prefill 3d mask splits={splits}")
+    o16, o32 = run_varlen(w, num_splits=splits)
+    check(o16, o32, oracle.decode_varlen(w), "varlen prefill 3d mask")
+    w1 = workloads.varlen("vp1", q_lens=[300], kv_lens=[2500], B=1, Hq=16, Hkv=2, D=128, page_size=32, seed=4301,
+                          causal="lastv")
+    w1 = w1.replace(q_len=512, q=np.concatenate([w1.q, np.zeros((1, 212, 16, 128), np.uint16)], axis=1))
+    assert pkv.plan_varlen(problem(w1, splits), w1.total_tokens).rows_per_block == 128
+    note(f"varlen prefill single sequence splits={splits}")
+    o16, o32 = run_varlen(w1, num_splits=splits)
+    check(o16, o32, oracle.decode_varlen(w1), "varlen prefill single sequence")
