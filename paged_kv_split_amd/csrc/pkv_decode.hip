@@ -234,8 +234,7 @@ struct QRows {
 template <int D, int RP, bool CAUSAL, bool MASK, class Q>
 __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, RP> &c, int base,
                                              const Tile<D, RP, MASK> &t, const Q &qrows,
-                                             const int (&lim)[RP], int b, int r0, float *pbuf, float *kbuf,
-                                             State<RP> &st) {
+                                             const int (&lim)[RP], float *pbuf, float *kbuf, State<RP> &st) {
   using Lay = Layout<D, RP>;
   constexpr int NPASS = Lay::NPASS, KPP = Lay::KPP, LPK = Lay::LPK;
   // K tile: row layout (registers) -> per-wave LDS slice -> key-major layout
@@ -387,7 +386,7 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> 
   for (int t = t0; t < ntiles; t += NBUF * tstep) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
-      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * tstep) * T, tr[i], qrows, lim, b, r0, pbuf, kbuf, st);
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * tstep) * T, tr[i], qrows, lim, pbuf, kbuf, st);
       load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + (i + NBUF) * tstep) * T, tr[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -501,7 +500,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
     for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
   };
-  if (threadIdx.x < RP * a.hpb) {
+  if ((int)threadIdx.x < RP * a.hpb) {
     const int rr = r0 + (threadIdx.x >> a.lhpb);
     rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }

@@ -194,8 +194,8 @@ __device__ __forceinline__ void mstore(const MTile<D, NRB, MASK> &t, uint16_t *k
 template <int D, int NRB, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int base,
                                          const float *mkt, const uint4 (&qb)[NRB][D / 32],
-                                         const int (&lim)[NRB], int b, int r0, const uint16_t *kt,
-                                         const uint16_t *vt, int lane, MState<D, NRB> &st) {
+                                         const int (&lim)[NRB], const uint16_t *kt, const uint16_t *vt,
+                                         int lane, MState<D, NRB> &st) {
   using L = MLay<D>;
   const int cc = lane & 15;
   const int q = lane >> 4;
@@ -437,7 +437,7 @@ __device__ __forceinline__ void mstep(const DecodeArgs &a, const MCtx &c, int b,
   // mload): the loads in flight are then the same on every path, and the
   // wait before the next tile leaves this prefetch in flight
   mload<D, NRB, MASK, UPAGE>(a, c, b, r0, wb + tnext * KT, lane, tr);
-  mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mkt, qb, lim, b, r0, kt, vt, lane, st);
+  mcompute<D, NRB, CAUSAL, MASK>(a, c, wb + tt * KT, mkt, qb, lim, kt, vt, lane, st);
 }
 
 // Register tiles per wave, as measured on MI355X (B = 16 x 4096 keys and
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     for (int nb = 0; nb < D / 16; ++nb) st.o[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (threadIdx.x < RW * a.hpb) {
+  if ((int)threadIdx.x < RW * a.hpb) {
     const int rr = r0 + (threadIdx.x >> a.lhpb);
     rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
