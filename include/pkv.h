@@ -122,7 +122,7 @@ typedef struct pkv_plan_info {
   int32_t heads_per_block;  /* kv heads per split workgroup (1, 2 or 4) */
   int32_t rows_per_block;   /* packed query rows (G * q_len) per kv head per workgroup:
                                1 or 2 (vector kernel), 16 or 32 (matrix-core kernel),
-                               128 (prefill-shaped matrix-core kernel: from 512 rows on at
+                               128 (prefill-shaped matrix-core kernel: from 128 rows on at
                                D <= 128 with one kv head per workgroup, four waves of 32
                                rows sharing each K/V tile) */
   int32_t matrix_core;      /* 1: a matrix-core split kernel; 0: the vector one */

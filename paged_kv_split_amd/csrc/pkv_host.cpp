@@ -117,9 +117,12 @@ int split_cap_keys(int rows) {
 // latency (VALU kernel: 8-16 KB tiles per wave; matrix-core kernel at
 // D = 128), two where it keeps fewer (matrix-core 16-key tiles of 2-4 KB at
 // D <= 64) or has a single register tile (matrix-core kernel at D = 256).
+// The prefill-shaped kernel: one, its 128-row workgroups being compute-heavy
+// (4 x 64 tokens over 2048 keys: 4 splits 52 us, 8 splits 68 us; 8 x 32 over
+// 8192: 109 against 123 us).
 int blocks_per_cu(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 2;
+  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 1;
   if (pkv::use_mfma(R)) return p->head_dim == 128 ? 1 : 2;
   return 1;
 }
@@ -142,26 +145,15 @@ int64_t units_of(const pkv_problem *p, int hpb) {
   return (int64_t)p->batch * (p->num_kv_heads / hpb) * row_blocks(p);
 }
 
-// The work the split heuristic sizes the grid for: (sequence, kv-head group,
-// row block) units that hold rows, and packed rows per such unit.  A batch
-// of q_len tokens per sequence (or a varlen batch that has them all): every
-// unit, R rows.  A varlen batch of `tokens` tokens: its row blocks number at most
-// ceil(tokens * G / rp) + B (each sequence may end in a partial block), and
-// the rows spread over them; the other units of the grid exit at once.
-struct Load {
-  int64_t units;
-  int rows;
-};
-
 // Varlen batches up to this size take the exact schedule (every workgroup
 // counts the work items of the whole batch, each lane a run of up to 4
 // sequences, which keeps the kernels' register counts unchanged); other
 // calls get one block per (sequence, split, row block).  Measured on MI355X:
 // a batch of 32 sequences, a quarter with prefill chunks of up to 64 tokens,
-// 240 -> 110 us.  For fixed-length batches the per-block split-major order is
-// as fast or faster (B = 256 lognormal lengths: 382 against 373 us at 4
-// splits, 401 against 433 us at 8; the 1B decode shape: 10.0 against 11.0 us),
-// so they keep it.
+// 240 -> 110 us.  Fixed-length batches keep the per-block split-major order:
+// there the exact schedule won only on the B = 256, q_len = 4 lognormal batch
+// at 4 splits (2-5%) and lost elsewhere (the same batch at 8 splits 8-13%,
+// other ragged shapes 1-3%, the 1B decode shape 10.0 -> 11.0 us).
 constexpr int kExactMaxBatch = 64 * 4;
 
 // Row-block slots the grid holds: B * ceil(R / rp); a varlen batch of
@@ -180,6 +172,17 @@ int64_t row_block_slots(const pkv_problem *p, int64_t tokens) {
 int64_t grid_units(const pkv_problem *p, int hpb, int64_t tokens) {
   return row_block_slots(p, tokens) * (p->num_kv_heads / hpb);
 }
+
+// The work the split heuristic sizes the grid for: (sequence, kv-head group,
+// row block) units that hold rows, and packed rows per such unit.  A batch
+// of q_len tokens per sequence (or a varlen batch that has them all): every
+// unit, R rows.  A varlen batch of `tokens` tokens: its row blocks number at most
+// ceil(tokens * G / rp) + B (each sequence may end in a partial block), and
+// the rows spread over them; the other units of the grid exit at once.
+struct Load {
+  int64_t units;
+  int rows;
+};
 
 Load load_of(const pkv_problem *p, int hpb, int64_t tokens) {
   const int G = p->num_q_heads / p->num_kv_heads;

@@ -65,15 +65,16 @@ inline bool use_mfma(int R) { return R > 2; }
 // The prefill-shaped matrix-core kernel: four waves of 32 rows each share
 // every K/V tile (128 rows per workgroup), so a key is read once per 128 rows
 // rather than once per 32.  Taken at D <= 128 with one kv head per workgroup
-// from 512 rows on (a chunk of 512 / G tokens: four of its row blocks).
-// Measured on MI355X (Hq = 32, Hkv = 8, D = 128, causal at the sequence end):
-// 4 x 512 tokens over 4096 keys 455 -> 387 us, 8 x 128 over 8192 keys
-// 467 -> 418 us, 1 x 512 over 8192 keys unchanged, 1 x 2048 over 2048 keys
-// 164 -> 177 us; below 512 rows, in a varlen batch of 32 sequences of which a
-// quarter hold prefill chunks of up to 64 tokens (256 rows), 105 -> 174 us,
-// so smaller row counts keep the 32-row kernel.
+// from 128 rows on (a chunk of 128 / G tokens).  Measured on MI355X against
+// the 32-row kernel (Hq = 32, Hkv = 8, D = 128, causal at the sequence end;
+// B x tokens over keys): 4 x 512 over 4096 369 -> 243 us, 1 x 2048 over 2048
+// 134 -> 101 us, 8 x 128 over 8192 384 -> 271 us, 1 x 512 over 8192
+// 187 -> 157 us, 64 x 32 over 1024 138 -> 74 us, 16 x 64 over 4096
+// 217 -> 166 us, 8 x 32 over 8192 136 -> 109 us; a varlen batch of 32
+// sequences of which a quarter hold prefill chunks of up to 64 tokens (256
+// rows) 115 us either way.
 constexpr int kPrefillRows = 128;      // rows per prefill-shaped workgroup
-constexpr int kPrefillMinRows = 512;   // packed rows per kv head from which it is taken
+constexpr int kPrefillMinRows = 128;   // packed rows per kv head from which it is taken
 inline bool use_prefill(int R, int head_dim, int forced_hpb) {
   return R >= kPrefillMinRows && head_dim <= 128 && forced_hpb <= 1;
 }

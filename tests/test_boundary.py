@@ -350,18 +350,19 @@ def test_varlen_decode_checks():
 
 def test_plan_varlen():
     """pkv_plan_varlen sizes the grid for the rows the tokens fill: a batch of
-    32 sequences bounded at 64 tokens (G = 4, 32-row blocks) that holds 273
-    tokens has about 66 row blocks with rows, so its sequences are split
-    (8 splits of about 1024 keys at 8192 keys); holding every token, it
-    plans as pkv_plan does."""
+    32 sequences bounded at 64 tokens (G = 4: 256 rows, 128-row blocks) that
+    holds 273 tokens has about 41 row blocks with rows, ~27 rows each, so its
+    sequences are split (5 splits of at most 1728 keys at 8192 keys); holding
+    every token, it plans as pkv_plan does."""
     p = base_problem(batch=32, q_len=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=32,
                      num_pages=9000, max_pages_per_seq=256, max_kv_len=8192, causal_offset=pkv.PKV_CAUSAL_LAST)
     full = pkv.plan(p, 256)
-    assert (full.splits, full.matrix_core, full.rows_per_block) == (1, 1, 32)
+    assert (full.splits, full.matrix_core, full.rows_per_block, full.units) == (1, 1, 128, 32 * 8 * 2)
     same = pkv.plan_varlen(p, 32 * 64, 256)
     assert [getattr(same, f) for f, _ in same._fields_] == [getattr(full, f) for f, _ in full._fields_]
     mixed = pkv.plan_varlen(p, 273, 256)
-    assert mixed.splits == 8 and mixed.merge_in_kernel == 1 and mixed.kernels == 1
+    assert mixed.splits == 5 and mixed.units == (273 * 4 // 128 + 32) * 8
+    assert mixed.merge_in_kernel == 1 and mixed.kernels == 1
     assert pkv.plan_varlen(p, 0, 256).splits == 1
     with pytest.raises(pkv.PkvError):
         pkv.plan_varlen(p, 32 * 64 + 1, 256)

@@ -1,4 +1,4 @@
-"""GPU parity of the prefill-shaped matrix-core kernel (from 512 packed rows
+"""GPU parity of the prefill-shaped matrix-core kernel (from 128 packed rows
 per kv head at D <= 128: four waves of 32 rows sharing each 64-key K/V tile)
 against the fp64 oracle: chunks of query tokens over paged K/V, causal at the
 end of the sequence or at a fixed position, 2D/3D masks, forced splits with

@@ -131,10 +131,13 @@ def test_compact_row_blocks_over_64_sequences(splits):
     lens = [max(L, n) for L, n in zip(lens, q_lens)]
     w = workloads.varlen("compact150", q_lens=q_lens, kv_lens=lens, B=B, Hq=16, Hkv=2, D=64, page_size=16,
                          seed=3500, causal="lastv")
-    pl = _plan(w, splits)
+    pl = _plan(w, splits, 2)           # two kv heads per workgroup: the 32-row kernel
     assert pl.rows_per_block == 32
-    assert pl.units == (w.total_tokens * 8 // 32 + B) * 2 // pl.heads_per_block
-    compare_varlen(w, num_splits=splits)
+    assert pl.units == w.total_tokens * 8 // 32 + B
+    compare_varlen(w, num_splits=splits, heads_per_block=2)
+    pl = _plan(w, splits, 1)           # one: the 128-row prefill-shaped kernel (128 rows per sequence)
+    assert pl.rows_per_block == 128 and pl.units == B * 2
+    compare_varlen(w, num_splits=splits, heads_per_block=1)
 
 
 def test_large_varlen_batch_with_separate_combine():
