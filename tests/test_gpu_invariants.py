@@ -1,7 +1,7 @@
 """GPU invariants that need no oracle value: byte-identity under physical page
 reshuffles and buffer moves, exact closed forms, poisoned unused memory,
-agreement across split counts, graph capture, stream ordering and guard
-bands around every output."""
+agreement across split counts, graph capture, stream ordering, guard bands
+around every output, and keys stored past element 2^32 of a cache."""
 import numpy as np
 import pytest
 import torch
@@ -362,3 +362,92 @@ def test_both_merge_paths_are_exercised():
               (dict(B=600, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 600), 2)]
     flags = [pkv.merges_in_kernel(problem(workloads.build("paths", seed=1, **kw), S), S) for kw, S in shapes]
     assert flags == [True, True, False]
+
+
+# Keys stored past 2^32 elements of a cache (8 GiB of bf16): page and sequence
+# offsets are 64-bit products, so the same keys placed there give the same
+# bytes as in a small cache.  One case per kernel family: the VALU kernel
+# (one row per kv head), the 32-row matrix-core kernel and the prefill-shaped
+# one (512 rows per kv head).
+FAR = 1 << 32
+FAR_CASES = [
+    ("split_decode_valu", lambda: workloads.build("far_valu", B=3, q_len=1, Hq=8, Hkv=8, D=64, page_size=32,
+                                                   kv_lens=[700, 33, 1500], seed=3101, mask="2d")),
+    ("split_decode_mfma", lambda: workloads.build("far_mfma", B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=16,
+                                                   kv_lens=[1200, 5, 640], seed=3102)),
+    ("split_prefill_mfma", lambda: workloads.build("far_prefill", B=2, q_len=128, Hq=16, Hkv=4, D=64, page_size=32,
+                                                    kv_lens=[900, 300], seed=3103).replace(
+                                                        causal_offset=workloads.CAUSAL_LAST)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FAR_CASES)))
+def test_pages_past_4g_elements(i):
+    family, make = FAR_CASES[i]
+    w = make()
+    stride = w.page_size * w.Hkv * w.D
+    n = w.num_pages
+    big = (FAR + stride - 1) // stride + n          # pages n .. big - 1 lie wholly past element 2^32
+    assert (big - n) * stride >= FAR
+    p_big = problem(w)
+    p_big.num_pages = big
+    assert pkv.kernel_family(p_big) == family
+    note(f"far pages {w.name} num_pages={big} ({2 * big * stride * 2 / 2**30:.1f} GiB of K/V)")
+    ref16, ref32 = run(w, num_splits=3)
+    d = dev_tensors(w)
+    shape = (big, w.page_size, w.Hkv, w.D)
+    kb = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    vb = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    kb[big - n:] = d["k"]
+    vb[big - n:] = d["v"]
+    bt = torch.where(d["bt"] >= 0, d["bt"] + (big - n), d["bt"])
+    p_big.num_splits = 3
+    out = torch.empty(tuple(d["q"].shape), dtype=torch.bfloat16, device="cuda:0")
+    out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
+    pkv.paged_decode(d["q"], kb, vb, bt, d["kl"], scale=w.scale, causal_offset=w.causal_offset,
+                     causal_offsets=d["co"], mask=d["mask"], out=out, out_f32=out32, problem=p_big)
+    torch.cuda.synchronize()
+    got16 = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    got32 = out32.cpu().numpy()
+    del kb, vb
+    torch.cuda.empty_cache()
+    assert np.array_equal(got16, ref16)
+    assert np.array_equal(got32.view(np.uint32), ref32.view(np.uint32))
+
+
+@pytest.mark.parametrize("layout", ["blhd", "bhld"])
+def test_contiguous_sequences_past_4g_elements(layout):
+    w = workloads.build("far_contig", B=2, q_len=2, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[1000, 777],
+                        seed=3104, causal="last")
+    from gpu_util import run_contiguous
+    ref16, ref32, k, v = run_contiguous(w, layout, num_splits=3)
+    cap_small = k.shape[1] if layout == "blhd" else k.shape[2]
+    # the last (sequence, head) region starts past element 2^32
+    per_seq = FAR // (w.Hkv * w.D) + 1 if layout == "blhd" else FAR // (3 * w.D) + 1
+    cap = max(per_seq, cap_small)
+    last_region = (w.B - 1) * cap * w.Hkv * w.D if layout == "blhd" else (w.B * w.Hkv - 1) * cap * w.D
+    assert last_region >= FAR
+    note(f"far contiguous {layout} capacity={cap} ({2 * w.B * w.Hkv * cap * w.D * 2 / 2**30:.1f} GiB of K/V)")
+    d = dev_tensors(w)
+    ks = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    vs = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    shape = (w.B, cap, w.Hkv, w.D) if layout == "blhd" else (w.B, w.Hkv, cap, w.D)
+    kb = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    vb = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    if layout == "blhd":
+        kb[:, :cap_small] = ks
+        vb[:, :cap_small] = vs
+    else:
+        kb[:, :, :cap_small] = ks
+        vb[:, :, :cap_small] = vs
+    out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device="cuda:0")
+    out = pkv.contiguous_decode(d["q"], kb, vb, d["kl"], layout=layout, scale=w.scale,
+                                causal_offset=w.causal_offset, causal_offsets=d["co"], mask=d["mask"],
+                                num_splits=3, max_kv_len=w.max_kv_len, out_f32=out32)
+    torch.cuda.synchronize()
+    got16 = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    got32 = out32.cpu().numpy()
+    del kb, vb
+    torch.cuda.empty_cache()
+    assert np.array_equal(got16, ref16)
+    assert np.array_equal(got32.view(np.uint32), ref32.view(np.uint32))
