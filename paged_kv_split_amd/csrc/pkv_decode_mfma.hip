@@ -39,7 +39,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Two probabilities as bf16 high parts (round to nearest even, one
+// v_cvt_pk_bf16_f32 for the pair) and the bf16 roundings of what remains of
+// each.  The high parts' fp32 values come back from the packed word by a
+// shift and a mask, not by converting each value on its own.
+__device__ __forceinline__ void split_pair(float x, float y, bf16x2_t &hi, bf16x2_t &lo) {
+  hi = __builtin_convertvector(f32x2_t{x, y}, bf16x2_t);
+  const uint32_t u = __builtin_bit_cast(uint32_t, hi);
+  lo = __builtin_convertvector(f32x2_t{x - __uint_as_float(u << 16), y - __uint_as_float(u & 0xffff0000u)},
+                               bf16x2_t);
+}
 
 constexpr int kBtCap = 1024;
 constexpr int KT = 16;  // keys per wave tile
@@ -263,13 +276,17 @@ __device__ __forceinline__ void mcompute(const DecodeArgs &a, const MCtx &c, int
     const float use = st.m[rb] == -INFINITY ? 0.f : st.m[rb];
     float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(sv[rb][i] - use);
-      lsum += p;
-      // the gfx950 conversion (v_cvt_pk_bf16_f32, round to nearest even)
-      const __bf16 hi = (__bf16)p;
-      ph[rb][i] = hi;
-      pl[rb][i] = (__bf16)(p - (float)hi);
+    for (int i = 0; i < 4; i += 2) {
+      const float p0 = fast_exp2(sv[rb][i] - use);
+      const float p1 = fast_exp2(sv[rb][i + 1] - use);
+      lsum += p0;
+      lsum += p1;
+      bf16x2_t hi, lo;
+      split_pair(p0, p1, hi, lo);
+      ph[rb][i] = hi[0];
+      ph[rb][i + 1] = hi[1];
+      pl[rb][i] = lo[0];
+      pl[rb][i + 1] = lo[1];
     }
     st.l[rb] += lsum;
   }
@@ -390,13 +407,17 @@ __device__ __forceinline__ void mcompute2(const DecodeArgs &a, const MCtx &c, in
     const float use = st.m[rb] == -INFINITY ? 0.f : st.m[rb];
     float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = fast_exp2(sv[rb][i] - use);
-      lsum += p;
-      // the gfx950 conversion (v_cvt_pk_bf16_f32, round to nearest even)
-      const __bf16 hi = (__bf16)p;
-      ph[rb][i] = hi;
-      pl[rb][i] = (__bf16)(p - (float)hi);
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = fast_exp2(sv[rb][i] - use);
+      const float p1 = fast_exp2(sv[rb][i + 1] - use);
+      lsum += p0;
+      lsum += p1;
+      bf16x2_t hi, lo;
+      split_pair(p0, p1, hi, lo);
+      ph[rb][i] = hi[0];
+      ph[rb][i + 1] = hi[1];
+      pl[rb][i] = lo[0];
+      pl[rb][i + 1] = lo[1];
     }
     st.l[rb] += lsum;
   }

@@ -128,3 +128,32 @@ def test_all_masked_and_empty_rows_are_zero():
         out16, out32 = run(w, num_splits=s)
         assert not out32[1:].any() and not out16[1:].any()
         check(out16, out32, oracle.decode(w), "masked")
+
+
+# ---- the score scale at its edges -------------------------------------------
+# A negative scale (the kernels negate q and use |scale|), a zero scale (every
+# visible key weighs the same: the rows are plain means of V) and a large
+# one (near one-hot rows), on each kernel family, with and without a mask and
+# causal limits.
+SCALE_CASES = [
+    lambda: workloads.build("scale_valu", B=3, q_len=1, Hq=8, Hkv=8, D=64, page_size=32,
+                            kv_lens=[700, 33, 1500], seed=2201),
+    lambda: workloads.build("scale_mfma", B=3, q_len=2, Hq=32, Hkv=8, D=128, page_size=16,
+                            kv_lens=[1200, 5, 640], seed=2202, causal="last"),
+    lambda: workloads.build("scale_mfma_mask", B=2, q_len=1, Hq=16, Hkv=2, D=64, page_size=32,
+                            kv_lens=[900, 77], seed=2203, mask="3d", mask_p=0.2),
+    lambda: workloads.build("scale_prefill", B=2, q_len=128, Hq=16, Hkv=4, D=64, page_size=32,
+                            kv_lens=[900, 300], seed=2204).replace(causal_offset=workloads.CAUSAL_LAST),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SCALE_CASES)))
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.6])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_negative_zero_and_large_scale(i, scale, splits):
+    w = SCALE_CASES[i]().replace(scale=scale)
+    note(f"scale {w.name} scale={scale} splits={splits}")
+    out16, out32 = run(w, num_splits=splits)
+    ref = oracle.decode_varlen(w).reshape(out32.shape) if w.causal_offset == workloads.CAUSAL_LAST \
+        else oracle.decode(w)
+    check(out16, out32, ref, f"{w.name} scale={scale}")
