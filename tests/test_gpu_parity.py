@@ -157,3 +157,34 @@ def test_negative_zero_and_large_scale(i, scale, splits):
     ref = oracle.decode_varlen(w).reshape(out32.shape) if w.causal_offset == workloads.CAUSAL_LAST \
         else oracle.decode(w)
     check(out16, out32, ref, f"{w.name} scale={scale}")
+
+
+# ---- the documented limits ---------------------------------------------------
+# PKV_MAX_SPLITS splits (most of them past a sequence's end or a few keys
+# long), and pages of 4096 keys (the largest page size: one page-table entry
+# covers more keys than a split), on each kernel family.
+LIMIT_CASES = [
+    lambda: workloads.build("max_splits_valu", B=3, q_len=1, Hq=8, Hkv=8, D=64, page_size=16,
+                            kv_lens=[5000, 17, 1300], seed=2301),
+    lambda: workloads.build("max_splits_mfma", B=2, q_len=2, Hq=32, Hkv=8, D=128, page_size=32,
+                            kv_lens=[4100, 300], seed=2302, causal="last", mask="2d", mask_p=0.1),
+    lambda: workloads.build("page4096_valu", B=3, q_len=1, Hq=16, Hkv=16, D=32, page_size=4096,
+                            kv_lens=[9000, 4096, 1], seed=2303, spare_pages=1),
+    lambda: workloads.build("page4096_mfma", B=2, q_len=4, Hq=16, Hkv=2, D=256, page_size=4096,
+                            kv_lens=[8193, 600], seed=2304, causal="last"),
+    lambda: workloads.build("page4096_prefill", B=1, q_len=160, Hq=8, Hkv=1, D=64, page_size=4096,
+                            kv_lens=[5000], seed=2305).replace(causal_offset=workloads.CAUSAL_LAST),
+]
+
+
+@pytest.mark.parametrize("i", range(len(LIMIT_CASES)))
+@pytest.mark.parametrize("splits", [0, 256])
+def test_documented_limits(i, splits):
+    import paged_kv_split_amd as pkv
+    assert pkv.PKV_MAX_SPLITS == 256
+    w = LIMIT_CASES[i]()
+    note(f"limits {w.name} splits={splits}")
+    out16, out32 = run(w, num_splits=splits)
+    ref = oracle.decode_varlen(w).reshape(out32.shape) if w.causal_offset == workloads.CAUSAL_LAST \
+        else oracle.decode(w)
+    check(out16, out32, ref, f"{w.name} splits={splits}")
