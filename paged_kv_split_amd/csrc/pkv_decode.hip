@@ -196,13 +196,28 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, const Ctx<D, RP> 
     const int64_t pofs = (int64_t)page * c.page_stride + (int64_t)(bj & c.pmask) * c.row_stride;
     const uint16_t *kp = c.kbase + pofs;
     const uint16_t *vp = c.vbase + pofs;
+    if (D == 256 && base + Lay::T - 1 <= jlast) {
+      // every key of the tile exists (bj = base): one multiply for the lane,
+      // a wave-uniform step per load (at D = 256 only: 16 x 4096 keys, one
+      // query head per kv head, 85.0 -> 83.9 us; at D = 64 and 128 the same
+      // shapes ran 5% slower, at D = 32 no change)
+      const uint32_t o0 = (uint32_t)(c.kg * c.row_stride);
+      const uint32_t step = (uint32_t)(Lay::KPV * c.row_stride);
 #pragma unroll
-    for (int st = 0; st < Lay::NSTEP; ++st) {
-      int j = base + st * Lay::KPV + c.kg;
-      j = j < jlast ? j : jlast;
-      const uint32_t off = (uint32_t)((j - bj) * c.row_stride);
-      t.k[st] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + c.ds);
-      t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + c.ds);
+      for (int st = 0; st < Lay::NSTEP; ++st) {
+        const uint32_t off = o0 + st * step;
+        t.k[st] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + c.ds);
+        t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + c.ds);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < Lay::NSTEP; ++st) {
+        int j = base + st * Lay::KPV + c.kg;
+        j = j < jlast ? j : jlast;
+        const uint32_t off = (uint32_t)((j - bj) * c.row_stride);
+        t.k[st] = load_stream(reinterpret_cast<const uint4 *>(kp + off) + c.ds);
+        t.v[st] = load_stream(reinterpret_cast<const uint4 *>(vp + off) + c.ds);
+      }
     }
   } else {
 #pragma unroll
