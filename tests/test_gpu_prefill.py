@@ -118,3 +118,14 @@ def test_varlen_prefill_with_3d_mask_and_single_sequence(splits):
     note(f"varlen prefill single sequence splits={splits}")
     o16, o32 = run_varlen(w1, num_splits=splits)
     check(o16, o32, oracle.decode_varlen(w1), "varlen prefill single sequence")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 8])
+def test_whole_sequence_causal_prefill_of_2048_tokens(splits):
+    """A 2048-token sequence prefilled whole (causal, G = 8: 16384 rows, 128
+    row blocks of one kv head): the triangle of visible keys spans every
+    position from 1 to 2048 keys, each row block's causal skip differs, and
+    the (pair, row block) list is dealt over the eight XCDs."""
+    w = workloads.build("long_prefill", B=1, q_len=2048, Hq=8, Hkv=1, D=64, page_size=64, kv_lens=[2048],
+                        seed=4400).replace(causal_offset=LAST)
+    compare(w, splits)
