@@ -2,7 +2,9 @@
 options together (head dim, GQA ratio, page size, batch, query tokens,
 lengths including empty and one-key sequences, causal mode, mask, forced
 splits and kv-head grouping, fixed-length or varlen), so combinations that
-the hand-picked cases do not list are compared with the fp64 oracle too.
+the hand-picked cases do not list are compared with the fp64 oracle too;
+fixed-length cases also run over a contiguous copy of their keys, which must
+give the same bits.
 The draws are fixed by the case seed; sizes keep the oracle to a fraction of
 a second per case."""
 import numpy as np
@@ -13,7 +15,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, note, run, run_varlen  # noqa: E402
+from gpu_util import check, note, run, run_contiguous, run_varlen  # noqa: E402
 
 N_CASES = 160
 
@@ -63,3 +65,9 @@ def test_random_problem(seed):
         o16, o32 = run(w, num_splits=splits, heads_per_block=hpb)
         ref = oracle.decode(w)
     check(o16, o32, ref.reshape(o32.shape), f"random seed={seed}")
+    if not varlen:
+        # the same keys in a contiguous cache: the same plan, the same bits
+        layout = ("blhd", "bhld")[seed % 2]
+        c16, c32, _, _ = run_contiguous(w, layout, num_splits=splits, heads_per_block=hpb)
+        assert np.array_equal(c16, o16), f"contiguous {layout} bf16 differs"
+        assert np.array_equal(c32.view(np.uint32), o32.view(np.uint32)), f"contiguous {layout} fp32 differs"
