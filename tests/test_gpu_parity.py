@@ -99,15 +99,13 @@ def test_small_cases(i, splits):
     compare(w, num_splits=splits)
 
 
-@pytest.mark.parametrize("i", range(len(SMALL)))
+@pytest.mark.parametrize("i,hpb", [(i, h) for i in range(len(SMALL)) for h in (1, 2, 4)
+                                   if SMALL[i]["Hkv"] % h == 0])
 @pytest.mark.parametrize("splits", [1, 5])
-@pytest.mark.parametrize("hpb", [1, 2, 4])
-def test_small_cases_heads_per_block(i, splits, hpb):
+def test_small_cases_heads_per_block(i, hpb, splits):
     """Every kv-head grouping of a workgroup (one to four heads, one or more
-    waves per head) on the same cases."""
+    waves per head, each dividing the case's kv heads) on the same cases."""
     kw = dict(SMALL[i])
-    if kw["Hkv"] % hpb:
-        pytest.skip("heads per workgroup must divide Hkv")
     w = workloads.build(f"small{i}", seed=2000 + i, spare_pages=3, **kw)
     compare(w, num_splits=splits, heads_per_block=hpb)
 
