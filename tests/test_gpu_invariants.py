@@ -212,6 +212,40 @@ def test_runs_on_the_given_stream_in_order():
     assert np.array_equal(out16, ref16)
 
 
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state between calls: two problems, each with its
+    own outputs and split workspace (in-kernel merge counters included), run
+    interleaved on two streams at once give the bits each gives alone."""
+    wa = workloads.build("conc_a", B=8, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                         kv_lens=[3000, 17, 2048, 900, 1, 4096, 333, 1500], seed=3095)
+    wb = workloads.build("conc_b", B=5, q_len=4, Hq=16, Hkv=2, D=64, page_size=16,
+                         kv_lens=[700, 2100, 64, 5, 1300], seed=3096, causal="last", mask="2d")
+    refs = [run(w, num_splits=s) for w, s in ((wa, 6), (wb, 5))]
+    ws = [(wa, dev_tensors(wa), 6), (wb, dev_tensors(wb), 5)]
+    outs = []
+    for w, d, S in ws:
+        p = problem(w, S)
+        o_part, ml_part = pkv.alloc_workspace(p, S, d["q"].device)
+        out = torch.empty(tuple(d["q"].shape), dtype=torch.bfloat16, device=d["q"].device)
+        out32 = torch.empty(tuple(d["q"].shape), dtype=torch.float32, device=d["q"].device)
+        outs.append((p, o_part, ml_part, out, out32))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    note("two streams, 20 interleaved calls each")
+    for _ in range(20):
+        for k, ((w, d, S), (p, o_part, ml_part, out, out32)) in enumerate(zip(ws, outs)):
+            pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale,
+                             causal_offset=w.causal_offset, causal_offsets=d["co"], mask=d["mask"],
+                             out=out, out_f32=out32, o_part=o_part, ml_part=ml_part, stream=streams[k],
+                             problem=p)
+    torch.cuda.synchronize()
+    for (ref16, ref32), (p, o_part, ml_part, out, out32) in zip(refs, outs):
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref16)
+        assert np.array_equal(out32.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+        head = ml_part[:pkv.PKV_COUNTER_BYTES // 4]
+        assert not head.any().item()   # every counter back at zero
+
+
 def test_guard_bands_untouched():
     w = workloads.build("canary", B=3, q_len=2, Hq=8, Hkv=2, D=64, page_size=32, kv_lens=[500, 3, 200],
                         seed=3100, mask="2d", causal="last")
