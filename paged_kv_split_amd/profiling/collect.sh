@@ -1,8 +1,9 @@
 #!/bin/bash
 # Collect, for each bench.py workload named, a rocprofv3 kernel trace with
-# per-kernel statistics and three counter passes (FETCH_SIZE; WRITE_SIZE;
+# per-kernel statistics and four counter passes (FETCH_SIZE; WRITE_SIZE;
 # matrix-core busy cycles and bf16 MFMA operations, LDS bank conflicts and LDS
-# activity, GPU active cycles), plus FETCH_SIZE and WRITE_SIZE for a plain
+# activity, GPU active cycles; instruction counts and VALU / matrix-core issue
+# overlap), plus FETCH_SIZE and WRITE_SIZE for a plain
 # 1 GiB device copy (calibration).
 # usage: bash paged_kv_split_amd/profiling/collect.sh OUTDIR WORKLOAD...
 set -u
@@ -40,5 +41,8 @@ for wl in "$@"; do
   step "${wl}_sq" 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT \
     SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE MfmaUtil -d "$out/${wl}_sq" -o sq --output-format csv -- \
     $BENCH --workload "$wl" --steps 4
+  step "${wl}_issue" 120 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 \
+    SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE \
+    -d "$out/${wl}_issue" -o issue --output-format csv -- $BENCH --workload "$wl" --steps 4
 done
 echo "collected in $out" >&2

@@ -150,6 +150,26 @@ def summarize(out, profiles, wl, cal, command):
                       f"rocprofv3 average duration (dense bf16 peak 2500 TFLOP/s)",
                       f"- LDS bank conflicts: {conf:,.0f} cycles over {lds:,.0f} LDS-active cycles "
                       f"({sq['lds_bank_conflict_pct']:.2f}%)", ""]
+    if glob.glob(f"{out}/{wl}_issue/*counter_collection.csv"):
+        rows = _csv(f"{out}/{wl}_issue/*counter_collection.csv")
+        names = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU",
+                 "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAVES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+        c = {n: counter_per_dispatch(rows, n) for n in names}
+        name = next((k for k in c["GRBM_GUI_ACTIVE"] if _short(k) == _short(split["Name"])), None)
+        waves = c["SQ_WAVES"].get(name, 0.0) if name is not None else 0.0
+        if waves > 0:
+            g = {n: c[n].get(name, 0.0) for n in names}
+            simd_cycles = g["GRBM_GUI_ACTIVE"] / XCDS * SIMDS
+            lines += ["## Instruction issue (SQ counters, per launch of the split kernel)", "",
+                      f"- per wave: {g['SQ_INSTS_VALU'] / waves:,.0f} VALU instructions (MFMAs included), "
+                      f"{g['SQ_INSTS_MFMA'] / waves:,.0f} MFMAs, {g['SQ_INSTS_VALU_TRANS_F32'] / waves:,.0f} "
+                      f"fp32 transcendentals, {g['SQ_INSTS_LDS'] / waves:,.0f} LDS instructions "
+                      f"({waves:,.0f} waves)",
+                      f"- VALU and matrix cores issuing together: "
+                      f"{100.0 * g['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd_cycles:.1f}% of SIMD cycles "
+                      f"(SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs))",
+                      f"- VALU instructions executing: {100.0 * g['SQ_ACTIVE_INST_VALU'] / g['SQ_WAVE_CYCLES']:.1f}% "
+                      f"of wave cycles (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)", ""]
     path = os.path.join(profiles, f"{fam}_{wl}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
