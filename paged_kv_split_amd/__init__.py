@@ -255,6 +255,17 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _call_stream(stream):
+    """The torch stream a call runs on: ``stream``, else the current one.
+    Outputs and workspace that a wrapper allocates are allocated with this
+    stream current, so torch's caching allocator ties them to it (their memory
+    is not handed to other streams while the call's kernels may still use
+    it) and the zero fill of a new workspace is queued on it, ahead of the
+    call."""
+    import torch
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
 def _require(t, name, dtype, ndim=None):
     import torch
     if t.dtype != dtype:
@@ -319,15 +330,17 @@ def paged_decode(q, k_cache, v_cache, block_table, kv_lens, *, scale: float,
                                                          causal_offset=causal_offset, mask=mask,
                                                          num_splits=num_splits, max_kv_len=max_kv_len)
     S = num_splits_for(p)
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    if S > 1 and (o_part is None or ml_part is None):
-        o_part, ml_part = alloc_workspace(p, S, q.device)
+    s = _call_stream(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if S > 1 and (o_part is None or ml_part is None):
+            o_part, ml_part = alloc_workspace(p, S, q.device)
     st = paged_decode_raw(p, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(kv_lens),
                           _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
                           0 if o_part is None else o_part.numel() * o_part.element_size(),
                           _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
-                          _ptr(out), _ptr(out_f32), _stream_handle(stream))
+                          _ptr(out), _ptr(out_f32), int(s.cuda_stream))
     _check(st, "pkv_paged_decode")
     return out
 
@@ -373,15 +386,17 @@ def paged_decode_varlen(q, k_cache, v_cache, block_table, kv_lens, cu_q_lens, *,
                      scale=scale, causal_offset=causal_offset, num_splits=num_splits, mask_stride_b=msb,
                      mask_stride_q=msq, heads_per_block=heads_per_block)
     S = num_splits if num_splits > 0 else plan_varlen(p, T).splits
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    if S > 1 and (o_part is None or ml_part is None):
-        o_part, ml_part = alloc_workspace(p, S, q.device)
+    s = _call_stream(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if S > 1 and (o_part is None or ml_part is None):
+            o_part, ml_part = alloc_workspace(p, S, q.device)
     st = paged_decode_varlen_raw(p, _ptr(cu_q_lens), T, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(kv_lens), _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
                                  0 if o_part is None else o_part.numel() * o_part.element_size(), _ptr(ml_part),
                                  0 if ml_part is None else ml_part.numel() * ml_part.element_size(), _ptr(out),
-                                 _ptr(out_f32), _stream_handle(stream))
+                                 _ptr(out_f32), int(s.cuda_stream))
     _check(st, "pkv_paged_decode_varlen")
     return out
 
@@ -437,15 +452,17 @@ def contiguous_decode(q, k_cache, v_cache, kv_lens, *, layout: str = "blhd", sca
                            max_kv_len=max_kv_len, scale=scale, causal_offset=causal_offset, num_splits=num_splits,
                            mask_stride_b=msb, mask_stride_q=msq, heads_per_block=heads_per_block)
     S = num_splits_for(p)
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    if S > 1 and (o_part is None or ml_part is None):
-        o_part, ml_part = alloc_workspace(p, S, q.device)
+    s = _call_stream(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if S > 1 and (o_part is None or ml_part is None):
+            o_part, ml_part = alloc_workspace(p, S, q.device)
     st = contiguous_decode_raw(p, KV_LAYOUTS[layout], cap, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
                                _ptr(causal_offsets), _ptr(mask), _ptr(o_part),
                                0 if o_part is None else o_part.numel() * o_part.element_size(),
                                _ptr(ml_part), 0 if ml_part is None else ml_part.numel() * ml_part.element_size(),
-                               _ptr(out), _ptr(out_f32), _stream_handle(stream))
+                               _ptr(out), _ptr(out_f32), int(s.cuda_stream))
     _check(st, "pkv_contiguous_decode")
     return out
 
@@ -496,8 +513,10 @@ def combine(o_part, ml_part, *, rows: int, splits: int, head_dim: int, out=None,
     import torch
     _require(o_part, "o_part", torch.float32)
     _require(ml_part, "ml_part", torch.float32)
+    s = _call_stream(stream)
     if out is None:
-        out = torch.empty((rows, head_dim), dtype=torch.bfloat16, device=o_part.device)
+        with torch.cuda.stream(s):
+            out = torch.empty((rows, head_dim), dtype=torch.bfloat16, device=o_part.device)
     _check(combine_raw(rows, splits, head_dim, _ptr(o_part), _ptr(ml_part), _ptr(out), _ptr(out_f32),
-                       _stream_handle(stream)), "pkv_combine")
+                       int(s.cuda_stream)), "pkv_combine")
     return out

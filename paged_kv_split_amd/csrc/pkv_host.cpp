@@ -264,8 +264,12 @@ struct Plan {
   bool fused;     // pkv_paged_decode merges the splits inside the split kernel
 };
 
-// tokens: -1 for q_len tokens per sequence, else a varlen batch's total.
+// tokens: -1 for q_len tokens per sequence, else a varlen batch's total.  A
+// varlen batch that holds every token (B * q_len) is planned as the
+// fixed-length batch, so both entry points give it the same splits and
+// grouping, hence the same bits.
 Plan make_plan(const pkv_problem *p, int cus, int64_t tokens = -1) {
+  if (tokens >= (int64_t)p->batch * p->q_len) tokens = -1;
   Plan pl;
   pl.hpb = p->heads_per_block > 0 ? p->heads_per_block : heuristic_hpb(p, cus, tokens);
   pl.S = p->num_splits > 0 ? p->num_splits : heuristic_splits(p, cus, pl.hpb, tokens);

@@ -4,7 +4,8 @@
 # matrix-core busy cycles and bf16 MFMA operations, LDS bank conflicts and LDS
 # activity, GPU active cycles; instruction counts and VALU / matrix-core issue
 # overlap), plus FETCH_SIZE and WRITE_SIZE for a plain
-# 1 GiB device copy (calibration).
+# 1 GiB device copy (calibration).  A workload may carry a forced split count
+# as NAME:sN (e.g. long_ctx:s64); its files are tagged NAME_sN.
 # usage: bash paged_kv_split_amd/profiling/collect.sh OUTDIR WORKLOAD...
 set -u
 cd "$(dirname "$0")/../.." || exit 1
@@ -12,7 +13,7 @@ export TMPDIR=/tmp
 out=$1
 shift
 mkdir -p "$out"
-BENCH="python3 -u bench.py --warmup 3 --runs 1 --no-cpu-baseline"
+BENCH="python3 -u bench.py --warmup 3 --runs 1 --no-cpu-baseline --no-configs"
 
 step() {  # step TAG LIMIT_SECONDS COMMAND...
   local tag=$1 lim=$2
@@ -31,18 +32,28 @@ step copy_fetch 120 rocprofv3 --pmc FETCH_SIZE -d "$out/copy_fetch" -o copy_fetc
   python3 -u bench.py --copy-calibration 1073741824
 step copy_write 120 rocprofv3 --pmc WRITE_SIZE -d "$out/copy_write" -o copy_write --output-format csv -- \
   python3 -u bench.py --copy-calibration 1073741824
-for wl in "$@"; do
+for key in "$@"; do
+  wl=${key%%:*}
+  extra=""
+  tag=$wl
+  if [ "$key" != "$wl" ]; then
+    extra="--splits ${key##*:s}"
+    tag="${wl}_s${key##*:s}"
+  fi
+  BW="$BENCH $extra"
+  wl=$tag
+  name=${key%%:*}
   step "${wl}_trace" 300 rocprofv3 --kernel-trace --stats -d "$out/${wl}_trace" -o trace --output-format csv -- \
-    $BENCH --workload "$wl" --steps 20
+    $BW --workload "$name" --steps 20
   step "${wl}_fetch" 120 rocprofv3 --pmc FETCH_SIZE -d "$out/${wl}_fetch" -o fetch --output-format csv -- \
-    $BENCH --workload "$wl" --steps 4
+    $BW --workload "$name" --steps 4
   step "${wl}_write" 120 rocprofv3 --pmc WRITE_SIZE -d "$out/${wl}_write" -o write --output-format csv -- \
-    $BENCH --workload "$wl" --steps 4
+    $BW --workload "$name" --steps 4
   step "${wl}_sq" 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT \
     SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE MfmaUtil -d "$out/${wl}_sq" -o sq --output-format csv -- \
-    $BENCH --workload "$wl" --steps 4
+    $BW --workload "$name" --steps 4
   step "${wl}_issue" 120 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 \
     SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE \
-    -d "$out/${wl}_issue" -o issue --output-format csv -- $BENCH --workload "$wl" --steps 4
+    -d "$out/${wl}_issue" -o issue --output-format csv -- $BW --workload "$name" --steps 4
 done
 echo "collected in $out" >&2

@@ -71,7 +71,10 @@ def calibration(out):
             "fetch_scale": COPY_BYTES / (copy_f * 1024), "write_scale": COPY_BYTES / (copy_w * 1024)}
 
 
-def summarize(out, profiles, wl, cal, command):
+def summarize(out, profiles, key, cal, command):
+    """Summary of one workload key (NAME or NAME:sN, a forced split count;
+    its collected files are tagged NAME_sN)."""
+    wl = key.replace(":", "_")
     stats = _csv(f"{out}/{wl}_trace/*kernel_stats.csv")
     ours = [r for r in stats if any(t in r["Name"] for t in OURS)]
     with open(f"{out}/{wl}_trace.out") as fh:

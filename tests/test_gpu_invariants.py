@@ -212,6 +212,37 @@ def test_runs_on_the_given_stream_in_order():
     assert np.array_equal(out16, ref16)
 
 
+def test_wrapper_allocates_on_the_call_stream():
+    """A call on a side stream that lets the wrapper allocate its output and
+    split workspace: both are allocated with that stream current, so the
+    workspace's zero fill runs on it ahead of the kernel.  The current stream
+    is kept busy and holds a freed block of the workspace's size filled with
+    non-zero counters; were the fill queued there (or that block handed to
+    the side stream), the kernel would start on stale counters."""
+    w = workloads.build("side_stream", B=8, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+                        kv_lens=[2048, 1900, 700, 2048, 33, 1500, 2048, 1024], seed=3091)
+    p = problem(w, 0)
+    S = pkv.num_splits_for(p)
+    assert S > 1 and pkv.merges_in_kernel(p, S)
+    ref16, _ = run(w, num_splits=S)
+    d = dev_tensors(w)
+    _, mb = pkv.workspace_bytes(problem(w, S), S)
+    junk = torch.full((mb // 4,), 1.0, dtype=torch.float32, device="cuda:0")   # counters 0x3f800000
+    del junk                                   # back to the current stream's pool
+    big = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    note("side stream call with wrapper-allocated workspace")
+    for _ in range(20):
+        big.mul_(1.0001)                       # the current stream stays busy
+    out = pkv.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["kl"], scale=w.scale, num_splits=S,
+                           max_kv_len=w.max_kv_len, stream=s)
+    s.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, ref16)
+
+
 def test_concurrent_calls_on_two_streams():
     """The library keeps no state between calls: two problems, each with its
     own outputs and split workspace (in-kernel merge counters included), run

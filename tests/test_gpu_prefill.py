@@ -129,3 +129,13 @@ def test_whole_sequence_causal_prefill_of_2048_tokens(splits):
     w = workloads.build("long_prefill", B=1, q_len=2048, Hq=8, Hkv=1, D=64, page_size=64, kv_lens=[2048],
                         seed=4400).replace(causal_offset=LAST)
     compare(w, splits)
+
+
+def test_prefill_workload_at_full_size_every_row():
+    """The benchmark's prefill workload as timed (4 sequences of 4096 keys
+    whose last 512 are a chunk of query tokens, Hq = 32, Hkv = 8, D = 128,
+    the library's own split count and grouping): every row of every sequence
+    against the oracle."""
+    w = workloads.prefill()
+    errs = compare(w)
+    note(f"prefill workload: max err fp32 {errs['err32']:.3e} bf16 {errs['err16']:.3e}")

@@ -6,11 +6,12 @@ import numpy as np
 import pytest
 
 import oracle
+import paged_kv_split_amd as pkv
 import workloads
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, note, run, run_varlen  # noqa: E402
+from gpu_util import check, note, problem, run, run_varlen  # noqa: E402
 
 LAST = workloads.CAUSAL_LAST
 
@@ -81,6 +82,29 @@ def test_equal_counts_are_the_fixed_batch_bit_for_bit():
     lv16, lv32 = run_varlen(last.replace(q_lens=np.full(5, 3, np.int32)), num_splits=3)
     assert np.array_equal(l16, f16) and np.array_equal(l32.view(np.uint32), f32.view(np.uint32))
     assert np.array_equal(lv16, v16) and np.array_equal(lv32.view(np.uint32), v32.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", ["long_mha_d64", "gqa_causal_last"])
+def test_equal_counts_auto_splits_bit_for_bit(shape):
+    """Every sequence with q_len tokens and the split count and grouping left
+    to the library: the varlen call follows pkv_paged_decode's plan (the
+    first shape is one where a varlen-only key cap once gave 32 splits
+    against 8) and gives the same bits."""
+    if shape == "long_mha_d64":
+        w = workloads.build("eq_auto_long", B=4, q_len=1, Hq=8, Hkv=8, D=64, page_size=32,
+                            kv_lens=[32768] * 4, seed=3210)
+    else:
+        w = workloads.build("eq_auto_gqa", B=6, q_len=3, Hq=32, Hkv=8, D=128, page_size=32,
+                            kv_lens=[5000, 37, 2049, 8000, 640, 3], seed=3211, causal="last", mask="2d")
+    p = problem(w, 0)
+    fx = pkv.plan(p)
+    vl = pkv.plan_varlen(p, w.B * w.q_len)
+    assert (vl.splits, vl.heads_per_block) == (fx.splits, fx.heads_per_block)
+    note(f"varlen equal counts, auto splits: {shape} S={fx.splits} hpb={fx.heads_per_block}")
+    f16, f32 = run(w)
+    v16, v32 = run_varlen(w.replace(q_lens=np.full(w.B, w.q_len, np.int32)))
+    assert np.array_equal(v16.reshape(f16.shape), f16)
+    assert np.array_equal(v32.reshape(f32.shape).view(np.uint32), f32.view(np.uint32))
 
 
 def test_causal_last_with_fewer_keys_than_tokens_fixed_entry():

@@ -2,9 +2,8 @@
 no GPU): every plan pkv_plan / pkv_plan_varlen returns is one the kernels
 can run, the split count covers the longest sequence, the in-kernel merge is
 taken only when its counters fit the workspace head, the workspace sizes
-follow the documented layout, and a varlen batch that holds every token
-splits at least as finely as the fixed-length batch (the varlen rule adds a
-cap on the keys per workgroup)."""
+follow the documented layout, and a varlen batch that holds every token is
+planned exactly as the fixed-length batch."""
 import math
 
 from hypothesis import given, settings, strategies as st
@@ -79,7 +78,18 @@ def test_every_varlen_plan_is_runnable(p, frac):
     tokens = int(round(frac * total))
     pl = pkv.plan_varlen(p, tokens, CUS)
     _check_plan(p, pl)
-    if tokens == total and p.num_splits == 0 and p.heads_per_block:
-        # every token present: the varlen rule only adds a cap on the keys
-        # per workgroup to the fixed-length split count
-        assert pl.splits >= pkv.plan(p, CUS).splits
+    if tokens == total:
+        # every token present: the plan of the fixed-length batch, field for field
+        fx = pkv.plan(p, CUS)
+        assert [getattr(pl, f) for f, _ in pkv.PlanInfo._fields_] == \
+            [getattr(fx, f) for f, _ in pkv.PlanInfo._fields_]
+
+
+@settings(max_examples=200, deadline=None, derandomize=True)
+@given(problems())
+def test_varlen_plan_with_every_token_is_the_fixed_plan(p):
+    """A varlen batch holding all B * q_len tokens is planned exactly as the
+    fixed-length batch (so the two entry points give it the same bits)."""
+    fx = pkv.plan(p, CUS)
+    vl = pkv.plan_varlen(p, p.batch * p.q_len, CUS)
+    assert [getattr(vl, f) for f, _ in pkv.PlanInfo._fields_] == [getattr(fx, f) for f, _ in pkv.PlanInfo._fields_]
