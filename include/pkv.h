@@ -30,10 +30,13 @@
  *    kernels on it, so they may be captured into a hipGraph.  Kernel arguments depend only on
  *    host values, so device data (kv_lens, block_table, q, K/V, mask) may
  *    change between graph replays.
- *  - Every host-side check runs before any HIP call; a failed check returns
- *    its status with nothing enqueued.  There are no exceptions, aborts or
- *    prints.  The library is stateless apart from a per-device cache of the
- *    compute-unit count, and is thread-safe.
+ *  - Every host-side check runs before any launch (the only other HIP calls
+ *    are queries: the current device, its compute-unit count and, for
+ *    pkv_paged_decode_noalloc, the address of its static workspace); a failed
+ *    check returns its status with nothing enqueued.  There are no
+ *    exceptions, aborts or prints.  The library is stateless apart from a
+ *    per-device cache of the compute-unit count and the static workspace of
+ *    pkv_paged_decode_noalloc, and is thread-safe.
  *  - Caller contract (not checkable without a device sync): block-table
  *    entries for the pages that hold keys j < kv_lens[b] are in
  *    [0, num_pages); 0 <= kv_lens[b] <= max_kv_len; causal_offsets[b] >= -1.
@@ -63,7 +66,8 @@ enum {
   PKV_ERR_WORKSPACE = 4,   /* o_part / ml_part missing or smaller than pkv_workspace_bytes */
   PKV_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
   PKV_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
-  PKV_ERR_DEVICE = 7       /* querying the current device failed */
+  PKV_ERR_DEVICE = 7,      /* querying the current device failed */
+  PKV_ERR_SCRATCH = 8      /* pkv_paged_decode_noalloc: the split workspace exceeds PKV_NOALLOC_SCRATCH_BYTES */
 };
 
 #define PKV_MAX_SPLITS 256
@@ -183,6 +187,35 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                      const float *mask, float *o_part, size_t o_part_bytes,
                      float *ml_part, size_t ml_part_bytes, void *out_bf16,
                      float *out_f32, hipStream_t stream);
+
+/* Size of the static split workspace of pkv_paged_decode_noalloc: one array
+ * of this many bytes per GPU the library runs on, held until the process
+ * ends. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* pkv_paged_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under hipGraph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split partials and merge counters
+ * live in a static device array of PKV_NOALLOC_SCRATCH_BYTES bytes per GPU
+ * (its address looked up once per device, on the first call with that device
+ * current); the call allocates nothing, and the caller passes only inputs and
+ * outputs.  The plan, kernels and results are those of pkv_paged_decode on
+ * the same problem, bit for bit.
+ *  - Size limit: with S > 1 splits (pkv_plan), pkv_workspace_bytes(p, S)'s
+ *    ml_part bytes rounded up to 256 plus its o_part bytes must not exceed
+ *    PKV_NOALLOC_SCRATCH_BYTES, else PKV_ERR_SCRATCH with nothing enqueued
+ *    (one split needs no workspace and has no limit).
+ *  - Shared state: every call on one GPU uses that GPU's one array, which
+ *    keeps the last call's contents.  The first call on a device clears the
+ *    merge counters with a fill kernel on its stream; every call leaves them
+ *    zero.  Calls that overlap on one GPU (unordered streams, threads) race
+ *    on the array and give undefined results: order them.
+ * Arguments and other statuses as for pkv_paged_decode. */
+int pkv_paged_decode_noalloc(const pkv_problem *p, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *kv_lens, const int32_t *causal_offsets,
+                             const float *mask, void *out_bf16, float *out_f32,
+                             hipStream_t stream);
 
 /* The launch plan of pkv_paged_decode_varlen for a batch of total_tokens
  * query tokens (0 .. B * q_len, else PKV_ERR_SHAPE): as pkv_plan, with the

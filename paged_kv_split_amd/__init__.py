@@ -24,6 +24,7 @@ PKV_ERR_WORKSPACE = 4
 PKV_ERR_ALIGN = 5
 PKV_ERR_LAUNCH = 6
 PKV_ERR_DEVICE = 7
+PKV_ERR_SCRATCH = 8
 PKV_MAX_SPLITS = 256
 PKV_COUNTER_BYTES = 16384
 PKV_MAX_FUSED_UNITS = PKV_COUNTER_BYTES // 4
@@ -31,10 +32,11 @@ PKV_KV_BLHD = 1
 PKV_KV_BHLD = 2
 PKV_MAX_CONTIGUOUS_KEYS = 1 << 30
 PKV_CAUSAL_LAST = -2
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_LAYOUTS = {"blhd": PKV_KV_BLHD, "bhld": PKV_KV_BHLD}
 
 EXPORTED = ("pkv_num_splits", "pkv_plan", "pkv_plan_varlen", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
-            "pkv_paged_decode_varlen", "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
+            "pkv_paged_decode_noalloc", "pkv_paged_decode_varlen", "pkv_contiguous_decode", "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus",
             "pkv_status_string")
 
 
@@ -101,6 +103,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, P, P, P]
         L.pkv_paged_decode_partials.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                                 ctypes.c_size_t, P]
+        L.pkv_paged_decode_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P]
         L.pkv_paged_decode_varlen.argtypes = [PP, P, ctypes.c_int64, P, P, P, P, P, P, P, P,
                                               ctypes.c_size_t, P, ctypes.c_size_t, P, P, P]
         L.pkv_contiguous_decode.argtypes = [PP, ctypes.c_int, ctypes.c_int64, P, P, P, P, P, P, P,
@@ -110,7 +113,7 @@ def lib() -> ctypes.CDLL:
         L.pkv_status_string.argtypes = [ctypes.c_int]
         L.pkv_status_string.restype = ctypes.c_char_p
         for name in ("pkv_num_splits", "pkv_plan", "pkv_plan_varlen", "pkv_workspace_bytes", "pkv_workspace_clear", "pkv_paged_decode",
-                     "pkv_paged_decode_varlen", "pkv_contiguous_decode",
+                     "pkv_paged_decode_noalloc", "pkv_paged_decode_varlen", "pkv_contiguous_decode",
                      "pkv_paged_decode_partials", "pkv_combine", "pkv_device_cus"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -202,6 +205,15 @@ def paged_decode_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block
                                   block_table or None, kv_lens or None, causal_offsets or None,
                                   mask or None, o_part or None, o_part_bytes, ml_part or None,
                                   ml_part_bytes, out_bf16 or None, out_f32 or None, stream or None)
+
+
+def paged_decode_noalloc_raw(problem: Problem, q: int, k_cache: int, v_cache: int, block_table: int,
+                             kv_lens: int, causal_offsets: int, mask: int, out_bf16: int, out_f32: int,
+                             stream: int) -> int:
+    """pkv_paged_decode_noalloc on raw addresses (0 = NULL); returns the status code."""
+    return lib().pkv_paged_decode_noalloc(ctypes.byref(problem), q or None, k_cache or None, v_cache or None,
+                                          block_table or None, kv_lens or None, causal_offsets or None,
+                                          mask or None, out_bf16 or None, out_f32 or None, stream or None)
 
 
 def paged_decode_varlen_raw(problem: Problem, cu_q_lens: int, total_tokens: int, q: int, k_cache: int,

@@ -304,6 +304,7 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_ALIGN: return "pointer misaligned";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_DEVICE: return "device query failed";
+    case PKV_ERR_SCRATCH: return "split workspace exceeds the static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -570,6 +571,63 @@ int pkv_paged_decode(const pkv_problem *p, const void *q, const void *k_cache,
                    kv_lens, causal_offsets, mask, o_part, o_part_bytes, ml_part, ml_part_bytes, out_bf16, out_f32,
                    false, &a);
   if (rc) return rc;
+  return launch_all(a, p, o_part, out_bf16, out_f32, stream);
+}
+
+int pkv_paged_decode_noalloc(const pkv_problem *p, const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_table, const int32_t *kv_lens, const int32_t *causal_offsets,
+                             const float *mask, void *out_bf16, float *out_f32, hipStream_t stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->batch == 0) return PKV_OK;
+  // the split count (the workspace size follows from it)
+  int S = p->num_splits;
+  if (S == 0) {
+    int cus = 0;
+    rc = query_cus(&cus);
+    if (rc) return rc;
+    S = make_plan(p, cus).S;
+  }
+  // the static workspace: ml_part (counter head + (m, l)) first, then o_part
+  size_t ob = 0, mb = 0, mb_al = 0;
+  if (S > 1) {
+    const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
+    ob = rows * (size_t)S * (size_t)p->head_dim * sizeof(float);
+    mb = ml_bytes_split(p, S);
+    mb_al = (mb + 255) & ~(size_t)255;
+    if (mb_al > PKV_NOALLOC_SCRATCH_BYTES || ob > PKV_NOALLOC_SCRATCH_BYTES - mb_al) return PKV_ERR_SCRATCH;
+  }
+  // plan_decode plans from the caller's problem as pkv_paged_decode does (it
+  // finds the same split count); forcing S here would change the heads-per-
+  // workgroup choice, which depends on whether the split count was forced
+  const QSource qs{nullptr, (int64_t)p->batch * p->q_len};
+  const KvSource src{k_cache, v_cache, block_table, 0, 0};
+  pkv::DecodeArgs a;
+  // every argument check first, on a placeholder workspace address (256-byte
+  // aligned, never dereferenced): the static array is looked up only for a
+  // call that will launch
+  char *const placeholder = reinterpret_cast<char *>((uintptr_t)1 << 20);
+  float *o_part = S > 1 ? reinterpret_cast<float *>(placeholder + mb_al) : nullptr;
+  float *ml_part = S > 1 ? reinterpret_cast<float *>(placeholder) : nullptr;
+  rc = plan_decode(p, q, qs, src, kv_lens, causal_offsets, mask, o_part, ob, ml_part, mb, out_bf16, out_f32, false,
+                   &a);
+  if (rc) return rc;
+  bool cleared = true;
+  if (S > 1) {
+    void *base = nullptr;
+    rc = pkv::noalloc_scratch(&base, &cleared);
+    if (rc) return rc;
+    ml_part = static_cast<float *>(base);
+    o_part = reinterpret_cast<float *>(static_cast<char *>(base) + mb_al);
+    rc = plan_decode(p, q, qs, src, kv_lens, causal_offsets, mask, o_part, ob, ml_part, mb, out_bf16, out_f32,
+                     false, &a);
+    if (rc) return rc;
+  }
+  if (!cleared) {  // first use on this device: zero the merge counters ahead of the kernel
+    (void)hipGetLastError();
+    if (pkv::launch_zero(ml_part, PKV_COUNTER_BYTES / 4, stream) != hipSuccess) return PKV_ERR_LAUNCH;
+    pkv::noalloc_mark_cleared();
+  }
   return launch_all(a, p, o_part, out_bf16, out_f32, stream);
 }
 

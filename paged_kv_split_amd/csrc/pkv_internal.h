@@ -101,4 +101,10 @@ int launch_split_prefill(const DecodeArgs &a, int head_dim, bool causal, bool ha
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
 int launch_zero(void *p, int64_t words, hipStream_t stream);
 
+// The static split workspace of pkv_paged_decode_noalloc (pkv_noalloc.hip):
+// the current device's copy of the scratch array (looked up once per device)
+// and whether its counter head has been zeroed yet; returns a PKV status.
+int noalloc_scratch(void **ptr, bool *cleared);
+void noalloc_mark_cleared();
+
 }  // namespace pkv

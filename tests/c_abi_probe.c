@@ -62,8 +62,9 @@ int main(void) {
   FIELD(pkv_plan_info, kernels);
   printf("const %d %d %d %d %d %d %d\n", PKV_MAX_SPLITS, PKV_CAUSAL_LAST, PKV_COUNTER_BYTES, PKV_MAX_FUSED_UNITS,
          PKV_KV_BLHD, PKV_KV_BHLD, PKV_MAX_CONTIGUOUS_KEYS);
-  printf("status %d %d %d %d %d %d %d %d\n", PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED,
-         PKV_ERR_WORKSPACE, PKV_ERR_ALIGN, PKV_ERR_LAUNCH, PKV_ERR_DEVICE);
+  printf("status %d %d %d %d %d %d %d %d %d\n", PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED,
+         PKV_ERR_WORKSPACE, PKV_ERR_ALIGN, PKV_ERR_LAUNCH, PKV_ERR_DEVICE, PKV_ERR_SCRATCH);
+  printf("scratch %llu\n", (unsigned long long)PKV_NOALLOC_SCRATCH_BYTES);
 
   pkv_problem p = decode_problem();
   pkv_plan_info info;

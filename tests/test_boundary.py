@@ -257,8 +257,8 @@ def test_combine_argument_checks():
 
 
 def test_status_strings_are_distinct():
-    msgs = {pkv.status_string(s) for s in range(8)}
-    assert len(msgs) == 8
+    msgs = {pkv.status_string(s) for s in range(9)}
+    assert len(msgs) == 9
     assert pkv.status_string(99) == "unknown status"
 
 
@@ -380,3 +380,36 @@ def test_grouping_needs_short_splits():
     assert (pl.splits, pl.heads_per_block, pl.rows_per_block) == (8, 1, 16)
     p.heads_per_block = 2
     assert pkv.plan(p, 256).splits == 2
+
+
+def call_noalloc(p, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, kl=FAKE, co=0, mask=0, out=FAKE, out32=0)
+    a.update(ptrs)
+    return pkv.paged_decode_noalloc_raw(p, a["q"], a["k"], a["v"], a["bt"], a["kl"], a["co"], a["mask"],
+                                        a["out"], a["out32"], 0)
+
+
+def test_noalloc_argument_checks():
+    """pkv_paged_decode_noalloc checks its arguments as pkv_paged_decode does,
+    before anything touches a device, and refuses a split workspace larger
+    than its static buffer."""
+    p = base_problem(num_splits=3)
+    assert call_noalloc(p, q=0) == pkv.PKV_ERR_NULL
+    assert call_noalloc(p, out=0) == pkv.PKV_ERR_NULL
+    assert call_noalloc(p, k=FAKE + 2) == pkv.PKV_ERR_ALIGN
+    assert call_noalloc(base_problem(q_len=0)) == pkv.PKV_ERR_SHAPE
+    assert call_noalloc(base_problem(head_dim=48, num_splits=1)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call_noalloc(base_problem(batch=0), q=0, k=0, v=0, bt=0, kl=0, out=0) == pkv.PKV_OK
+    # the limit: ml_part bytes rounded to 256, then o_part bytes
+    big = base_problem(batch=64, q_len=4, num_q_heads=64, num_kv_heads=8, head_dim=128, num_pages=64 * 4,
+                       max_pages_per_seq=4, max_kv_len=128)
+    for S in (2, 4, 7, 8, 64):
+        big.num_splits = S           # 8 MiB of o_part per split, plus (m, l) and the counters
+        ob, mb = pkv.workspace_bytes(big, S)
+        fits = (mb + 255) // 256 * 256 + ob <= pkv.PKV_NOALLOC_SCRATCH_BYTES
+        assert fits == (S <= 7), S
+        if not fits:
+            assert call_noalloc(big) == pkv.PKV_ERR_SCRATCH
+    # one split needs no workspace: no limit applies
+    big.num_splits = 1
+    assert call_noalloc(big, q=0) == pkv.PKV_ERR_NULL

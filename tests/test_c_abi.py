@@ -56,7 +56,8 @@ def test_constants_match_the_binding(probe):
     c = list(map(int, probe["const"]))
     assert c == [pkv.PKV_MAX_SPLITS, pkv.PKV_CAUSAL_LAST, pkv.PKV_COUNTER_BYTES, pkv.PKV_COUNTER_BYTES // 4,
                  pkv.PKV_KV_BLHD, pkv.PKV_KV_BHLD, 1 << 30]
-    assert list(map(int, probe["status"])) == list(range(8))
+    assert list(map(int, probe["status"])) == list(range(9))
+    assert int(probe["scratch"][0]) == pkv.PKV_NOALLOC_SCRATCH_BYTES
 
 
 def _decode_problem(**kw):
