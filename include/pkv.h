@@ -62,7 +62,7 @@ enum {
   PKV_OK = 0,
   PKV_ERR_NULL = 1,        /* a required pointer is NULL */
   PKV_ERR_SHAPE = 2,       /* bad dimension, Hq % Hkv != 0, Hkv % heads_per_block != 0, Hkv * D > 2^24, max_kv_len too big, bad stride */
-  PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS, heads_per_block not in {0, 1, 2, 4} */
+  PKV_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, page_size not a power of two in [1, 4096], splits > PKV_MAX_SPLITS, heads_per_block not in {0, 1, 2, 4, 8} (8: head_dim <= 64) */
   PKV_ERR_WORKSPACE = 4,   /* o_part / ml_part missing or smaller than pkv_workspace_bytes */
   PKV_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
   PKV_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
@@ -106,9 +106,10 @@ typedef struct pkv_problem {
   int32_t num_splits;        /* 0 heuristic; 1..PKV_MAX_SPLITS forced */
   int64_t mask_stride_b;     /* mask element stride between sequences (>= 0) */
   int64_t mask_stride_q;     /* mask element stride between query tokens; 0 => 2D [B, kv] mask */
-  int32_t heads_per_block;   /* kv heads per split workgroup: 0 heuristic; 1, 2 or 4 forced
-                                (must divide num_kv_heads); a launch-shape choice only, the
-                                results do not depend on it beyond rounding order */
+  int32_t heads_per_block;   /* kv heads per split workgroup: 0 heuristic; 1, 2, 4 or 8 forced
+                                (must divide num_kv_heads; 8 needs head_dim <= 64); a
+                                launch-shape choice only, the results do not depend on it
+                                beyond rounding order */
 } pkv_problem;
 
 /* Number of splits pkv_paged_decode uses for this problem on a device with
@@ -123,7 +124,7 @@ int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out);
  * heads_per_block are reported unchanged. */
 typedef struct pkv_plan_info {
   int32_t splits;           /* key splits per sequence */
-  int32_t heads_per_block;  /* kv heads per split workgroup (1, 2 or 4) */
+  int32_t heads_per_block;  /* kv heads per split workgroup (1, 2, 4 or 8) */
   int32_t rows_per_block;   /* packed query rows (G * q_len) per kv head per workgroup:
                                1 or 2 (vector kernel), 16 or 32 (matrix-core kernel),
                                128 (prefill-shaped matrix-core kernel: from 128 rows on at
@@ -134,7 +135,20 @@ typedef struct pkv_plan_info {
   int64_t workgroups;       /* split-kernel workgroups: units * splits */
   int32_t merge_in_kernel;  /* 1: the split kernel merges the splits itself */
   int32_t kernels;          /* kernel launches per pkv_paged_decode call (0 when batch == 0) */
+  int32_t kernel;           /* the split kernel: PKV_KERNEL_* below */
 } pkv_plan_info;
+
+/* pkv_plan_info.kernel: the vector kernel (1 or 2 rows per kv head); the
+ * one-head matrix-core kernel (16 or 32 rows of one kv head per wave, each
+ * wave its own key tiles); the shared-tile matrix-core kernel (a workgroup
+ * of 4 or 8 kv heads whose waves share each K/V tile of the whole head group,
+ * read as contiguous runs of the page slots, through LDS: 8 kv heads per
+ * workgroup, or 4 from 3 rows per kv head on at head_dim <= 128); the
+ * prefill-shaped matrix-core kernel (128 rows of one kv head). */
+#define PKV_KERNEL_VECTOR 0
+#define PKV_KERNEL_MATRIX 1
+#define PKV_KERNEL_SHARED_TILE 2
+#define PKV_KERNEL_PREFILL 3
 
 int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info);
 

@@ -32,6 +32,12 @@ PKV_KV_BLHD = 1
 PKV_KV_BHLD = 2
 PKV_MAX_CONTIGUOUS_KEYS = 1 << 30
 PKV_CAUSAL_LAST = -2
+PKV_KERNEL_VECTOR = 0
+PKV_KERNEL_MATRIX = 1
+PKV_KERNEL_SHARED_TILE = 2
+PKV_KERNEL_PREFILL = 3
+KERNEL_NAMES = {PKV_KERNEL_VECTOR: "split_decode_valu", PKV_KERNEL_MATRIX: "split_decode_mfma",
+                PKV_KERNEL_SHARED_TILE: "split_decode_group", PKV_KERNEL_PREFILL: "split_prefill_mfma"}
 PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_LAYOUTS = {"blhd": PKV_KV_BLHD, "bhld": PKV_KV_BHLD}
 
@@ -78,6 +84,7 @@ class PlanInfo(ctypes.Structure):
         ("workgroups", ctypes.c_int64),
         ("merge_in_kernel", ctypes.c_int32),
         ("kernels", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
     ]
 
 
@@ -506,10 +513,7 @@ def merges_in_kernel(problem: Problem, splits: int, num_cus: int = 0) -> bool:
 
 def kernel_family(problem: Problem) -> str:
     """Which split kernel serves the problem (pkv_plan)."""
-    pl = plan(problem)
-    if pl.rows_per_block == 128:
-        return "split_prefill_mfma"
-    return "split_decode_mfma" if pl.matrix_core else "split_decode_valu"
+    return KERNEL_NAMES[plan(problem).kernel]
 
 
 def num_splits_for(problem: Problem) -> int:

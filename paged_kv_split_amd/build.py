@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("pkv_host.cpp", "pkv_decode.hip", "pkv_decode_mfma.hip",
-                                           "pkv_noalloc.hip")]
+                                           "pkv_decode_group.hip", "pkv_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -46,11 +46,12 @@
 
 namespace pkv {
 
-int rows_per_block(int R, int head_dim, int forced_hpb) {
-  if (R <= 1) return 1;
-  if (R <= 2) return 2;
-  if (use_prefill(R, head_dim, forced_hpb)) return kPrefillRows;
-  return R <= 16 ? 16 : 32;
+int rows_per_block(int R, int head_dim, int hpb) {
+  switch (kernel_kind(R, head_dim, hpb)) {
+    case kKernelPrefill: return kPrefillRows;
+    case kKernelValu: return R <= 1 ? 1 : 2;
+    default: return R <= 16 ? 16 : 32;
+  }
 }
 
 // Keys per VALU wave tile (one QK pass: 64 / (D/32)), never below the
@@ -377,14 +378,18 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs &a, const Ctx<D, R
 template <int D, int RP>
 constexpr int valu_nbuf() { return 2; }
 
-// The key-tile loop of one wave (tiles t0, t0 + tstep, ...), NBUF register
-// tiles in a ring: while tile i computes, the loads of tiles i+1 .. i+NBUF-1
-// are in flight; after it, its registers take the loads of tile i+NBUF.  The loads are issued
-// unconditionally (a tile past the end loads the last key again, clamped in
-// load_tile) and in a fixed order, and a round has no early exit (a step past
-// the last tile computes a tile whose keys all get weight 0), so the number
-// of loads in flight is the same on every path into the loop header; a
-// conditional load or an exit there makes the compiler wait for all loads.
+// The key-tile loop of one wave (tiles t0, t0 + tstep, ... < ntiles), NBUF
+// register tiles in a ring: while tile i computes, the loads of tiles i+1 ..
+// i+NBUF-1 are in flight; after it, its registers take the loads of tile
+// i+NBUF.  Whole rounds run while every prefetch of the round is a tile of
+// this wave: their loads are issued unconditionally and in a fixed order, and
+// a round has no early exit, so the number of loads in flight is the same on
+// both paths into the loop header (a conditional load or an exit there makes
+// the compiler wait for all loads).  The last tiles are computed after the
+// loop with prefetches only of tiles that exist, so no load is left in flight
+// past the last tile (the epilogue would wait for it before reusing its
+// registers).  With fewer tiles than NBUF the first loads repeat the last key
+// (clamped in load_tile).
 template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, class Q, int NBUF = valu_nbuf<D, RP>()>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> &c, int b, int r0, int wb,
                                           int t0, int tstep, int ntiles, const Q &qrows, const int (&lim)[RP],
@@ -398,13 +403,27 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> 
     load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t0 + i * tstep) * T, tr[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int t = t0; t < ntiles; t += NBUF * tstep) {
+  int t = t0;
+  for (; t + (2 * NBUF - 1) * tstep < ntiles; t += NBUF * tstep) {
 #pragma unroll
     for (int i = 0; i < NBUF; ++i) {
       compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + (t + i * tstep) * T, tr[i], qrows, lim, pbuf, kbuf, st);
       load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (t + (i + NBUF) * tstep) * T, tr[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) {
+    const int tt = t + i * tstep;
+    if (tt < ntiles) {   // wave-uniform
+      compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + tt * T, tr[i], qrows, lim, pbuf, kbuf, st);
+      if (tt + NBUF * tstep < ntiles) load_tile<D, RP, MASK, UPAGE>(a, c, b, r0, wb + (tt + NBUF * tstep) * T, tr[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) {
+    const int tt = t + (NBUF + i) * tstep;
+    if (tt < ntiles) compute_tile<D, RP, CAUSAL, MASK>(a, c, wb + tt * T, tr[i], qrows, lim, pbuf, kbuf, st);
   }
 }
 

@@ -322,6 +322,142 @@ __device__ __forceinline__ bool work_exact(const DecodeArgs &a, int xcd, int slo
   return true;
 }
 
+// Longest first (a.lpt, with the exact schedule when every split past a
+// sequence's last key is trimmed): the same items, dealt in decreasing key
+// count so that the longest workgroups start first and the grid ends on short
+// ones.  An item's keys are those of its split: whole chunks for every split
+// but a sequence's last, which holds the rest.  Items fall in kLptBuckets
+// buckets -- whole chunks, then kLptBuckets - 1 equal ranges of partial
+// chunks -- taken from the largest down, sequence by sequence within a
+// bucket (split-major, row blocks adjacent within a sequence).  Item v goes
+// to block slot v / 8 of XCD v mod 8, so every XCD runs the same mix, longest
+// first.  Per-bucket counts are summed over the wave exactly in fp32 (counts
+// stay below 2^24); a wave prefix sum of the chosen bucket's counts then
+// finds the lane and sequence of the item.
+constexpr int kLptBuckets = 8;
+
+template <bool CAUSAL>
+__device__ __forceinline__ bool work_lpt(const DecodeArgs &a, int xcd, int slot, Work &w) {
+  constexpr int NB = kLptBuckets;
+  const int lane = threadIdx.x & 63;
+  const int k = (a.B + 63) >> 6;
+  const int b0 = lane * k;
+  int Lq[kExactPerLane], c0q[kExactPerLane], c1q[kExactPerLane], coq[kExactPerLane];
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    const int b = b0 + j;
+    const bool ok = j < k && b < a.B;
+    Lq[j] = ok ? a.kv_lens[b] : 0;
+    c0q[j] = ok && a.cu_q ? a.cu_q[b] : 0;
+    c1q[j] = ok && a.cu_q ? a.cu_q[b + 1] : 0;
+    coq[j] = ok && CAUSAL && a.causal_offsets ? a.causal_offsets[b] : -1;
+  }
+  // per sequence: row blocks, whole-chunk splits, bucket of its partial split
+  // (-1: none); per lane and bucket: items
+  int rbs[kExactPerLane], nfull[kExactPerLane], pbk[kExactPerLane];
+  int cnt[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) cnt[q] = 0;
+  int usum = 0;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    rbs[j] = 0;
+    nfull[j] = 0;
+    pbk[j] = -1;
+    if (j < k && b0 + j < a.B) {
+      const SeqRows sr = seq_rows_of<CAUSAL>(a, b0 + j, Lq[j], c0q[j], c1q[j], coq[j]);
+      rbs[j] = (sr.R + a.rp - 1) / a.rp;
+      const int kmax = sr.R > 0 ? row_keys(a, sr, Lq[j], sr.R - 1) : 0;
+      if (kmax <= 0) {  // no key: one split that writes zero rows
+        pbk[j] = 0;
+      } else {
+        nfull[j] = kmax / a.chunk;
+        const int rem = kmax - nfull[j] * a.chunk;
+        if (rem > 0) pbk[j] = (int)(((int64_t)rem * (NB - 1)) / a.chunk);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) cnt[q] += (q == NB - 1 ? nfull[j] * rbs[j] : 0) + (q == pbk[j] ? rbs[j] : 0);
+    usum += rbs[j];
+  }
+  const int uscan = wave_scan(usum);
+  int tot[NB];
+  int n_items = 0;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    tot[q] = (int)reduce_hi<0, OpSum>((float)cnt[q]);
+    n_items += tot[q];
+  }
+  const int kk = slot / a.inner;
+  const int v = kk * 8 + xcd;
+  if (v >= n_items) return false;
+  // the bucket of item v (whole chunks first, then the partial buckets from the largest)
+  int jv = 0, ov = v;
+  bool got = false;
+#pragma unroll
+  for (int q = NB - 1; q >= 0; --q) {
+    if (!got) {
+      if (ov < tot[q]) {
+        jv = q;
+        got = true;
+      } else {
+        ov -= tot[q];
+      }
+    }
+  }
+  int cj = 0;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) cj = q == jv ? cnt[q] : cj;
+  const int cscan = wave_scan(cj);
+  const uint64_t m = __builtin_amdgcn_ballot_w64(cscan > ov);
+  const int sel = __builtin_ctzll(m);
+  int off = ov - __builtin_amdgcn_readlane(cscan - cj, sel);
+  int ubase = __builtin_amdgcn_readlane(uscan - usum, sel);
+  bool found = false;
+  int jsel = 0, nrb = 1, nf = 0;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    const int r = __builtin_amdgcn_readlane(rbs[j], sel);
+    const int f = __builtin_amdgcn_readlane(nfull[j], sel);
+    const int pb = __builtin_amdgcn_readlane(pbk[j], sel);
+    const int c = jv == NB - 1 ? f * r : (pb == jv ? r : 0);
+    if (!found) {
+      if (off < c) {
+        found = true;
+        jsel = j;
+        nrb = r;
+        nf = f;
+      } else {
+        off -= c;
+        ubase += r;
+      }
+    }
+  }
+  int L = 0, c0 = 0, c1 = 0, co = -1;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    if (j == jsel) {
+      L = __builtin_amdgcn_readlane(Lq[j], sel);
+      c0 = __builtin_amdgcn_readlane(c0q[j], sel);
+      c1 = __builtin_amdgcn_readlane(c1q[j], sel);
+      co = __builtin_amdgcn_readlane(coq[j], sel);
+    }
+  }
+  w.b = sel * k + jsel;
+  if (jv == NB - 1) {
+    w.s = off / nrb;
+    w.rg = off - w.s * nrb;
+  } else {  // the sequence's partial split
+    w.s = nf;
+    w.rg = off;
+  }
+  w.hg = slot - kk * a.inner;
+  w.unit = (ubase + w.rg) * a.inner + w.hg;
+  w.L = L;
+  w.sr = seq_rows_of<CAUSAL>(a, w.b, L, c0, c1, co);
+  return true;
+}
+
 // The schedule of a workgroup.  Exact (above) when a.exact; otherwise one
 // block per (sequence, split) pair and unit slot (kv-head group, row block),
 // the pairs in split-major order (decode_pair), whose empty blocks exit.
@@ -335,7 +471,7 @@ __device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
   const int x = blockIdx.x;
   const int xcd = x & 7;
   const int slot = x >> 3;
-  if (a.exact) return work_exact<CAUSAL>(a, xcd, slot, w);
+  if (a.exact) return a.lpt ? work_lpt<CAUSAL>(a, xcd, slot, w) : work_exact<CAUSAL>(a, xcd, slot, w);
   int inner_idx, outer_idx;
   if (a.outer >= 8) {
     inner_idx = slot % a.inner;

@@ -60,7 +60,9 @@ int check_problem(const pkv_problem *p) {
   if (p->num_splits > PKV_MAX_SPLITS) return PKV_ERR_UNSUPPORTED;
   if (p->heads_per_block < 0) return PKV_ERR_SHAPE;
   if (p->heads_per_block > 0) {
-    if (!is_pow2(p->heads_per_block) || p->heads_per_block > pkv::kMaxHeadsPerBlock) return PKV_ERR_UNSUPPORTED;
+    if (!is_pow2(p->heads_per_block) || p->heads_per_block > pkv::kMaxGroupHeads) return PKV_ERR_UNSUPPORTED;
+    // eight kv heads per workgroup: the shared-tile kernel, built for D <= 64
+    if (p->heads_per_block == 8 && p->head_dim > 64) return PKV_ERR_UNSUPPORTED;
     if (p->num_kv_heads % p->heads_per_block) return PKV_ERR_SHAPE;
   }
   if (p->mask_stride_b < 0 || p->mask_stride_q < 0) return PKV_ERR_SHAPE;
@@ -120,29 +122,39 @@ int split_cap_keys(int rows) {
 // The prefill-shaped kernel: one, its 128-row workgroups being compute-heavy
 // (4 x 64 tokens over 2048 keys: 4 splits 52 us, 8 splits 68 us; 8 x 32 over
 // 8192: 109 against 123 us).
-int blocks_per_cu(const pkv_problem *p) {
+// The shared-tile kernel (two workgroups of at most 80 KB of LDS per CU): two.
+int blocks_per_cu(const pkv_problem *p, int hpb) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 1;
-  if (pkv::use_mfma(R)) return p->head_dim == 128 ? 1 : 2;
-  return 1;
+  switch (pkv::kernel_kind(R, p->head_dim, hpb)) {
+    case pkv::kKernelPrefill: return 1;
+    case pkv::kKernelGroup: return 2;
+    case pkv::kKernelMfma: return p->head_dim == 128 ? 1 : 2;
+    default: return 1;
+  }
 }
 
-// Packed rows per workgroup (the kernel family follows from it).
-int rows_per_block_of(const pkv_problem *p) {
+// The kernel serving the problem with hpb kv heads per workgroup.
+int kernel_of(const pkv_problem *p, int hpb) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  return pkv::rows_per_block(R, p->head_dim, p->heads_per_block);
+  return pkv::kernel_kind(R, p->head_dim, hpb);
+}
+
+// Packed rows per workgroup and kv head (the kernel family follows from it).
+int rows_per_block_of(const pkv_problem *p, int hpb) {
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  return pkv::rows_per_block(R, p->head_dim, hpb);
 }
 
 // Row blocks per kv head.
-int64_t row_blocks(const pkv_problem *p) {
+int64_t row_blocks(const pkv_problem *p, int hpb) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  return ceil_div(R, rows_per_block_of(p));
+  return ceil_div(R, rows_per_block_of(p, hpb));
 }
 
 // (sequence, kv-head group, row block) units with hpb kv heads per group:
 // the workgroups of one unit differ only in their split.
 int64_t units_of(const pkv_problem *p, int hpb) {
-  return (int64_t)p->batch * (p->num_kv_heads / hpb) * row_blocks(p);
+  return (int64_t)p->batch * (p->num_kv_heads / hpb) * row_blocks(p, hpb);
 }
 
 // Varlen batches up to this size take the exact schedule (every workgroup
@@ -155,22 +167,26 @@ int64_t units_of(const pkv_problem *p, int hpb) {
 // at 4 splits (2-5%) and lost elsewhere (the same batch at 8 splits 8-13%,
 // other ragged shapes 1-3%, the 1B decode shape 10.0 -> 11.0 us).
 constexpr int kExactMaxBatch = 64 * 4;
+// Fixed-length batches from this many sequences on also take the exact
+// schedule, dealt longest first (their lengths may differ widely; the
+// workgroups of the longest splits then start first).
+constexpr int kLptMinBatch = 32;
 
 // Row-block slots the grid holds: B * ceil(R / rp); a varlen batch of
 // `tokens` tokens under the exact schedule at most floor(tokens * G / rp) + B
 // (sequence b has ceil(n_b * G / rp) <= floor(n_b * G / rp) + 1 row blocks).
-int64_t row_block_slots(const pkv_problem *p, int64_t tokens) {
-  const int64_t all = (int64_t)p->batch * row_blocks(p);
+int64_t row_block_slots(const pkv_problem *p, int64_t tokens, int hpb) {
+  const int64_t all = (int64_t)p->batch * row_blocks(p, hpb);
   if (tokens < 0 || p->batch > kExactMaxBatch) return all;
   const int G = p->num_q_heads / p->num_kv_heads;
-  const int rp = rows_per_block_of(p);
+  const int rp = rows_per_block_of(p, hpb);
   const int64_t nv = tokens * G / rp + p->batch;
   return nv < all ? nv : all;
 }
 
 // Units of the grid: (sequence, kv-head group, row block) slots.
 int64_t grid_units(const pkv_problem *p, int hpb, int64_t tokens) {
-  return row_block_slots(p, tokens) * (p->num_kv_heads / hpb);
+  return row_block_slots(p, tokens, hpb) * (p->num_kv_heads / hpb);
 }
 
 // The work the split heuristic sizes the grid for: (sequence, kv-head group,
@@ -188,8 +204,8 @@ Load load_of(const pkv_problem *p, int hpb, int64_t tokens) {
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
   if (tokens < 0 || tokens >= (int64_t)p->batch * p->q_len) return Load{units_of(p, hpb), R};
-  int64_t rb = ceil_div(tokens * G, rows_per_block_of(p)) + p->batch;
-  const int64_t all = (int64_t)p->batch * row_blocks(p);
+  int64_t rb = ceil_div(tokens * G, rows_per_block_of(p, hpb)) + p->batch;
+  const int64_t all = (int64_t)p->batch * row_blocks(p, hpb);
   if (rb > all) rb = all;
   int64_t rows = ceil_div(tokens * G, rb);
   if (rows < 1) rows = 1;
@@ -200,13 +216,17 @@ int heuristic_splits(const pkv_problem *p, int cus, int hpb, int64_t tokens) {
   const Load ld = load_of(p, hpb, tokens);
   const int64_t units = ld.units;
   if (units <= 0 || tokens == 0) return 1;
-  const int64_t target = (int64_t)cus * blocks_per_cu(p);
+  const int64_t target = (int64_t)cus * blocks_per_cu(p, hpb);
   if (units >= target) {
     const int64_t s = ceil_div(max_len_of(p), split_cap_keys(ld.rows));
     return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
   }
+  // at least kMinTilesPerWave tiles per wave (the shared-tile kernel's waves
+  // all see every tile of the split)
   const int T = pkv::tile_keys(p->head_dim);
-  const int64_t min_keys = (int64_t)T * (pkv::kWavesPerBlock / hpb) * kMinTilesPerWave;
+  const int wpt = kernel_of(p, hpb) == pkv::kKernelGroup || hpb >= pkv::kWavesPerBlock
+                      ? 1 : pkv::kWavesPerBlock / hpb;
+  const int64_t min_keys = (int64_t)T * wpt * kMinTilesPerWave;
   const int64_t max_by_len = ceil_div(max_len_of(p), min_keys);
   int64_t s = target / units;
   if (s > max_by_len) s = max_by_len;
@@ -242,7 +262,7 @@ constexpr int64_t kMaxGroupedChunk = 2048;
 
 int max_heads_per_block(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
-  if (pkv::use_prefill(R, p->head_dim, p->heads_per_block)) return 1;
+  if (pkv::use_prefill(R, p->head_dim, 1)) return 1;
   if (pkv::use_mfma(R)) return (p->head_dim == 64 || p->head_dim == 128) ? 2 : 1;
   return p->head_dim <= 128 ? pkv::kMaxHeadsPerBlock : 1;
 }
@@ -339,12 +359,12 @@ int plan_query(const pkv_problem *p, int64_t tokens, int num_cus, pkv_plan_info 
     if (rc) return rc;
   }
   const Plan pl = make_plan(p, num_cus, tokens);
-  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
   *info = pkv_plan_info{};
   info->splits = pl.S;
   info->heads_per_block = pl.hpb;
-  info->rows_per_block = rows_per_block_of(p);
-  info->matrix_core = pkv::use_mfma(R) ? 1 : 0;
+  info->rows_per_block = rows_per_block_of(p, pl.hpb);
+  info->kernel = kernel_of(p, pl.hpb);
+  info->matrix_core = info->kernel == pkv::kKernelValu ? 0 : 1;
   info->units = pl.units;
   info->workgroups = pl.units * pl.S;
   info->merge_in_kernel = pl.fused ? 1 : 0;
@@ -450,12 +470,12 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
     pl = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1);
   }
   const int64_t tokens = qs.cu_q ? qs.total_tokens : -1;
-  const bool exact = tokens >= 0 && p->batch <= kExactMaxBatch;
+  const bool exact = p->batch <= kExactMaxBatch && (tokens >= 0 || p->batch >= kLptMinBatch);
   pl.units = grid_units(p, pl.hpb, tokens);
 
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = G * p->q_len;
-  const int rp = rows_per_block_of(p);
+  const int rp = rows_per_block_of(p, pl.hpb);
   const int T = pkv::tile_keys(p->head_dim);
   const int64_t L = max_len_of(p);
   int64_t chunk = ceil_div(ceil_div(L, S), T) * T;
@@ -508,7 +528,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->scale_log2 = p->scale * 1.4426950408889634f;
   a->exact = exact ? 1 : 0;
   a->rp = rp;
-  const int64_t outer = (exact ? row_block_slots(p, tokens) : (int64_t)p->batch) * S;
+  const int64_t outer = (exact ? row_block_slots(p, tokens, pl.hpb) : (int64_t)p->batch) * S;
   const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * (exact ? 1 : a->nrb);
   if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
   // the combine kernel's grid (several splits without the in-kernel merge)
@@ -519,6 +539,8 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->partials = (S > 1 || partials_only) ? 1 : 0;
   a->fused = split_ws && pl.fused ? 1 : 0;
   a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
+  // longest first where every split past a sequence's keys is trimmed
+  a->lpt = exact && (a->fused || S == 1) ? 1 : 0;
   return PKV_OK;
 }
 
@@ -526,11 +548,14 @@ int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stre
   const bool causal = a.causal_offsets != nullptr || p->causal_offset >= 0 || p->causal_offset == PKV_CAUSAL_LAST;
   (void)hipGetLastError();
   const int rows = a.rp;
-  int err = rows == pkv::kPrefillRows
-                ? pkv::launch_split_prefill(a, p->head_dim, causal, a.mask != nullptr, stream)
-            : pkv::use_mfma(a.R)
-                ? pkv::launch_split_mfma(a, p->head_dim, rows / 16, causal, a.mask != nullptr, stream)
-                : pkv::launch_split(a, p->head_dim, rows, causal, a.mask != nullptr, stream);
+  const bool mask = a.mask != nullptr;
+  int err;
+  switch (pkv::kernel_kind(a.R, p->head_dim, a.hpb)) {
+    case pkv::kKernelPrefill: err = pkv::launch_split_prefill(a, p->head_dim, causal, mask, stream); break;
+    case pkv::kKernelGroup: err = pkv::launch_split_group(a, p->head_dim, rows / 16, causal, mask, stream); break;
+    case pkv::kKernelMfma: err = pkv::launch_split_mfma(a, p->head_dim, rows / 16, causal, mask, stream); break;
+    default: err = pkv::launch_split(a, p->head_dim, rows, causal, mask, stream); break;
+  }
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

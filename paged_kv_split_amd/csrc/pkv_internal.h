@@ -40,6 +40,7 @@ struct DecodeArgs {
   int32_t inner;                  // (Hkv / hpb) * nrb unit slots (kv-head group, row block) per pair;
                                   // exact schedule: Hkv / hpb kv-head groups per item
   int32_t exact;                  // 1: exact schedule (B <= 64 * kExactPerLane)
+  int32_t lpt;                    // 1: the exact schedule deals its items longest first
   int32_t rp;                     // packed rows per row block
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
@@ -75,15 +76,30 @@ inline bool use_mfma(int R) { return R > 2; }
 // rows) 115 us either way.
 constexpr int kPrefillRows = 128;      // rows per prefill-shaped workgroup
 constexpr int kPrefillMinRows = 128;   // packed rows per kv head from which it is taken
-inline bool use_prefill(int R, int head_dim, int forced_hpb) {
-  return R >= kPrefillMinRows && head_dim <= 128 && forced_hpb <= 1;
+inline bool use_prefill(int R, int head_dim, int hpb) {
+  return R >= kPrefillMinRows && head_dim <= 128 && hpb <= 1;
 }
-// rows per workgroup: RP (VALU, 1 or 2), 16/32 (MFMA) or 128 (prefill-shaped)
-int rows_per_block(int R, int head_dim, int forced_hpb);
+// The split kernels (pkv_plan_info.kernel): the vector kernel (one or two
+// rows per kv head), the one-head matrix-core kernel (each wave its own
+// 16-key tiles of one kv head), the shared-tile matrix-core kernel (a
+// workgroup of 4 or 8 kv heads whose waves share whole head-group K/V tiles
+// in LDS: with 8 heads always, with 4 heads from 3 rows on at D <= 128) and
+// the prefill-shaped kernel.  hpb: the kv heads per workgroup of the plan (0
+// or 1 for one).
+enum { kKernelValu = 0, kKernelMfma = 1, kKernelGroup = 2, kKernelPrefill = 3 };
+inline int kernel_kind(int R, int head_dim, int hpb) {
+  if (use_prefill(R, head_dim, hpb)) return kKernelPrefill;
+  if (hpb == 8 || (hpb == 4 && R > 2 && head_dim <= 128)) return kKernelGroup;
+  return R > 2 ? kKernelMfma : kKernelValu;
+}
+// rows per workgroup and kv head: RP (vector kernel, 1 or 2), 16/32
+// (matrix-core kernels) or 128 (prefill-shaped)
+int rows_per_block(int R, int head_dim, int hpb);
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)
 constexpr int kWavesPerBlock = 4;  // waves per split workgroup
 constexpr int kCausalLast = -2;    // causal_offset: the query tokens are the sequence's last keys
-constexpr int kMaxHeadsPerBlock = 4;  // kv heads one split workgroup may cover (one wave or more each)
+constexpr int kMaxHeadsPerBlock = 4;  // kv heads a one-head-per-wave workgroup may cover (one wave or more each)
+constexpr int kMaxGroupHeads = 8;     // kv heads a shared-tile workgroup may cover (HW = hpb / 4 per wave)
 
 // Blocks of a split-kernel grid: 8 XCD queues of equal length holding every
 // (pair, unit slot), or (exact schedule) the item bound times the groups.
@@ -98,6 +114,8 @@ int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal,
 int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
                       hipStream_t stream);
 int launch_split_prefill(const DecodeArgs &a, int head_dim, bool causal, bool has_mask, hipStream_t stream);
+int launch_split_group(const DecodeArgs &a, int head_dim, int nrb16, bool causal, bool has_mask,
+                       hipStream_t stream);
 int launch_combine(const CombineArgs &a, int head_dim, hipStream_t stream);
 int launch_zero(void *p, int64_t words, hipStream_t stream);
 

@@ -239,7 +239,12 @@ def test_plan_report():
 def test_heads_per_block_checks():
     assert call(base_problem(num_splits=1, heads_per_block=-1)) == pkv.PKV_ERR_SHAPE
     assert call(base_problem(num_splits=1, heads_per_block=3)) == pkv.PKV_ERR_UNSUPPORTED
-    assert call(base_problem(num_splits=1, heads_per_block=8, num_kv_heads=8)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(base_problem(num_splits=1, heads_per_block=16, num_kv_heads=8, num_q_heads=16)) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    # eight kv heads per workgroup: the shared-tile kernel, head_dim <= 64 only
+    assert call(base_problem(num_splits=1, heads_per_block=8, num_kv_heads=8, head_dim=128)) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert call(base_problem(num_splits=1, heads_per_block=8, num_kv_heads=8)) == pkv.PKV_ERR_LAUNCH
     assert call(base_problem(num_splits=1, heads_per_block=4)) == pkv.PKV_ERR_SHAPE   # Hkv = 2
     # a valid forced grouping passes every host check (the launch then fails without a GPU)
     assert call(base_problem(num_splits=1, heads_per_block=2)) == pkv.PKV_ERR_LAUNCH
@@ -267,8 +272,9 @@ def test_problem_struct_layout():
     assert ctypes.sizeof(pkv.Problem) == 72
     assert pkv.Problem.mask_stride_b.offset == 48
     assert pkv.Problem.heads_per_block.offset == 64
-    assert ctypes.sizeof(pkv.PlanInfo) == 40
+    assert ctypes.sizeof(pkv.PlanInfo) == 48      # ... kernels, kernel, tail padding to 8 bytes
     assert pkv.PlanInfo.units.offset == 16 and pkv.PlanInfo.merge_in_kernel.offset == 32
+    assert pkv.PlanInfo.kernel.offset == 40
 
 
 def test_workspace_clear_checks():

@@ -58,6 +58,8 @@ def test_constants_match_the_binding(probe):
                  pkv.PKV_KV_BLHD, pkv.PKV_KV_BHLD, 1 << 30]
     assert list(map(int, probe["status"])) == list(range(9))
     assert int(probe["scratch"][0]) == pkv.PKV_NOALLOC_SCRATCH_BYTES
+    assert list(map(int, probe["kernels"])) == [pkv.PKV_KERNEL_VECTOR, pkv.PKV_KERNEL_MATRIX,
+                                                pkv.PKV_KERNEL_SHARED_TILE, pkv.PKV_KERNEL_PREFILL]
 
 
 def _decode_problem(**kw):
@@ -69,7 +71,7 @@ def _decode_problem(**kw):
 
 def _plan_tuple(pl):
     return [pl.splits, pl.heads_per_block, pl.rows_per_block, pl.matrix_core, pl.units, pl.workgroups,
-            pl.merge_in_kernel, pl.kernels]
+            pl.merge_in_kernel, pl.kernels, pl.kernel]
 
 
 def test_host_entry_points_answer_c_as_they_answer_python(probe):

@@ -99,12 +99,14 @@ def test_small_cases(i, splits):
     compare(w, num_splits=splits)
 
 
-@pytest.mark.parametrize("i,hpb", [(i, h) for i in range(len(SMALL)) for h in (1, 2, 4)
-                                   if SMALL[i]["Hkv"] % h == 0])
+@pytest.mark.parametrize("i,hpb", [(i, h) for i in range(len(SMALL)) for h in (1, 2, 4, 8)
+                                   if SMALL[i]["Hkv"] % h == 0 and (h < 8 or SMALL[i]["D"] <= 64)])
 @pytest.mark.parametrize("splits", [1, 5])
 def test_small_cases_heads_per_block(i, hpb, splits):
-    """Every kv-head grouping of a workgroup (one to four heads, one or more
-    waves per head, each dividing the case's kv heads) on the same cases."""
+    """Every kv-head grouping of a workgroup (one to four heads with one or
+    more waves per head; four heads from three rows on, and eight heads, in
+    the shared-tile kernel), each dividing the case's kv heads, on the same
+    cases."""
     kw = dict(SMALL[i])
     w = workloads.build(f"small{i}", seed=2000 + i, spare_pages=3, **kw)
     compare(w, num_splits=splits, heads_per_block=hpb)
@@ -116,6 +118,55 @@ def test_sweep_heads_per_block_sampled(hpb):
     for D, Hq in ((64, 8), (32, 16), (128, 64), (256, 32)):
         w = workloads.sweep(D, Hq)
         compare(w, seqs=[0, 15], heads_per_block=hpb)
+
+
+# ---- the shared-tile kernel (4 or 8 kv heads per workgroup) ----------------
+# Whole head-group rows of each key loaded by the workgroup into shared
+# tiles of 16 to 64 keys: pages smaller than a tile (per-key page lookups),
+# page size 1, 2D and 3D masks, causal limits, 16- and 32-row blocks, empty
+# and one-key sequences, one row per kv head.
+GROUP_CASES = [
+    dict(B=3, q_len=1, Hq=64, Hkv=8, D=32, page_size=32, kv_lens=[4096, 77, 1000], mask="2d"),      # R=8
+    dict(B=2, q_len=4, Hq=32, Hkv=8, D=64, page_size=8, kv_lens=[700, 33], causal="last", mask="3d",
+         mask_p=0.2),                                                                                 # R=16
+    dict(B=2, q_len=4, Hq=64, Hkv=8, D=128, page_size=16, kv_lens=[3000, 5], causal="last"),         # R=32
+    dict(B=3, q_len=2, Hq=24, Hkv=8, D=64, page_size=64, kv_lens=[1500, 64, 0]),                    # R=6
+    dict(B=2, q_len=1, Hq=8, Hkv=8, D=32, page_size=1, kv_lens=[300, 2]),                           # R=1
+    dict(B=2, q_len=3, Hq=16, Hkv=4, D=128, page_size=32, kv_lens=[1000, 129], causal="last",
+         mask="2d", mask_p=0.3),                                                                      # R=12
+    dict(B=2, q_len=1, Hq=16, Hkv=8, D=64, page_size=16, kv_lens=[2049, 1], outlier_p=0.05),        # R=2
+    dict(B=2, q_len=8, Hq=32, Hkv=8, D=32, page_size=32, kv_lens=[900, 60], causal="last",
+         mask="2d", mask_p=0.1),                                                                      # R=32
+]
+
+
+@pytest.mark.parametrize("i,hpb", [(i, h) for i in range(len(GROUP_CASES)) for h in (4, 8)
+                                   if GROUP_CASES[i]["Hkv"] % h == 0 and (h < 8 or GROUP_CASES[i]["D"] <= 64)
+                                   and (h == 8 or GROUP_CASES[i]["Hq"] // GROUP_CASES[i]["Hkv"]
+                                        * GROUP_CASES[i]["q_len"] > 2)])
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_shared_tile_cases(i, hpb, splits):
+    import paged_kv_split_amd as pkv
+    from gpu_util import problem
+    kw = dict(GROUP_CASES[i])
+    w = workloads.build(f"group{i}", seed=2400 + i, spare_pages=3, **kw)
+    assert pkv.plan(problem(w, splits, hpb)).kernel == pkv.PKV_KERNEL_SHARED_TILE
+    compare(w, num_splits=splits, heads_per_block=hpb)
+
+
+@pytest.mark.parametrize("D,Hq,hpb", [(32, 8, 8), (32, 64, 8), (32, 32, 4), (64, 8, 8), (64, 64, 8), (64, 32, 4),
+                                      (128, 64, 4), (128, 32, 4)])
+def test_sweep_shared_tile_sampled(D, Hq, hpb):
+    """Full-size sweep shapes in the shared-tile kernel."""
+    compare(workloads.sweep(D, Hq), seqs=[0, 7, 15], heads_per_block=hpb)
+
+
+def test_long_ctx_and_ragged_shared_tile_sampled():
+    compare(workloads.long_ctx(), seqs=[0, 3], heads_per_block=4)
+    compare(workloads.long_ctx(), num_splits=64, seqs=[1], heads_per_block=4)
+    w = workloads.ragged()
+    L = w.kv_lens
+    compare(w, seqs=sorted({int(L.argmax()), int(L.argmin()), 0, 100, 255}), heads_per_block=4)
 
 
 def test_all_masked_and_empty_rows_are_zero():

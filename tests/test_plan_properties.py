@@ -25,8 +25,8 @@ def problems(draw):
     pages_per_seq = max(1, math.ceil(max_len / page))
     causal = draw(st.sampled_from([-1, -1, 0, 17, pkv.PKV_CAUSAL_LAST]))
     splits = draw(st.sampled_from([0, 0, 0, 1, 2, 7, 64, 256]))
-    hpb = draw(st.sampled_from([0, 0, 0, 1, 2, 4]))
-    if hpb and hkv % hpb:
+    hpb = draw(st.sampled_from([0, 0, 0, 1, 2, 4, 8]))
+    if hpb and hkv % hpb or (hpb == 8 and d > 64):
         hpb = 0
     return pkv.make_problem(batch=batch, q_len=q_len, num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d,
                             page_size=page, num_pages=batch * pages_per_seq, max_pages_per_seq=pages_per_seq,
@@ -38,7 +38,7 @@ def _check_plan(p, pl):
     assert 1 <= pl.splits <= pkv.PKV_MAX_SPLITS
     if p.num_splits:
         assert pl.splits == p.num_splits
-    assert pl.heads_per_block in (1, 2, 4) and p.num_kv_heads % pl.heads_per_block == 0
+    assert pl.heads_per_block in (1, 2, 4, 8) and p.num_kv_heads % pl.heads_per_block == 0
     if p.heads_per_block:
         assert pl.heads_per_block == p.heads_per_block
     assert pl.rows_per_block in (1, 2, 16, 32, 128)
@@ -46,6 +46,14 @@ def _check_plan(p, pl):
     assert pl.matrix_core == (1 if pl.rows_per_block >= 16 else 0)
     if pl.rows_per_block == 128:
         assert rows >= 128 and p.head_dim <= 128 and pl.heads_per_block == 1
+    # the kernel follows from the rows, head dim and grouping
+    if pl.rows_per_block == 128:
+        assert pl.kernel == pkv.PKV_KERNEL_PREFILL
+    elif pl.heads_per_block == 8 or (pl.heads_per_block == 4 and rows > 2 and p.head_dim <= 128):
+        assert pl.kernel == pkv.PKV_KERNEL_SHARED_TILE and pl.rows_per_block in (16, 32)
+        assert pl.heads_per_block < 8 or p.head_dim <= 64
+    else:
+        assert pl.kernel == (pkv.PKV_KERNEL_MATRIX if rows > 2 else pkv.PKV_KERNEL_VECTOR)
     assert pl.workgroups == pl.units * pl.splits
     assert pl.merge_in_kernel in (0, 1) and pl.kernels in (1, 2)
     if pl.merge_in_kernel:
