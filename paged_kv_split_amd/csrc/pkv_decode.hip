@@ -588,8 +588,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     }
   }
   __syncthreads();
-  auto item = [&](int ri, int d, float &M, float &W, float &vx, float &vy) {
-    merge_waves<NW, D>(mlb, ob, HR, wph, ri, d, M, W, vx, vy);
+  auto item = [&](int ri, int d, float &M, float &W, float (&v)[8]) {
+    merge_waves<NW, D>(mlb, ob, HR, wph, ri, d, M, W, v);
   };
   write_rows<D>(a, s, direct, rowtab, nrows, item, NW * 64);
   if (a.fused && !direct) fused_tail<D>(a, wk0.unit, nact, rowtab, nrows, smem, NW * 64);

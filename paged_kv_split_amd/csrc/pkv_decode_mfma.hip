@@ -275,9 +275,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     if (q == 0) *reinterpret_cast<float2 *>(mlb + (rb * NW * 16 + u) * 2) = make_float2(st.m[rb], ltot[rb]);
   }
   __syncthreads();
-  auto item = [&](int ri, int d, float &M, float &W, float &vx, float &vy) {
+  auto item = [&](int ri, int d, float &M, float &W, float (&v)[8]) {
     const int rb = NRB == 1 ? 0 : ri / HR;
-    merge_waves<NW, L::OB_STRIDE>(mlb + rb * NW * 16 * 2, ob + rb * OBN, HR, wph, ri - rb * HR, d, M, W, vx, vy);
+    merge_waves<NW, L::OB_STRIDE>(mlb + rb * NW * 16 * 2, ob + rb * OBN, HR, wph, ri - rb * HR, d, M, W, v);
   };
   write_rows<D>(a, s, direct, rowtab, nrt, item, NW * 64);
   if (a.fused && !direct)

@@ -639,35 +639,50 @@ __device__ __forceinline__ void empty_partials(const DecodeArgs &a, int64_t tok0
 
 // Epilogue shared by the split kernels once a block's waves have left their
 // results in LDS, for its nrows output rows: `rowtab[r]` is the output row of
-// block row r; `item(r, d, M, W, vx, vy)` gives the row's base-2 reference
-// max M, its total weight W and the normalised results at columns d, d + 1
-// (0 when the row saw no key).  `direct`: write the output (the unit's only
-// split with keys).  Otherwise write this split's partial (o, m in
-// natural-log units, l = W); an empty split (W = 0) writes only
-// (m, l) = (-inf, 0).
+// block row r; `item(r, d, M, W, v)` gives the row's base-2 reference max M,
+// its total weight W and the normalised results at columns d .. d + 7 (0 when
+// the row saw no key).  `direct`: write the output (the unit's only split
+// with keys).  Otherwise write this split's partial (o, m in natural-log
+// units, l = W); an empty split (W = 0) writes only (m, l) = (-inf, 0).
+// Eight columns per item: the output goes out in 16-byte stores, which keeps
+// the store count low while other workgroups of the CU stream K/V.
 template <int D, class ItemF>
 __device__ void write_rows(const DecodeArgs &a, int s, bool direct, const int64_t *rowtab, int nrows, ItemF item,
                            int nthreads) {
-  constexpr int DP = D / 2;
-  for (int idx = threadIdx.x; idx < nrows * DP; idx += nthreads) {
-    const int r = idx / DP;
-    const int d = 2 * (idx - r * DP);
+  constexpr int DG = D / 8;
+  for (int idx = threadIdx.x; idx < nrows * DG; idx += nthreads) {
+    const int r = idx / DG;
+    const int d = 8 * (idx - r * DG);
     const int64_t row = rowtab[r];
-    float M, W, vx, vy;
-    item(r, d, M, W, vx, vy);
+    float M, W, v[8];
+    item(r, d, M, W, v);
     if (direct) {
-      *reinterpret_cast<uint32_t *>(a.out + row * D + d) =
-          (uint32_t)f32_to_bf16_rne(vx) | ((uint32_t)f32_to_bf16_rne(vy) << 16);
-      if (a.out_f32) *reinterpret_cast<float2 *>(a.out_f32 + row * D + d) = make_float2(vx, vy);
+      uint4 pk;
+      pk.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      pk.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+      pk.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+      *reinterpret_cast<uint4 *>(a.out + row * D + d) = pk;
+      if (a.out_f32) {
+        float4 *o32 = reinterpret_cast<float4 *>(a.out_f32 + row * D + d);
+        o32[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o32[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
     } else {
       float *po = a.o_part + (row * a.S + s) * D + d;
       float *pm = a.ml_part + (row * a.S + s) * 2;
       const float mx = W > 0.f ? M * kLn2 : -INFINITY;
       if (a.fused) {  // merged by another workgroup of this launch
-        if (W > 0.f) store_dev2(po, vx, vy);
+        if (W > 0.f) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) store_dev2(po + e, v[e], v[e + 1]);
+        }
         if (d == 0) store_dev2(pm, mx, W);
       } else {        // read after this kernel has ended
-        if (W > 0.f) *reinterpret_cast<float2 *>(po) = make_float2(vx, vy);
+        if (W > 0.f) {
+          reinterpret_cast<float4 *>(po)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4 *>(po)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
         if (d == 0) *reinterpret_cast<float2 *>(pm) = make_float2(mx, W);
       }
     }
@@ -695,31 +710,40 @@ __device__ __forceinline__ void wave_factors(const float (&m)[NW], const float (
   for (int ww = 0; ww < NW; ++ww) f[ww] *= inv;
 }
 
-// The merged result of block row ri at columns d, d + 1 from the per-wave
+// The merged result of block row ri at columns d .. d + 7 from the per-wave
 // results in LDS: wave slot kk*HR + ri holds wave kk's (m, l) in mlb and its
-// unnormalised O row in ob (row stride OBS floats); waves kk >= wph hold no
-// row of this head.  All loads are issued together, from clamped slots, and
-// unused waves are masked after loading, so no branch separates them.
+// unnormalised O row in ob (row stride OBS floats, d a multiple of 8 and rows
+// 16-byte aligned); waves kk >= wph hold no row of this head.  All loads are
+// issued together, from clamped slots, and unused waves are masked after
+// loading, so no branch separates them.
 template <int NW, int OBS>
 __device__ __forceinline__ void merge_waves(const float *mlb, const float *ob, int HR, int wph, int ri, int d,
-                                            float &M, float &W, float &vx, float &vy) {
+                                            float &M, float &W, float (&v)[8]) {
   float mw[NW], lw[NW], f[NW];
-  float2 o[NW];
+  float4 o0[NW], o1[NW];
 #pragma unroll
   for (int kk = 0; kk < NW; ++kk) {
     const int slot = (kk < wph ? kk : wph - 1) * HR + ri;
     const float2 ml = *reinterpret_cast<const float2 *>(mlb + 2 * slot);
-    o[kk] = *reinterpret_cast<const float2 *>(ob + slot * OBS + d);
+    const float4 *orow = reinterpret_cast<const float4 *>(ob + slot * OBS + d);
+    o0[kk] = orow[0];
+    o1[kk] = orow[1];
     mw[kk] = kk < wph ? ml.x : -INFINITY;
     lw[kk] = kk < wph ? ml.y : 0.f;
   }
   wave_factors<NW>(mw, lw, M, W, f);
-  vx = 0.f;
-  vy = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < NW; ++kk) {
-    vx = fmaf(f[kk], o[kk].x, vx);   // f = 0 for unused waves (their loads are finite rows of wave wph - 1)
-    vy = fmaf(f[kk], o[kk].y, vy);
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NW; ++kk) {   // f = 0 for unused waves (their loads are finite rows of wave wph - 1)
+    v[0] = fmaf(f[kk], o0[kk].x, v[0]);
+    v[1] = fmaf(f[kk], o0[kk].y, v[1]);
+    v[2] = fmaf(f[kk], o0[kk].z, v[2]);
+    v[3] = fmaf(f[kk], o0[kk].w, v[3]);
+    v[4] = fmaf(f[kk], o1[kk].x, v[4]);
+    v[5] = fmaf(f[kk], o1[kk].y, v[5]);
+    v[6] = fmaf(f[kk], o1[kk].z, v[6]);
+    v[7] = fmaf(f[kk], o1[kk].w, v[7]);
   }
 }
 
