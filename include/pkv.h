@@ -115,7 +115,8 @@ typedef struct pkv_problem {
 /* Number of splits pkv_paged_decode uses for this problem on a device with
  * `num_cus` compute units (num_cus <= 0: the current device's count).  A
  * forced p->num_splits is returned unchanged.  Pure host arithmetic once the
- * CU count is known. */
+ * CU count is known.  (The split-count heuristic of the AstrAI commit notes,
+ * "compute_num_splits"; 0 = automatic as in ejkernel's PageAttentionConfig.) */
 int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out);
 
 /* The launch plan pkv_paged_decode follows for this problem on a device with
@@ -152,27 +153,41 @@ typedef struct pkv_plan_info {
 
 int pkv_plan(const pkv_problem *p, int num_cus, pkv_plan_info *info);
 
-/* Workspace pkv_paged_decode needs with `splits` splits:
+/* Workspace pkv_paged_decode needs with `splits` splits (the caller-owned,
+ * pre-allocated split partials of the AstrAI commit notes, which replace
+ * cached static buffers so a decode step allocates nothing and can be
+ * captured into a graph):
  *   o_part : fp32 [B, q_len, Hq, splits, D]      (normalised partial outputs)
  *   ml_part: PKV_COUNTER_BYTES of int32 arrival counters, then
  *            fp32 [B, q_len, Hq, splits, 2]      (m, l) per partial,
  * m = max scaled+masked score in natural-log units, l = sum exp(s - m).
  * Both are 0 when splits == 1 (the split kernel then writes `out` itself).
  * The counter head must read zero when a call starts: clear a new workspace
- * once (pkv_workspace_clear, or any zero fill); every call returns the
- * counters it used to zero before its kernel ends, so a workspace stays
- * ready across calls of any shape.  Calls sharing one workspace must be
- * ordered (one stream, or synchronised streams). */
+ * once (pkv_workspace_clear, or any zero fill, ordered before the first call
+ * on the call's stream); every call returns the counters it used to zero
+ * before its kernel ends, so a workspace stays ready across calls of any
+ * shape.  Calls sharing one workspace must be ordered (one stream, or
+ * synchronised streams).  A head that does not read zero is not detected: a
+ * unit whose counter starts at k < n (n its splits with keys) merges before
+ * its last k partials land and leaves k behind; a counter at n or more never
+ * merges, leaving that unit's output unwritten.  For hipGraph capture, clear
+ * the head before capturing, or capture pkv_workspace_clear ahead of the
+ * call (a fill kernel, safe to replay). */
 int pkv_workspace_bytes(const pkv_problem *p, int splits, size_t *o_part_bytes,
                         size_t *ml_part_bytes);
 
 /* Zero `bytes` (a multiple of 4) of device memory at `ptr` (4-byte aligned)
+ * -- the workspace preparation that the AstrAI commit notes' graph-capture
+ * work does outside the captured step --
  * with a fill kernel on `stream` (not a runtime memset, so it may be
  * captured into a hipGraph).  Meant for a newly allocated ml_part workspace.
  * bytes == 0 is a no-op. */
 int pkv_workspace_clear(void *ptr, size_t bytes, hipStream_t stream);
 
-/* Paged decode attention.
+/* Paged decode attention: the whole split-KV path of the AstrAI commit notes
+ * (the scalar and MMA split-KV paged decode kernels with GQA head packing,
+ * the page table resolved per tile, the unified causal offset, 2D/3D
+ * additive masks and the LSE combine of the split partials) in one call.
  *   q            bf16 [B, q_len, Hq, D], contiguous, 16-byte aligned
  *   k_cache      bf16 [num_pages, page_size, Hkv, D], contiguous, 16-byte aligned
  *   v_cache      bf16 [num_pages, page_size, Hkv, D], contiguous, 16-byte aligned
@@ -292,7 +307,8 @@ int pkv_contiguous_decode(const pkv_problem *p, int kv_layout, int64_t kv_capaci
                           float *ml_part, size_t ml_part_bytes, void *out_bf16,
                           float *out_f32, hipStream_t stream);
 
-/* The split step alone: the same split kernel as pkv_paged_decode, always
+/* The split step alone (the split-KV kernels of the AstrAI commit notes,
+ * without their combine): the same split kernel as pkv_paged_decode, always
  * writing the split partials and never launching the combine.  For callers
  * that merge partials themselves, e.g. after gathering the partials of key
  * shards held by several devices, with pkv_combine.  o_part (fp32 [B, q_len,
@@ -310,7 +326,9 @@ int pkv_paged_decode_partials(const pkv_problem *p, const void *q,
                               float *ml_part, size_t ml_part_bytes,
                               hipStream_t stream);
 
-/* The combine step alone: merges `splits` partials per row with the
+/* The combine step alone (the single combine kernel of the AstrAI commit
+ * notes, merging split partials by their log-sum-exp): merges `splits`
+ * partials per row with the
  * log-sum-exp rule  M = max_{l_s>0} m_s,  w_s = l_s exp(m_s - M),
  * out = sum_s w_s o_s / sum_s w_s  (0 when no partial has l_s > 0); the
  * o_part rows of partials with l_s = 0 are never read; a row with exactly one

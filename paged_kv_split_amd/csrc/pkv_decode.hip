@@ -445,8 +445,55 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   const int wk = w >> a.lhpb;       // its index among the waves of that head
   const int wph = NW >> a.lhpb;     // waves per head
   const int g = hg * a.hpb + hw;
-
   const int r0 = rb * RP;
+
+  Ctx<D, RP> c;
+  c.kb = s * a.chunk;
+  c.jq = lane / LPK;
+  c.qq = lane % LPK;
+  c.kg = lane / LPV;
+  c.ds = lane % LPV;
+
+  // ---- q rows of this wave's head, in registers (QK layout: chunks qq +
+  // LPK*c4), and the split's first page-table window (key windows whose pages
+  // fit the LDS page-table slice: one unless the split spans more than kBtCap
+  // pages): issued before the sequence's length is used (see work_of)
+  QRows<D, RP> qrows;
+  {
+    const SeqRows &sr0 = wk0.sr;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const int rr = r0 + r;
+      if (rr < sr0.R) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * D);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
+      } else {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  float *pbuf = smem + kBtCap + 4 + w * (T * RP);
+  float *kbuf = smem + kBtCap + 4 + Lay::PBUF + w * (T * D / 2);
+  int *bt_lds = reinterpret_cast<int *>(smem);
+  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
+  const int win_keys = window_keys(kBtCap, a.page_shift, NW * T);
+  const int cap_keys = a.max_pages << a.page_shift;
+  auto load_bt = [&](int from) {
+    if (a.contig) {  // contiguous K/V: sequence b is page b
+      if (threadIdx.x == 0) bt_lds[0] = b;
+      return;
+    }
+    int to = from + win_keys;
+    if (to > c.kb + a.chunk) to = c.kb + a.chunk;
+    if (to > cap_keys) to = cap_keys;
+    const int p0 = from >> a.page_shift;
+    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
+  };
+  load_bt(c.kb);
+
   const int L = wk0.L;
   const SeqRows sr = wk0.sr;
   if (r0 >= sr.R) return;  // a row block past the sequence's tokens (varlen batches)
@@ -471,7 +518,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   // the unit's only split with keys writes the output itself
   const bool direct = !a.partials || (a.fused && nact == 1);
 
-  Ctx<D, RP> c;
   c.kbase = a.k + g * a.head_stride;
   c.vbase = a.v + g * a.head_stride;
   c.bt = reinterpret_cast<const int *>(smem);
@@ -480,33 +526,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   c.page_stride = a.page_stride;
   c.row_stride = a.row_stride;
   c.R = sr.R;
-  c.kb = s * a.chunk;
   int kend = c.kb + a.chunk;
   if (kend > kmax) kend = kmax;
-  c.jq = lane / LPK;
-  c.qq = lane % LPK;
-  c.kg = lane / LPV;
-  c.ds = lane % LPV;
-
-  // ---- q rows of this wave's head, in registers (QK layout: chunks qq + LPK*c4)
-  QRows<D, RP> qrows;
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const int rr = r0 + r;
-    if (rr < sr.R) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr.tok0, g, rr) * D);
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
-    } else {
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  float *pbuf = smem + kBtCap + 4 + w * (T * RP);
-  float *kbuf = smem + kBtCap + 4 + Lay::PBUF + w * (T * D / 2);
-  int *bt_lds = reinterpret_cast<int *>(smem);
-  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
 
   State<RP> st;
 #pragma unroll
@@ -517,29 +538,11 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     for (int e = 0; e < 8; ++e) st.acc[r][e] = 0.f;
   }
 
-  // ---- key windows whose pages fit the LDS page-table slice (one window
-  // unless the split spans more than kBtCap pages).  The first window's slice
-  // does not depend on kv_lens, so its load is issued with the q load.
-  const int win_keys = window_keys(kBtCap, a.page_shift, NW * T);
-  const int cap_keys = a.max_pages << a.page_shift;
-  auto load_bt = [&](int from) {
-    if (a.contig) {  // contiguous K/V: sequence b is page b
-      if (threadIdx.x == 0) bt_lds[0] = b;
-      return;
-    }
-    int to = from + win_keys;
-    if (to > c.kb + a.chunk) to = c.kb + a.chunk;
-    if (to > cap_keys) to = cap_keys;
-    const int p0 = from >> a.page_shift;
-    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
-    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
-  };
   if ((int)threadIdx.x < RP * a.hpb) {
     const int rr = r0 + (threadIdx.x >> a.lhpb);
     rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
-  load_bt(c.kb);
-  __syncthreads();
+  __syncthreads();   // the first page-table window (loaded above) is in LDS
   for (int wb = c.kb; wb < kend; wb += win_keys) {
     const int we = wb + win_keys < kend ? wb + win_keys : kend;
     if (wb != c.kb) {

@@ -150,6 +150,47 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   const int cc = lane & 15;
   const int q = lane >> 4;
   const int r0 = rg * RW;
+  const int kb = s * a.chunk;
+
+  int *bt_lds = reinterpret_cast<int *>(smem_raw);
+  uint16_t *kt = reinterpret_cast<uint16_t *>(smem_raw + L::BT_BYTES + w * L::WAVE_LDS);
+  uint16_t *vt = kt + L::TILE_ELEMS;
+
+  // q operand (lane supplies Q[row cc+16rb][d 32*stp + 8q .. +8]) and the
+  // split's first page-table window, issued before the sequence's length is
+  // used (see work_of)
+  uint4 qb[NRB][D / 32];
+  {
+    const SeqRows &sr0 = wk0.sr;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rr = r0 + cc + 16 * rb;
+      if (rr < sr0.R) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * D);
+#pragma unroll
+        for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
+      } else {
+#pragma unroll
+        for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
+  const int win_keys = window_keys(kBtCap, a.page_shift, NW * KT);
+  const int cap_keys = a.max_pages << a.page_shift;
+  auto load_bt = [&](int from) {
+    if (a.contig) {  // contiguous K/V: sequence b is page b
+      if (threadIdx.x == 0) bt_lds[0] = b;
+      return;
+    }
+    int to = from + win_keys;
+    if (to > kb + a.chunk) to = kb + a.chunk;
+    if (to > cap_keys) to = cap_keys;
+    const int p0 = from >> a.page_shift;
+    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
+  };
+  load_bt(kb);
 
   const int kvlen = wk0.L;
   const SeqRows sr = wk0.sr;
@@ -171,10 +212,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   // the unit's only split with keys writes the output itself
   const bool direct = !a.partials || (a.fused && nact == 1);
 
-  int *bt_lds = reinterpret_cast<int *>(smem_raw);
-  uint16_t *kt = reinterpret_cast<uint16_t *>(smem_raw + L::BT_BYTES + w * L::WAVE_LDS);
-  uint16_t *vt = kt + L::TILE_ELEMS;
-
   MCtx c;
   c.kbase = a.k + g * a.head_stride;
   c.vbase = a.v + g * a.head_stride;
@@ -185,40 +222,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   c.row_stride = a.row_stride;
   c.R = sr.R;
   c.kvis = wave_min_limit<NRB>(lim, r0, sr.R, lane);
-  const int kb = s * a.chunk;
   int kend = kb + a.chunk;
   if (kend > kmax) kend = kmax;
-
-  // q operand: lane supplies Q[row cc+16rb][d 32*stp + 8q .. +8]
-  uint4 qb[NRB][D / 32];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int rr = r0 + cc + 16 * rb;
-    if (rr < sr.R) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr.tok0, g, rr) * D);
-#pragma unroll
-      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
-    } else {
-#pragma unroll
-      for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  const int *bt_row = a.block_table + (int64_t)b * a.max_pages;
-  const int win_keys = window_keys(kBtCap, a.page_shift, NW * KT);
-  const int cap_keys = a.max_pages << a.page_shift;
-  auto load_bt = [&](int from) {
-    if (a.contig) {  // contiguous K/V: sequence b is page b
-      if (threadIdx.x == 0) bt_lds[0] = b;
-      return;
-    }
-    int to = from + win_keys;
-    if (to > kb + a.chunk) to = kb + a.chunk;
-    if (to > cap_keys) to = cap_keys;
-    const int p0 = from >> a.page_shift;
-    const int np = to > from ? ((to - 1) >> a.page_shift) - p0 + 1 : 0;
-    for (int i = threadIdx.x; i < np; i += NW * 64) bt_lds[i] = bt_row[p0 + i];
-  };
 
   MState<D, NRB> st;
 #pragma unroll
@@ -233,8 +238,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     const int rr = r0 + (threadIdx.x >> a.lhpb);
     rowtab[threadIdx.x] = rr < sr.R ? out_row(a, sr.tok0, hg * a.hpb + (threadIdx.x & (a.hpb - 1)), rr) : 0;
   }
-  load_bt(kb);
-  __syncthreads();
+  __syncthreads();   // the first page-table window (loaded above) is in LDS
   for (int wb = kb; wb < kend; wb += win_keys) {
     const int we = wb + win_keys < kend ? wb + win_keys : kend;
     if (wb != kb) {

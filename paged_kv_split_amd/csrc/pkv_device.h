@@ -466,6 +466,12 @@ __device__ __forceinline__ bool work_lpt(const DecodeArgs &a, int xcd, int slot,
 // fewer (a prefill-shaped call: few sequences, many row blocks) XCD x takes
 // the x-th eighth of the (pair, slot) list, so every XCD has work.  False:
 // no work.
+//
+// On the per-block schedule the sequence's length (and, for a varlen batch,
+// its token offsets) is read here but used by the kernels only after they
+// have issued the loads of their q rows and first page-table window, which do
+// not depend on it for fixed-length batches: the loads then share one memory
+// round trip.
 template <bool CAUSAL>
 __device__ __forceinline__ bool work_of(const DecodeArgs &a, Work &w) {
   const int x = blockIdx.x;
