@@ -215,14 +215,18 @@ struct Work {
   SeqRows sr;
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP moves (no LDS
+// permutes): shifts of 1, 2, 4 and 8 lanes within each row of 16 (lanes
+// shifted in from before the row add 0) give every row's own prefix sums;
+// then the last lane of row 0 (of row 2) is added to row 1 (row 3), and the
+// last lane of row 1, by then the total of rows 0 and 1, to rows 2 and 3.
 __device__ __forceinline__ int wave_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    x += lane >= d ? y : 0;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -262,7 +266,7 @@ __device__ __forceinline__ bool work_exact(const DecodeArgs &a, int xcd, int slo
     rbs[j] = 0;
     if (j < k && b0 + j < a.B) {
       const SeqRows sr = seq_rows_of<CAUSAL>(a, b0 + j, Lq[j], c0q[j], c1q[j], coq[j]);
-      rbs[j] = (sr.R + a.rp - 1) / a.rp;
+      rbs[j] = (sr.R + a.rp - 1) >> __builtin_ctz(a.rp);  // a.rp is a power of two
       const int ns = trimmed ? active_splits(a, row_keys(a, sr, Lq[j], sr.R - 1)) : a.S;
       items[j] = rbs[j] * ns;
     }
@@ -279,6 +283,7 @@ __device__ __forceinline__ bool work_exact(const DecodeArgs &a, int xcd, int slo
   if (v >= n_items) return false;
   // the lane whose run holds item v, then the sequence within the run
   const uint64_t m = __builtin_amdgcn_ballot_w64(iscan > v);
+  if (m == 0) return false;  // not reached: v < n_items
   const int sel = __builtin_ctzll(m);
   int ibase = __builtin_amdgcn_readlane(iscan - isum, sel);
   int ubase = __builtin_amdgcn_readlane(uscan - usum, sel);
@@ -352,45 +357,58 @@ __device__ __forceinline__ bool work_lpt(const DecodeArgs &a, int xcd, int slot,
     c1q[j] = ok && a.cu_q ? a.cu_q[b + 1] : 0;
     coq[j] = ok && CAUSAL && a.causal_offsets ? a.causal_offsets[b] : -1;
   }
-  // per sequence: row blocks, whole-chunk splits, bucket of its partial split
-  // (-1: none); per lane and bucket: items
-  int rbs[kExactPerLane], nfull[kExactPerLane], pbk[kExactPerLane];
-  int cnt[NB];
-#pragma unroll
-  for (int q = 0; q < NB; ++q) cnt[q] = 0;
-  int usum = 0;
+  // per sequence: row blocks, whole-chunk splits and the keys of its partial
+  // split; their items counted first, so that a block past every item (the
+  // grid is sized for a host-side bound) leaves before the buckets are formed
+  const int lrp = __builtin_ctz(a.rp);  // a.rp is a power of two
+  int rbs[kExactPerLane], nfull[kExactPerLane], remq[kExactPerLane];
+  int isum = 0, usum = 0;
 #pragma unroll
   for (int j = 0; j < kExactPerLane; ++j) {
     rbs[j] = 0;
     nfull[j] = 0;
-    pbk[j] = -1;
+    remq[j] = -1;   // -1: no partial split
     if (j < k && b0 + j < a.B) {
       const SeqRows sr = seq_rows_of<CAUSAL>(a, b0 + j, Lq[j], c0q[j], c1q[j], coq[j]);
-      rbs[j] = (sr.R + a.rp - 1) / a.rp;
+      rbs[j] = (sr.R + a.rp - 1) >> lrp;
       const int kmax = sr.R > 0 ? row_keys(a, sr, Lq[j], sr.R - 1) : 0;
-      if (kmax <= 0) {  // no key: one split that writes zero rows
-        pbk[j] = 0;
+      if (kmax <= 0) {  // no key: one split that writes zero rows (bucket 0)
+        remq[j] = 0;
       } else {
         nfull[j] = kmax / a.chunk;
         const int rem = kmax - nfull[j] * a.chunk;
-        if (rem > 0) pbk[j] = (int)(((int64_t)rem * (NB - 1)) / a.chunk);
+        if (rem > 0) remq[j] = rem;
       }
     }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) cnt[q] += (q == NB - 1 ? nfull[j] * rbs[j] : 0) + (q == pbk[j] ? rbs[j] : 0);
+    isum += rbs[j] * (nfull[j] + (remq[j] >= 0 ? 1 : 0));
     usum += rbs[j];
   }
-  const int uscan = wave_scan(usum);
-  int tot[NB];
-  int n_items = 0;
-#pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    tot[q] = (int)reduce_hi<0, OpSum>((float)cnt[q]);
-    n_items += tot[q];
-  }
+  const int n_items = (int)reduce_hi<0, OpSum>((float)isum);  // exact: counts stay below 2^24
   const int kk = slot / a.inner;
   const int v = kk * 8 + xcd;
   if (v >= n_items) return false;
+  // bucket of each partial split: floor(rem * (NB - 1) / chunk) (rem < chunk;
+  // in 32 bits while chunk * (NB - 1) fits, the branch being uniform)
+  int pbk[kExactPerLane];
+  int cnt[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) cnt[q] = 0;
+#pragma unroll
+  for (int j = 0; j < kExactPerLane; ++j) {
+    pbk[j] = -1;
+    if (remq[j] == 0) {
+      pbk[j] = 0;
+    } else if (remq[j] > 0) {
+      pbk[j] = a.chunk < (INT32_MAX / (NB - 1)) ? remq[j] * (NB - 1) / a.chunk
+                                                : (int)(((int64_t)remq[j] * (NB - 1)) / a.chunk);
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) cnt[q] += (q == NB - 1 ? nfull[j] * rbs[j] : 0) + (q == pbk[j] ? rbs[j] : 0);
+  }
+  const int uscan = wave_scan(usum);
+  int tot[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) tot[q] = (int)reduce_hi<0, OpSum>((float)cnt[q]);
   // the bucket of item v (whole chunks first, then the partial buckets from the largest)
   int jv = 0, ov = v;
   bool got = false;
@@ -410,6 +428,7 @@ __device__ __forceinline__ bool work_lpt(const DecodeArgs &a, int xcd, int slot,
   for (int q = 0; q < NB; ++q) cj = q == jv ? cnt[q] : cj;
   const int cscan = wave_scan(cj);
   const uint64_t m = __builtin_amdgcn_ballot_w64(cscan > ov);
+  if (m == 0) return false;  // not reached: ov < tot[jv], the bucket's total
   const int sel = __builtin_ctzll(m);
   int off = ov - __builtin_amdgcn_readlane(cscan - cj, sel);
   int ubase = __builtin_amdgcn_readlane(uscan - usum, sel);

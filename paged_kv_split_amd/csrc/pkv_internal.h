@@ -41,7 +41,7 @@ struct DecodeArgs {
                                   // exact schedule: Hkv / hpb kv-head groups per item
   int32_t exact;                  // 1: exact schedule (B <= 64 * kExactPerLane)
   int32_t lpt;                    // 1: the exact schedule deals its items longest first
-  int32_t rp;                     // packed rows per row block
+  int32_t rp;                     // packed rows per row block (a power of two)
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
   int32_t *counters;              // [units] arrival counters (fused), zero between calls
