@@ -87,6 +87,21 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
   // the loads are unconditional and a round has no exit, so the loads in
   // flight are the same on both paths into the loop header (a conditional
   // load or an exit there makes the compiler wait for all loads)
+  if constexpr (D == 256) {
+    // whole rounds to the end (a step past the last tile computes a tile
+    // whose keys all lie past the window end, at weight 0): the peeled form
+    // below spilled registers at D = 256 (16 x 4096 keys, 32 query heads:
+    // 91.6 -> 98.3 us)
+    for (int t = t0; t < ntiles; t += NBUF * tstep) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        const int tt = t + i * tstep;
+        mstep<D, NRB, CAUSAL, MASK, UPAGE>(a, c, b, r0, wb, tt, tt + NBUF * tstep, tr[i], qb, lim, kt, vt, lane,
+                                           st);
+      }
+    }
+    return;
+  }
   int t = t0;
   for (; t + (2 * NBUF - 1) * tstep < ntiles; t += NBUF * tstep) {
 #pragma unroll
@@ -266,14 +281,19 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   constexpr int OBN = NW * 16 * L::OB_STRIDE;            // floats per row block
   float *ob = reinterpret_cast<float *>(smem_raw);       // [NRB][NW * 16][OB_STRIDE]
   float *mlb = ob + NRB * OBN;                           // [NRB][NW * 16][2]
-  const int u = wk * HR + cc * a.hpb + hw;
+  const int u = wk * HR + 16 * hw + cc;   // a wave's rows consecutive (distinct banks for its lanes)
+  // columns swizzled at D = 128 (at D <= 64 a pass reads 16 groups of two or
+  // more rows already; at D = 256, at the register limit, the swizzled
+  // indices spilled more registers)
+  constexpr bool OBSW = D == 128;
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       // lane holds O^T[d = 16nb + 4q + i][row cc]
-      float4 *dst = reinterpret_cast<float4 *>(ob + rb * OBN + u * L::OB_STRIDE + 16 * nb + 4 * q);
+      float4 *dst = OBSW ? reinterpret_cast<float4 *>(ob + rb * OBN + u * L::OB_STRIDE) + ob_unit<true>(4 * nb + q)
+                         : reinterpret_cast<float4 *>(ob + rb * OBN + u * L::OB_STRIDE + 16 * nb + 4 * q);
       dst[0] = make_float4(st.o[rb][nb][0], st.o[rb][nb][1], st.o[rb][nb][2], st.o[rb][nb][3]);
     }
     if (q == 0) *reinterpret_cast<float2 *>(mlb + (rb * NW * 16 + u) * 2) = make_float2(st.m[rb], ltot[rb]);
@@ -281,7 +301,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   __syncthreads();
   auto item = [&](int ri, int d, float &M, float &W, float (&v)[8]) {
     const int rb = NRB == 1 ? 0 : ri / HR;
-    merge_waves<NW, L::OB_STRIDE>(mlb + rb * NW * 16 * 2, ob + rb * OBN, HR, wph, ri - rb * HR, d, M, W, v);
+    const int rl = ri - rb * HR;   // (16 rb + cc) * hpb + hw - rb * HR = cc * hpb + hw
+    merge_waves<NW, L::OB_STRIDE, OBSW>(mlb + rb * NW * 16 * 2, ob + rb * OBN, HR, wph,
+                                        16 * (rl & (a.hpb - 1)) + (rl >> a.lhpb), d, M, W, v);
   };
   write_rows<D>(a, s, direct, rowtab, nrt, item, NW * 64);
   if (a.fused && !direct)

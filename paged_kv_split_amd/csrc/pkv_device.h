@@ -735,24 +735,39 @@ __device__ __forceinline__ void wave_factors(const float (&m)[NW], const float (
   for (int ww = 0; ww < NW; ++ww) f[ww] *= inv;
 }
 
-// The merged result of block row ri at columns d .. d + 7 from the per-wave
-// results in LDS: wave slot kk*HR + ri holds wave kk's (m, l) in mlb and its
-// unnormalised O row in ob (row stride OBS floats, d a multiple of 8 and rows
-// 16-byte aligned); waves kk >= wph hold no row of this head.  All loads are
-// issued together, from clamped slots, and unused waves are masked after
-// loading, so no branch separates them.
-template <int NW, int OBS>
-__device__ __forceinline__ void merge_waves(const float *mlb, const float *ob, int HR, int wph, int ri, int d,
+// Where column group c (4 floats) of a merge-buffer row is kept, in 16-byte
+// units, when the columns are swizzled: groups 16..31 of each 32 swap
+// neighbours, so that the 16 lanes of one LDS pass that read groups 0, 2,
+// .., 30 (or 1, 3, .., 31) of a 128-column row hit 16 distinct bank groups (a
+// pass covers 256 bytes of banks).
+template <bool SWZ>
+__device__ __forceinline__ int ob_unit(int c) { return SWZ ? c ^ ((c >> 4) & 1) : c; }
+
+// The merged result of a block row at columns d .. d + 7 from the per-wave
+// results in LDS: wave slot kk*HR + rs (rs: the row's slot within a wave's
+// block of HR rows) holds wave kk's (m, l) in mlb and its unnormalised O row
+// in ob (row stride OBS floats, column groups placed by ob_unit<SWZ>, d a
+// multiple of 8 and rows 16-byte aligned); waves kk >= wph hold no row of
+// this head.  All loads are issued together, from clamped slots, and unused
+// waves are masked after loading, so no branch separates them.
+template <int NW, int OBS, bool SWZ = false>
+__device__ __forceinline__ void merge_waves(const float *mlb, const float *ob, int HR, int wph, int rs, int d,
                                             float &M, float &W, float (&v)[8]) {
   float mw[NW], lw[NW], f[NW];
   float4 o0[NW], o1[NW];
 #pragma unroll
   for (int kk = 0; kk < NW; ++kk) {
-    const int slot = (kk < wph ? kk : wph - 1) * HR + ri;
+    const int slot = (kk < wph ? kk : wph - 1) * HR + rs;
     const float2 ml = *reinterpret_cast<const float2 *>(mlb + 2 * slot);
-    const float4 *orow = reinterpret_cast<const float4 *>(ob + slot * OBS + d);
-    o0[kk] = orow[0];
-    o1[kk] = orow[1];
+    if constexpr (SWZ) {
+      const float4 *orow = reinterpret_cast<const float4 *>(ob + slot * OBS);
+      o0[kk] = orow[ob_unit<true>(d / 4)];
+      o1[kk] = orow[ob_unit<true>(d / 4 + 1)];
+    } else {
+      const float4 *orow = reinterpret_cast<const float4 *>(ob + slot * OBS + d);
+      o0[kk] = orow[0];
+      o1[kk] = orow[1];
+    }
     mw[kk] = kk < wph ? ml.x : -INFINITY;
     lw[kk] = kk < wph ? ml.y : 0.f;
   }

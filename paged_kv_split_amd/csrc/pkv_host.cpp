@@ -117,8 +117,10 @@ int split_cap_keys(int rows) {
 // Workgroups per CU to aim at, measured on MI355X over the decode shapes:
 // one where a workgroup keeps enough K/V bytes in flight to cover memory
 // latency (VALU kernel: 8-16 KB tiles per wave; matrix-core kernel at
-// D = 128), two where it keeps fewer (matrix-core 16-key tiles of 2-4 KB at
-// D <= 64) or has a single register tile (matrix-core kernel at D = 256).
+// D = 128) or sits at the register limit (matrix-core kernel at D = 256:
+// 16 sequences x 1024 / 4096 / 8192 keys, 32 query heads, 2 splits against 4:
+// 31.6 / 93.3 / 176.0 against 32.6 / 96.3 / 181.3 us), two where it keeps
+// fewer (matrix-core 16-key tiles of 2-4 KB at D <= 64).
 // The prefill-shaped kernel: one, its 128-row workgroups being compute-heavy
 // (4 x 64 tokens over 2048 keys: 4 splits 52 us, 8 splits 68 us; 8 x 32 over
 // 8192: 109 against 123 us).
@@ -128,7 +130,7 @@ int blocks_per_cu(const pkv_problem *p, int hpb) {
   switch (pkv::kernel_kind(R, p->head_dim, hpb)) {
     case pkv::kKernelPrefill: return 1;
     case pkv::kKernelGroup: return 2;
-    case pkv::kKernelMfma: return p->head_dim == 128 ? 1 : 2;
+    case pkv::kKernelMfma: return p->head_dim >= 128 ? 1 : 2;
     default: return 1;
   }
 }

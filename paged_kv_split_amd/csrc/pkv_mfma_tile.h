@@ -66,9 +66,28 @@ struct MLay {
   // merge phase, per 16-row block: per-wave O rows and (m, l)
   static constexpr int MERGE_BYTES = NW * 16 * OB_STRIDE * 4 + NW * 16 * 2 * 4;
   static constexpr int MAIN_BYTES = BT_BYTES + NW * WAVE_LDS;
-  // swizzles (16-byte chunk index within a row)
-  __device__ static int swk(int ch, int row) { return ch ^ (row & (NCH - 1)); }
-  __device__ static int swv(int ch, int row) { return ch ^ ((2 * row) & (NCH - 2)); }
+  // swizzles (16-byte chunk index within a row).  K: row r's chunks XOR
+  // r mod NCH (at D = 32: (r >> 1) mod NCH), so that the eight lanes of one LDS pass of a
+  // key-major read (rows 8i .. 8i + 7, one chunk each) hit distinct banks
+  // (at D = 32 four chunks per row make a plain XOR with r repeat every four
+  // rows, which 128-byte passes cover twice).  V: the
+  // transposing read gives each lane 8 bytes of one row; four lanes cover one
+  // 32-byte segment of a row, and one pass serves 8 rows.  Segment s of row r
+  // moves to s XOR ((r >> SSH) mod NSEG), SSH chosen so that those 8 rows
+  // land on 8 distinct 32-byte bank groups (the pass covers 256 bytes of
+  // banks): measured on MI355X at D = 64, an XOR with r mod 4 left rows r and
+  // r + 4 on the same banks (12% of LDS cycles in bank conflicts).
+  static constexpr int NSEG = NCH / 2;  // 32-byte segments per row
+  static constexpr int SSH = NSEG >= 8 ? 0 : (NSEG == 4 ? 1 : 2);
+  // (written as before the D <= 64 forms were added where those reduce to the
+  // plain XOR: at D = 256 the kernels sit at the register limit, and
+  // equivalent but differently written indices spilled twice as much)
+  __device__ static int swk(int ch, int row) {
+    return NCH >= 8 ? ch ^ (row & (NCH - 1)) : ch ^ ((row >> 1) & (NCH - 1));
+  }
+  __device__ static int swv(int ch, int row) {
+    return NSEG >= 8 ? ch ^ ((2 * row) & (NCH - 2)) : ch ^ (2 * ((row >> SSH) & (NSEG - 1)));
+  }
 };
 
 template <int D, int NRB, bool MASK>

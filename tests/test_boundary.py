@@ -161,14 +161,14 @@ def test_split_heuristic_shapes():
     mha = base_problem(batch=4, num_q_heads=8, num_kv_heads=8, head_dim=64, page_size=64,
                        max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
     assert plan_of(mha) == (8, 1)
-    # matrix-core rows (G=8) at D=64: two workgroups per CU, two heads each; at D=128: one workgroup
-    # per CU; at D=32 and 256 one head per workgroup
+    # matrix-core rows (G=8) at D=64: two workgroups per CU, two heads each; at D=128 and 256: one
+    # workgroup per CU (D=256: one head each, two splits); at D=32 one head per workgroup
     mf = {d: base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
                           max_kv_len=4096, num_pages=2048) for d in (32, 64, 128, 256)}
     assert plan_of(mf[32]) == (4, 1)
     assert plan_of(mf[64]) == (8, 2)
     assert plan_of(mf[128]) == (4, 2)
-    assert plan_of(mf[256]) == (4, 1)
+    assert plan_of(mf[256]) == (2, 1)
     # B=8 decode (1B model): grouping would need 16+ splits -> one head per workgroup
     d1b = base_problem(batch=8, num_q_heads=24, num_kv_heads=4, head_dim=64, max_pages_per_seq=64,
                        max_kv_len=2048, num_pages=512)
