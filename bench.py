@@ -359,10 +359,12 @@ class Bench:
         warm_ms = timed(self.step, rotate=False)
 
         def graph_ms(fn):
-            """ms per launch when one call per replica (up to 64) is captured
-            into a hipGraph and the graph is replayed back to back, bracketed
-            by two events on the stream the replays run on."""
-            nrep_g = min(n_rep, 64)
+            """ms per launch when calls cycling over the replicas (one per
+            replica, up to 64, and at least 16 so that a replay's own launch
+            gap is spread over many calls) are captured into a hipGraph and the
+            graph is replayed back to back, bracketed by two events on the
+            stream the replays run on."""
+            nrep_g = max(min(n_rep, 64), 16)
             gs = torch.cuda.Stream()
             gs.wait_stream(torch.cuda.current_stream())
             g = torch.cuda.CUDAGraph()
@@ -372,7 +374,7 @@ class Bench:
                     self.sh = int(gs.cuda_stream)     # the raw calls launch on the capture stream
                     with torch.cuda.graph(g, stream=gs):
                         for r in range(nrep_g):
-                            fn(r)
+                            fn(r % n_rep)
             finally:
                 self.sh = saved
             torch.cuda.current_stream().wait_stream(gs)

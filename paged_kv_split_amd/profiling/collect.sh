@@ -13,7 +13,12 @@ export TMPDIR=/tmp
 out=$1
 shift
 mkdir -p "$out"
-BENCH="python3 -u bench.py --warmup 3 --runs 1 --no-cpu-baseline --no-configs"
+# the kernel trace times each workload as bench.py does by default (20
+# warmup calls, then timed runs of 200); the counter passes need only a few
+# calls each
+BENCH="python3 -u bench.py --no-cpu-baseline --no-configs"
+TRACE="--warmup 20 --steps 200 --runs 2"
+COUNT="--warmup 3 --steps 4 --runs 1"
 
 step() {  # step TAG LIMIT_SECONDS COMMAND...
   local tag=$1 lim=$2
@@ -44,16 +49,16 @@ for key in "$@"; do
   wl=$tag
   name=${key%%:*}
   step "${wl}_trace" 300 rocprofv3 --kernel-trace --stats -d "$out/${wl}_trace" -o trace --output-format csv -- \
-    $BW --workload "$name" --steps 20
+    $BW --workload "$name" $TRACE
   step "${wl}_fetch" 120 rocprofv3 --pmc FETCH_SIZE -d "$out/${wl}_fetch" -o fetch --output-format csv -- \
-    $BW --workload "$name" --steps 4
+    $BW --workload "$name" $COUNT
   step "${wl}_write" 120 rocprofv3 --pmc WRITE_SIZE -d "$out/${wl}_write" -o write --output-format csv -- \
-    $BW --workload "$name" --steps 4
+    $BW --workload "$name" $COUNT
   step "${wl}_sq" 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT \
     SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE MfmaUtil -d "$out/${wl}_sq" -o sq --output-format csv -- \
-    $BW --workload "$name" --steps 4
+    $BW --workload "$name" $COUNT
   step "${wl}_issue" 120 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 \
     SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE \
-    -d "$out/${wl}_issue" -o issue --output-format csv -- $BW --workload "$name" --steps 4
+    -d "$out/${wl}_issue" -o issue --output-format csv -- $BW --workload "$name" $COUNT
 done
 echo "collected in $out" >&2
