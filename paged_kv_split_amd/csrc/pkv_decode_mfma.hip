@@ -534,8 +534,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (MASK && D == 128) ? 1 : 2) vo
         } else if (W > 0.f) {
           float *po = a.o_part + (row * a.S + s) * D + d0;
           if (a.fused) {  // merged by another workgroup of this launch
-            store_dev2(po, v[0], v[1]);
-            store_dev2(po + 2, v[2], v[3]);
+            store_part4(a, po, v[0], v[1], v[2], v[3]);
           } else {
             *reinterpret_cast<float4 *>(po) = make_float4(v[0], v[1], v[2], v[3]);
           }

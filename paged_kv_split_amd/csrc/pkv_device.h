@@ -106,6 +106,29 @@ __device__ __forceinline__ void store_dev2(float *p, float x, float y) {  // p 8
   const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t *>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Four floats of a partial that another workgroup of the running launch
+// reads (the in-kernel merge), p 16-byte aligned inside a.o_part.  With
+// a.wide_part (a workspace under 2^31 bytes, so byte offsets fit 32 bits) one
+// 16-byte raw buffer store with the sc1 cache policy -- written through to the
+// device-coherent level, as the agent-scope atomic stores of store_dev2 are --
+// over a resource that spans the workspace; otherwise two 8-byte agent-scope
+// atomic stores.  Measured on MI355X (B = 256 ragged batch): each 8-byte
+// write-through store cost a 32-byte memory write, 106 MB of writes per call
+// for 39 MB of partials and outputs.
+constexpr int kCpolSc1 = 16;               // cache-policy operand of the buffer builtins: sc1
+constexpr int kRawBufferDword3 = 0x00020000;  // buffer resource word 3 for untyped (raw) access
+__device__ __forceinline__ void store_part4(const DecodeArgs &a, float *p, float x, float y, float z, float w) {
+  if (a.wide_part) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(a.o_part, 0, 0x7fffffff, kRawBufferDword3);
+    typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+    const i32x4_t v = {__float_as_int(x), __float_as_int(y), __float_as_int(z), __float_as_int(w)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)((p - a.o_part) * 4), 0, kCpolSc1);
+  } else {
+    store_dev2(p, x, y);
+    store_dev2(p + 2, z, w);
+  }
+}
+
 template <bool DEV>
 __device__ __forceinline__ float2 load2(const float *p) {  // p 8-byte aligned
   if constexpr (DEV) {
@@ -699,8 +722,8 @@ __device__ void write_rows(const DecodeArgs &a, int s, bool direct, const int64_
       const float mx = W > 0.f ? M * kLn2 : -INFINITY;
       if (a.fused) {  // merged by another workgroup of this launch
         if (W > 0.f) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) store_dev2(po + e, v[e], v[e + 1]);
+          store_part4(a, po, v[0], v[1], v[2], v[3]);
+          store_part4(a, po + 4, v[4], v[5], v[6], v[7]);
         }
         if (d == 0) store_dev2(pm, mx, W);
       } else {        // read after this kernel has ended

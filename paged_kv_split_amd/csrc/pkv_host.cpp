@@ -540,6 +540,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->inner = (int32_t)inner;
   a->partials = (S > 1 || partials_only) ? 1 : 0;
   a->fused = split_ws && pl.fused ? 1 : 0;
+  a->wide_part = a->o_part && o_part_bytes <= (size_t)INT32_MAX ? 1 : 0;
   a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
   // longest first where every split past a sequence's keys is trimmed
   a->lpt = exact && (a->fused || S == 1) ? 1 : 0;

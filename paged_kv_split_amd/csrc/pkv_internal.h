@@ -44,6 +44,7 @@ struct DecodeArgs {
   int32_t rp;                     // packed rows per row block (a power of two)
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
+  int32_t wide_part;              // 1: o_part under 2^31 bytes (16-byte partial stores, store_part4)
   int32_t *counters;              // [units] arrival counters (fused), zero between calls
   int64_t rows;                   // output rows: tokens * Hq
 };
