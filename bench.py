@@ -270,8 +270,15 @@ class Bench:
                                           mask_stride_b=msb, mask_stride_q=msq, heads_per_block=heads_per_block)
         self.plan = plan = pkv.plan_varlen(prob, w.total_tokens) if varlen else pkv.plan(prob)
         self.S = S = plan.splits
-        prob.num_splits = S
-        prob.heads_per_block = plan.heads_per_block
+        if not plan.paired_heads:
+            # lock the reported plan in (the contiguous layouts then run the paged plan's
+            # splits and grouping)
+            prob.num_splits = S
+            prob.heads_per_block = plan.heads_per_block
+        # a paired plan stays automatic (as given on the command line), so every call runs the
+        # plan reported here: a forced grouping is never paired, and forcing the split count
+        # alone may change the grouping the heuristic picks; the [B, Hkv, L, D] layout runs
+        # the same split count unpaired
         self.prob = prob
         self.out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
         self.o_part, self.ml_part = pkv.alloc_workspace(prob, S, dev)     # ml_part zeroed (counter head)

@@ -137,6 +137,20 @@ typedef struct pkv_plan_info {
   int32_t merge_in_kernel;  /* 1: the split kernel merges the splits itself */
   int32_t kernels;          /* kernel launches per pkv_paged_decode call (0 when batch == 0) */
   int32_t kernel;           /* the split kernel: PKV_KERNEL_* below */
+  int32_t paired_heads;     /* 1: head pairing.  At head_dim 32 (an even number of kv heads,
+                               at most 8 packed rows per kv head, heads_per_block 0, paged
+                               or [B, L, Hkv, D] K/V) kv heads 2g and 2g + 1, adjacent in
+                               every key row, are read as one head of 64 columns, so each
+                               load fetches whole 128-byte lines; a row's q fills its own
+                               head's half (zero in the other) and its output is that half.
+                               heads_per_block then counts kv heads (two per pair),
+                               rows_per_block and units those of the paired launch (2 * G
+                               query heads per pair).  Results stay within the same bounds;
+                               their bits differ from an unpaired plan's.  Forced groupings
+                               are never paired; pkv_contiguous_decode in the [B, Hkv, L, D]
+                               layout (whose head slices are not adjacent) runs the same
+                               split count unpaired, one kv head per workgroup, so the split
+                               count and workspace of a problem never depend on its layout. */
 } pkv_plan_info;
 
 /* pkv_plan_info.kernel: the vector kernel (1 or 2 rows per kv head); the

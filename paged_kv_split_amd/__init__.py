@@ -85,6 +85,7 @@ class PlanInfo(ctypes.Structure):
         ("merge_in_kernel", ctypes.c_int32),
         ("kernels", ctypes.c_int32),
         ("kernel", ctypes.c_int32),
+        ("paired_heads", ctypes.c_int32),
     ]
 
 

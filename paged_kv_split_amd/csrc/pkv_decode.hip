@@ -427,10 +427,13 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, const Ctx<D, RP> 
   }
 }
 
-template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE>
+// PAIR: head pairing (pair_half), two kv heads of D/2 columns per head of the
+// launch; q, the output and the partials have DO = D/2 columns.
+template <int D, int RP, bool CAUSAL, bool MASK, bool UPAGE, bool PAIR = false>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const DecodeArgs a) {
   using Lay = Layout<D, RP>;
   constexpr int NW = Lay::NW, LPK = Lay::LPK, T = Lay::T, LPV = Lay::LPV;
+  constexpr int DO = PAIR ? D / 2 : D;
   __shared__ __attribute__((aligned(16))) float smem[Lay::SMEM];
   // output row of packed row r of head slot hh of the block, at r * hpb + hh
   __shared__ int64_t rowtab[RP * kMaxHeadsPerBlock];
@@ -465,9 +468,18 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
     for (int r = 0; r < RP; ++r) {
       const int rr = r0 + r;
       if (rr < sr0.R) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * D);
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * DO);
+        if constexpr (PAIR) {  // the row's D/2 columns in its half (chunks h * D/16 ..), zeros in the other
+          const int h = pair_half(a, rr);
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int ch = c.qq + LPK * c4;
+            qrows.v[r][c4] = ch / (D / 16) == h ? src[ch % (D / 16)] : make_uint4(0u, 0u, 0u, 0u);
+          }
+        } else {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = src[c.qq + LPK * c4];
+        }
       } else {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) qrows.v[r][c4] = make_uint4(0u, 0u, 0u, 0u);
@@ -592,10 +604,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void split_decode_valu(const D
   }
   __syncthreads();
   auto item = [&](int ri, int d, float &M, float &W, float (&v)[8]) {
-    merge_waves<NW, D>(mlb, ob, HR, wph, ri, d, M, W, v);
+    // paired: output column d of the row is column d of its half
+    const int dd = PAIR ? d + DO * pair_half(a, r0 + (ri >> a.lhpb)) : d;
+    merge_waves<NW, D>(mlb, ob, HR, wph, ri, dd, M, W, v);
   };
-  write_rows<D>(a, s, direct, rowtab, nrows, item, NW * 64);
-  if (a.fused && !direct) fused_tail<D>(a, wk0.unit, nact, rowtab, nrows, smem, NW * 64);
+  write_rows<DO>(a, s, direct, rowtab, nrows, item, NW * 64);
+  if (a.fused && !direct) fused_tail<DO>(a, wk0.unit, nact, rowtab, nrows, smem, NW * 64);
 }
 
 // Combine (the standalone pkv_combine entry point): each block merges
@@ -619,25 +633,25 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-template <int D, int RP, bool C, bool M, bool U>
+template <int D, int RP, bool C, bool M, bool U, bool PAIR>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
   const int64_t grid = split_grid(a);
-  hipLaunchKernelGGL((split_decode_valu<D, RP, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
+  hipLaunchKernelGGL((split_decode_valu<D, RP, C, M, U, PAIR>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D, int RP, bool C, bool M>
+template <int D, int RP, bool C, bool M, bool PAIR = false>
 hipError_t launch_u(const DecodeArgs &a, hipStream_t s) {
   // the page of a whole tile is wave-uniform when a page holds at least a tile
   constexpr int T = Layout<D, RP>::T;
-  return a.page_shift >= ilog2c(T) ? launch_t<D, RP, C, M, true>(a, s) : launch_t<D, RP, C, M, false>(a, s);
+  return a.page_shift >= ilog2c(T) ? launch_t<D, RP, C, M, true, PAIR>(a, s) : launch_t<D, RP, C, M, false, PAIR>(a, s);
 }
 
-template <int D, int RP>
+template <int D, int RP, bool PAIR = false>
 hipError_t launch_rp(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
-  if (causal) return mask ? launch_u<D, RP, true, true>(a, s) : launch_u<D, RP, true, false>(a, s);
-  return mask ? launch_u<D, RP, false, true>(a, s) : launch_u<D, RP, false, false>(a, s);
+  if (causal) return mask ? launch_u<D, RP, true, true, PAIR>(a, s) : launch_u<D, RP, true, false, PAIR>(a, s);
+  return mask ? launch_u<D, RP, false, true, PAIR>(a, s) : launch_u<D, RP, false, false, PAIR>(a, s);
 }
 
 template <int D>
@@ -654,7 +668,9 @@ int launch_split(const DecodeArgs &a, int head_dim, int rp, bool causal, bool ha
                  hipStream_t stream) {
   switch (head_dim) {
     case 32: return launch_d<32>(a, rp, causal, has_mask, stream);
-    case 64: return launch_d<64>(a, rp, causal, has_mask, stream);
+    case 64:  // head pairing: two rows of 64 columns (one query head of each of two kv heads of 32)
+      if (a.pair) return rp == 2 ? launch_rp<64, 2, true>(a, causal, has_mask, stream) : hipErrorInvalidValue;
+      return launch_d<64>(a, rp, causal, has_mask, stream);
     case 128: return launch_d<128>(a, rp, causal, has_mask, stream);
     default: return launch_d<256>(a, rp, causal, has_mask, stream);
   }

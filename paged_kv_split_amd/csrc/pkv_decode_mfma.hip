@@ -140,11 +140,14 @@ __device__ __forceinline__ void mtile_loop(const DecodeArgs &a, const MCtx &c, i
 template <int D, int NRB, bool MASK>
 constexpr int mfma_min_blocks() { return (NRB == 2 && (D >= 256 || (D == 128 && MASK))) ? 1 : 2; }
 
-template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE>
+// PAIR: head pairing (pair_half), two kv heads of D/2 columns per head of the
+// launch; q, the output and the partials have DO = D/2 columns.
+template <int D, int NRB, bool CAUSAL, bool MASK, bool UPAGE, bool PAIR = false>
 __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>())) void split_decode_mfma(
     const DecodeArgs a) {
   using L = MLay<D>;
   constexpr int NW = L::NW;
+  constexpr int DO = PAIR ? D / 2 : D;
   constexpr int RW = 16 * NRB;
   // the merge of the waves takes both row blocks at once (one LDS hand-over)
   constexpr int SMEM = L::MAIN_BYTES > NRB * L::MERGE_BYTES ? L::MAIN_BYTES : NRB * L::MERGE_BYTES;
@@ -181,9 +184,16 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
     for (int rb = 0; rb < NRB; ++rb) {
       const int rr = r0 + cc + 16 * rb;
       if (rr < sr0.R) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * D);
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + out_row(a, sr0.tok0, g, rr) * DO);
+        if constexpr (PAIR) {  // the row's D/2 columns in its half (steps h * D/64 ..), zeros in the other
+          const int h = pair_half(a, rr);
 #pragma unroll
-        for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
+          for (int stp = 0; stp < D / 32; ++stp)
+            qb[rb][stp] = (stp / (D / 64)) == h ? src[4 * (stp % (D / 64)) + q] : make_uint4(0u, 0u, 0u, 0u);
+        } else {
+#pragma unroll
+          for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = src[4 * stp + q];
+        }
       } else {
 #pragma unroll
         for (int stp = 0; stp < D / 32; ++stp) qb[rb][stp] = make_uint4(0u, 0u, 0u, 0u);
@@ -302,12 +312,14 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (mfma_min_blocks<D, NRB, MASK>
   auto item = [&](int ri, int d, float &M, float &W, float (&v)[8]) {
     const int rb = NRB == 1 ? 0 : ri / HR;
     const int rl = ri - rb * HR;   // (16 rb + cc) * hpb + hw - rb * HR = cc * hpb + hw
+    // paired: output column d of the row is column d of its half
+    const int dd = PAIR ? d + DO * pair_half(a, r0 + 16 * rb + (rl >> a.lhpb)) : d;
     merge_waves<NW, L::OB_STRIDE, OBSW>(mlb + rb * NW * 16 * 2, ob + rb * OBN, HR, wph,
-                                        16 * (rl & (a.hpb - 1)) + (rl >> a.lhpb), d, M, W, v);
+                                        16 * (rl & (a.hpb - 1)) + (rl >> a.lhpb), dd, M, W, v);
   };
-  write_rows<D>(a, s, direct, rowtab, nrt, item, NW * 64);
+  write_rows<DO>(a, s, direct, rowtab, nrt, item, NW * 64);
   if (a.fused && !direct)
-    fused_tail<D>(a, wk0.unit, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
+    fused_tail<DO>(a, wk0.unit, nact, rowtab, nrt, reinterpret_cast<float *>(smem_raw), NW * 64);
 }
 
 // ---- prefill-shaped workgroup ----------------------------------------------
@@ -572,24 +584,24 @@ hipError_t plaunch_d(const DecodeArgs &a, bool causal, bool mask, hipStream_t s)
   return mask ? plaunch_u<D, false, true>(a, s) : plaunch_u<D, false, false>(a, s);
 }
 
-template <int D, int NRB, bool C, bool M, bool U>
+template <int D, int NRB, bool C, bool M, bool U, bool PAIR>
 hipError_t mlaunch_t(const DecodeArgs &a, hipStream_t stream) {
   const int64_t grid = split_grid(a);
-  hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M, U>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((split_decode_mfma<D, NRB, C, M, U, PAIR>), dim3((unsigned)grid), dim3(kWavesPerBlock * 64),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int NRB, bool C, bool M>
+template <int D, int NRB, bool C, bool M, bool PAIR = false>
 hipError_t mlaunch_u(const DecodeArgs &a, hipStream_t s) {
   // a 16-key tile's page is wave-uniform when pages hold at least 16 keys
-  return a.page_shift >= 4 ? mlaunch_t<D, NRB, C, M, true>(a, s) : mlaunch_t<D, NRB, C, M, false>(a, s);
+  return a.page_shift >= 4 ? mlaunch_t<D, NRB, C, M, true, PAIR>(a, s) : mlaunch_t<D, NRB, C, M, false, PAIR>(a, s);
 }
 
-template <int D, int NRB>
+template <int D, int NRB, bool PAIR = false>
 hipError_t mlaunch_nrb(const DecodeArgs &a, bool causal, bool mask, hipStream_t s) {
-  if (causal) return mask ? mlaunch_u<D, NRB, true, true>(a, s) : mlaunch_u<D, NRB, true, false>(a, s);
-  return mask ? mlaunch_u<D, NRB, false, true>(a, s) : mlaunch_u<D, NRB, false, false>(a, s);
+  if (causal) return mask ? mlaunch_u<D, NRB, true, true, PAIR>(a, s) : mlaunch_u<D, NRB, true, false, PAIR>(a, s);
+  return mask ? mlaunch_u<D, NRB, false, true, PAIR>(a, s) : mlaunch_u<D, NRB, false, false, PAIR>(a, s);
 }
 
 template <int D>
@@ -611,7 +623,9 @@ int launch_split_mfma(const DecodeArgs &a, int head_dim, int nrb16, bool causal,
                       hipStream_t stream) {
   switch (head_dim) {
     case 32: return mlaunch_d<32>(a, nrb16, causal, has_mask, stream);
-    case 64: return mlaunch_d<64>(a, nrb16, causal, has_mask, stream);
+    case 64:  // head pairing: one 16-row block of 64 columns (two kv heads of 32)
+      if (a.pair) return nrb16 == 1 ? mlaunch_nrb<64, 1, true>(a, causal, has_mask, stream) : hipErrorInvalidValue;
+      return mlaunch_d<64>(a, nrb16, causal, has_mask, stream);
     case 128: return mlaunch_d<128>(a, nrb16, causal, has_mask, stream);
     default: return mlaunch_d<256>(a, nrb16, causal, has_mask, stream);
   }

@@ -550,6 +550,17 @@ __device__ __forceinline__ int64_t out_row(const DecodeArgs &a, int64_t tok0, in
   return (tok0 + i) * a.Hq + h;
 }
 
+// Head pairing (a.pair): kv heads 2g and 2g + 1 of D/2 columns each, adjacent
+// in every key row, are read as one head g of D columns, and its G = 2 G'
+// packed rows per token are the query heads of both.  Packed row rr belongs
+// to the second of the two (its q fills columns D/2 .. D-1, zeros elsewhere,
+// and its output is those columns) when its query head is among the last G'
+// of the group.  Its scores are those of its own head, since the other half
+// of q is zero.
+__device__ __forceinline__ int pair_half(const DecodeArgs &a, int rr) {
+  return (rr - (rr / a.G) * a.G) >= (a.G >> 1) ? 1 : 0;
+}
+
 // ---- log-sum-exp merge of split partials -----------------------------------
 // For each of `nrows` rows (row index rowf(r); partials of a row S apart) and
 // each 4-element group of its D outputs, one thread walks the first nsp <= S

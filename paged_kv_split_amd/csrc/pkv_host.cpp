@@ -306,6 +306,54 @@ Plan make_plan(const pkv_problem *p, int cus, int64_t tokens = -1) {
   return pl;
 }
 
+// Head pairing.  At head_dim 32 one kv head's slice of a key row is 64
+// bytes, half of a 128-byte cache line whose other half is the next head's;
+// requests for half lines leave memory concurrency unused (the L2 held about
+// half the reads in flight that it holds at head_dim 64 and up).  Two
+// adjacent kv heads 2g, 2g + 1 are then read as one head g of 64 columns --
+// in the paged and [B, L, Hkv, D] layouts their slices are adjacent in every
+// key row (in [B, Hkv, L, D] they are not: that layout runs the paired
+// problem's split count, one kv head per workgroup, so that a problem's split
+// count and workspace do not depend on its layout) -- whose packed rows are
+// the query heads of both: a row's q fills
+// its own head's half and is zero in the other, so its scores are those of
+// its own head, and its output is its half of the 64 columns.  The paired
+// problem (Hkv / 2 heads of 64 columns, 2G query heads per kv head) is planned
+// and launched like any other, on the vector kernel (one query head per kv
+// head: two rows) or the matrix-core kernel (up to 16 rows).  Measured on
+// MI355X, B = 16, 4096 keys, Hkv = 8, with 64-column heads standing in for the
+// pairs: 8 query heads 19.8 -> 17.9 us, 32 query heads 20.9 -> 18.2 us, 64
+// query heads 21.0 -> 18.9 us.  Not with forced kv heads per workgroup (they
+// count real heads).
+bool pair_eligible(const pkv_problem *p) {
+  if (p->head_dim != 32 || (p->num_kv_heads & 1) || p->heads_per_block != 0) return false;
+  const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
+  return 2 * R <= 16;
+}
+
+bool pair_heads(const pkv_problem *p, int layout) { return layout != PKV_KV_BHLD && pair_eligible(p); }
+
+pkv_problem paired_problem(const pkv_problem *p) {
+  pkv_problem v = *p;
+  v.head_dim = 2 * p->head_dim;
+  v.num_kv_heads = p->num_kv_heads / 2;
+  return v;
+}
+
+// The plan of a problem whose K/V sit in `layout` (0: paged): with head
+// pairing, that of the paired problem (its kv heads per workgroup count
+// pairs).
+Plan plan_of(const pkv_problem *p, int layout, int cus, int64_t tokens = -1) {
+  if (!pair_eligible(p)) return make_plan(p, cus, tokens);
+  const pkv_problem v = paired_problem(p);
+  const Plan pl = make_plan(&v, cus, tokens);
+  if (pair_heads(p, layout)) return pl;
+  pkv_problem u = *p;   // [B, Hkv, L, D]: the paired split count, one kv head per workgroup
+  u.num_splits = pl.S;
+  u.heads_per_block = 1;
+  return make_plan(&u, cus, tokens);
+}
+
 // ml_part bytes of pkv_paged_decode with S >= 2 splits: counter head + (m, l).
 size_t ml_bytes_split(const pkv_problem *p, int S) {
   const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
@@ -345,7 +393,7 @@ int pkv_num_splits(const pkv_problem *p, int num_cus, int *splits_out) {
     rc = query_cus(&num_cus);
     if (rc) return rc;
   }
-  *splits_out = make_plan(p, num_cus).S;
+  *splits_out = plan_of(p, 0, num_cus).S;
   return PKV_OK;
 }
 
@@ -360,12 +408,15 @@ int plan_query(const pkv_problem *p, int64_t tokens, int num_cus, pkv_plan_info 
     rc = query_cus(&num_cus);
     if (rc) return rc;
   }
-  const Plan pl = make_plan(p, num_cus, tokens);
+  const Plan pl = plan_of(p, 0, num_cus, tokens);
+  const bool pair = pair_heads(p, 0);
+  const pkv_problem pv = pair ? paired_problem(p) : *p;
   *info = pkv_plan_info{};
   info->splits = pl.S;
-  info->heads_per_block = pl.hpb;
-  info->rows_per_block = rows_per_block_of(p, pl.hpb);
-  info->kernel = kernel_of(p, pl.hpb);
+  info->heads_per_block = pair ? 2 * pl.hpb : pl.hpb;
+  info->rows_per_block = rows_per_block_of(&pv, pl.hpb);
+  info->kernel = kernel_of(&pv, pl.hpb);
+  info->paired_heads = pair ? 1 : 0;
   info->matrix_core = info->kernel == pkv::kKernelValu ? 0 : 1;
   info->units = pl.units;
   info->workgroups = pl.units * pl.S;
@@ -449,7 +500,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   if (S == 0) {
     const int rc = query_cus(&cus);
     if (rc) return rc;
-    S = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1).S;
+    S = plan_of(p, src.layout, cus, qs.cu_q ? qs.total_tokens : -1).S;
   }
   // pkv_paged_decode with several splits: ml_part = counter head + (m, l)
   const bool split_ws = S > 1 && !partials_only;
@@ -469,16 +520,19 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
       const int rc = query_cus(&cus);
       if (rc) return rc;
     }
-    pl = make_plan(p, cus, qs.cu_q ? qs.total_tokens : -1);
+    pl = plan_of(p, src.layout, cus, qs.cu_q ? qs.total_tokens : -1);
   }
   const int64_t tokens = qs.cu_q ? qs.total_tokens : -1;
   const bool exact = p->batch <= kExactMaxBatch && (tokens >= 0 || p->batch >= kLptMinBatch);
-  pl.units = grid_units(p, pl.hpb, tokens);
+  // the launch's problem: with head pairing, Hkv / 2 heads of 64 columns
+  const bool pair = pair_heads(p, src.layout);
+  const pkv_problem pv = pair ? paired_problem(p) : *p;
+  pl.units = grid_units(&pv, pl.hpb, tokens);
 
-  const int G = p->num_q_heads / p->num_kv_heads;
-  const int R = G * p->q_len;
-  const int rp = rows_per_block_of(p, pl.hpb);
-  const int T = pkv::tile_keys(p->head_dim);
+  const int G = pv.num_q_heads / pv.num_kv_heads;
+  const int R = G * pv.q_len;
+  const int rp = rows_per_block_of(&pv, pl.hpb);
+  const int T = pkv::tile_keys(pv.head_dim);
   const int64_t L = max_len_of(p);
   int64_t chunk = ceil_div(ceil_div(L, S), T) * T;
   if (chunk < T) chunk = T;
@@ -504,13 +558,13 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   if (paged) {
     a->page_stride = (int64_t)p->page_size * p->num_kv_heads * p->head_dim;
     a->row_stride = p->num_kv_heads * p->head_dim;
-    a->head_stride = p->head_dim;
+    a->head_stride = pv.head_dim;   // paired: head g of the launch starts at kv head 2g
     a->page_shift = ilog2(p->page_size);
     a->max_pages = p->max_pages_per_seq;
   } else {  // one page of 2^30 key slots per sequence, addressed with the cache's strides
     a->page_stride = src.capacity * p->num_kv_heads * p->head_dim;
     a->row_stride = src.layout == PKV_KV_BLHD ? p->num_kv_heads * p->head_dim : p->head_dim;
-    a->head_stride = src.layout == PKV_KV_BLHD ? (int64_t)p->head_dim : src.capacity * p->head_dim;
+    a->head_stride = src.layout == PKV_KV_BLHD ? (int64_t)pv.head_dim : src.capacity * p->head_dim;
     a->page_shift = 30;
     a->max_pages = 1;
     a->contig = 1;
@@ -518,7 +572,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->B = p->batch;
   a->q_len = p->q_len;
   a->Hq = p->num_q_heads;
-  a->Hkv = p->num_kv_heads;
+  a->Hkv = pv.num_kv_heads;
   a->G = G;
   a->R = R;
   a->S = S;
@@ -530,8 +584,8 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->scale_log2 = p->scale * 1.4426950408889634f;
   a->exact = exact ? 1 : 0;
   a->rp = rp;
-  const int64_t outer = (exact ? row_block_slots(p, tokens, pl.hpb) : (int64_t)p->batch) * S;
-  const int64_t inner = (int64_t)(p->num_kv_heads / pl.hpb) * (exact ? 1 : a->nrb);
+  const int64_t outer = (exact ? row_block_slots(&pv, tokens, pl.hpb) : (int64_t)p->batch) * S;
+  const int64_t inner = (int64_t)(pv.num_kv_heads / pl.hpb) * (exact ? 1 : a->nrb);
   if (outer > INT32_MAX / 8 || inner * ceil_div(outer, 8) * 8 > kMaxBlocks) return PKV_ERR_SHAPE;
   // the combine kernel's grid (several splits without the in-kernel merge)
   const int64_t rows_all = (int64_t)p->batch * p->q_len * p->num_q_heads;
@@ -541,6 +595,7 @@ int plan_decode(const pkv_problem *p, const void *q, const QSource &qs, const Kv
   a->partials = (S > 1 || partials_only) ? 1 : 0;
   a->fused = split_ws && pl.fused ? 1 : 0;
   a->wide_part = a->o_part && o_part_bytes <= (size_t)INT32_MAX ? 1 : 0;
+  a->pair = pair ? 1 : 0;
   a->counters = a->fused ? reinterpret_cast<int32_t *>(ml_part) : nullptr;
   // longest first where every split past a sequence's keys is trimmed
   a->lpt = exact && (a->fused || S == 1) ? 1 : 0;
@@ -552,12 +607,13 @@ int launch_plan(const pkv::DecodeArgs &a, const pkv_problem *p, hipStream_t stre
   (void)hipGetLastError();
   const int rows = a.rp;
   const bool mask = a.mask != nullptr;
+  const int hd = a.pair ? 2 * p->head_dim : p->head_dim;   // the launch's head width
   int err;
-  switch (pkv::kernel_kind(a.R, p->head_dim, a.hpb)) {
-    case pkv::kKernelPrefill: err = pkv::launch_split_prefill(a, p->head_dim, causal, mask, stream); break;
-    case pkv::kKernelGroup: err = pkv::launch_split_group(a, p->head_dim, rows / 16, causal, mask, stream); break;
-    case pkv::kKernelMfma: err = pkv::launch_split_mfma(a, p->head_dim, rows / 16, causal, mask, stream); break;
-    default: err = pkv::launch_split(a, p->head_dim, rows, causal, mask, stream); break;
+  switch (pkv::kernel_kind(a.R, hd, a.hpb)) {
+    case pkv::kKernelPrefill: err = pkv::launch_split_prefill(a, hd, causal, mask, stream); break;
+    case pkv::kKernelGroup: err = pkv::launch_split_group(a, hd, rows / 16, causal, mask, stream); break;
+    case pkv::kKernelMfma: err = pkv::launch_split_mfma(a, hd, rows / 16, causal, mask, stream); break;
+    default: err = pkv::launch_split(a, hd, rows, causal, mask, stream); break;
   }
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
@@ -614,7 +670,7 @@ int pkv_paged_decode_noalloc(const pkv_problem *p, const void *q, const void *k_
     int cus = 0;
     rc = query_cus(&cus);
     if (rc) return rc;
-    S = make_plan(p, cus).S;
+    S = plan_of(p, 0, cus).S;
   }
   // the static workspace: ml_part (counter head + (m, l)) first, then o_part
   size_t ob = 0, mb = 0, mb_al = 0;

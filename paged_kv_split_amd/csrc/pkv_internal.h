@@ -45,6 +45,9 @@ struct DecodeArgs {
   int32_t partials;               // 1: write o_part/ml_part even when S == 1
   int32_t fused;                  // 1: the last block of a unit merges the partials (S > 1)
   int32_t wide_part;              // 1: o_part under 2^31 bytes (16-byte partial stores, store_part4)
+  int32_t pair;                   // 1: head pairing -- kv heads 2g, 2g + 1 of 32 columns read as one
+                                  // head g of 64 (the fields above describe that problem: Hkv / 2
+                                  // heads, G = 2 * G_real); q, out and the partials keep 32 columns
   int32_t *counters;              // [units] arrival counters (fused), zero between calls
   int64_t rows;                   // output rows: tokens * Hq
 };

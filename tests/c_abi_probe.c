@@ -28,8 +28,9 @@ static pkv_problem decode_problem(void) {
 }
 
 static void print_plan(const char *tag, int rc, const pkv_plan_info *i) {
-  printf("%s %d %d %d %d %d %lld %lld %d %d %d\n", tag, rc, i->splits, i->heads_per_block, i->rows_per_block,
-         i->matrix_core, (long long)i->units, (long long)i->workgroups, i->merge_in_kernel, i->kernels, i->kernel);
+  printf("%s %d %d %d %d %d %lld %lld %d %d %d %d\n", tag, rc, i->splits, i->heads_per_block, i->rows_per_block,
+         i->matrix_core, (long long)i->units, (long long)i->workgroups, i->merge_in_kernel, i->kernels, i->kernel,
+         i->paired_heads);
 }
 
 #define FIELD(T, f) printf("offset " #T " " #f " %zu %zu\n", offsetof(T, f), sizeof(((T *)0)->f))
@@ -61,6 +62,7 @@ int main(void) {
   FIELD(pkv_plan_info, merge_in_kernel);
   FIELD(pkv_plan_info, kernels);
   FIELD(pkv_plan_info, kernel);
+  FIELD(pkv_plan_info, paired_heads);
   printf("const %d %d %d %d %d %d %d\n", PKV_MAX_SPLITS, PKV_CAUSAL_LAST, PKV_COUNTER_BYTES, PKV_MAX_FUSED_UNITS,
          PKV_KV_BLHD, PKV_KV_BHLD, PKV_MAX_CONTIGUOUS_KEYS);
   printf("kernels %d %d %d %d\n", PKV_KERNEL_VECTOR, PKV_KERNEL_MATRIX, PKV_KERNEL_SHARED_TILE, PKV_KERNEL_PREFILL);

@@ -45,6 +45,13 @@ def problem(w, num_splits=0, heads_per_block=0):
                             mask_stride_b=msb, mask_stride_q=msq, heads_per_block=heads_per_block)
 
 
+def paired(w, heads_per_block=0) -> bool:
+    """Whether the library's paged plan pairs kv heads (pkv_plan_info.paired_heads):
+    the [B, Hkv, L, D] contiguous layout never does, so its bits match the paged
+    call's only when this is False."""
+    return bool(pkv.plan(problem(w, heads_per_block=heads_per_block)).paired_heads)
+
+
 def run(w, d=None, num_splits=0, stream=None, sync=True, heads_per_block=0):
     """Call pkv_paged_decode; return (out_bf16 bits uint16, out_f32 float32) as numpy."""
     if d is None:

@@ -162,10 +162,14 @@ def test_split_heuristic_shapes():
                        max_pages_per_seq=512, max_kv_len=32768, num_pages=2048)
     assert plan_of(mha) == (8, 1)
     # matrix-core rows (G=8) at D=64: two workgroups per CU, two heads each; at D=128 and 256: one
-    # workgroup per CU (D=256: one head each, two splits); at D=32 one head per workgroup
+    # workgroup per CU (D=256: one head each, two splits); at D=32 head pairing: one pair (two kv
+    # heads read as one of 64 columns, 16 rows) per workgroup, planned as D=64 with Hkv=4
     mf = {d: base_problem(batch=16, num_q_heads=64, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
                           max_kv_len=4096, num_pages=2048) for d in (32, 64, 128, 256)}
-    assert plan_of(mf[32]) == (4, 1)
+    info = pkv.plan(mf[32], 256)
+    assert plan_of(mf[32]) == (8, 2) and info.paired_heads == 1
+    assert info.rows_per_block == 16 and info.kernel == pkv.PKV_KERNEL_MATRIX and info.units == 16 * 4
+    assert all(pkv.plan(mf[d], 256).paired_heads == 0 for d in (64, 128, 256))
     assert plan_of(mf[64]) == (8, 2)
     assert plan_of(mf[128]) == (4, 2)
     assert plan_of(mf[256]) == (2, 1)
@@ -173,11 +177,14 @@ def test_split_heuristic_shapes():
     d1b = base_problem(batch=8, num_q_heads=24, num_kv_heads=4, head_dim=64, max_pages_per_seq=64,
                        max_kv_len=2048, num_pages=512)
     assert plan_of(d1b)[1] == 1
-    # VALU kernel, B=16, Hkv=8: four heads per workgroup and 8 splits at D <= 128, one head at 256
+    # VALU kernel, B=16, Hkv=8: four heads per workgroup and 8 splits at D <= 128, one head at 256;
+    # at D=32 two pairs per workgroup (the paired problem: two rows per head of 64 columns)
     for d, want in ((32, (8, 4)), (64, (8, 4)), (128, (8, 4)), (256, (2, 1))):
         v = base_problem(batch=16, num_q_heads=8, num_kv_heads=8, head_dim=d, max_pages_per_seq=128,
                          max_kv_len=4096, num_pages=2048)
         assert plan_of(v) == want, d
+        info = pkv.plan(v, 256)
+        assert info.paired_heads == (d == 32) and info.rows_per_block == (2 if d == 32 else 1)
     # more sequences: fewer splits; once the units fill the chip the splits hold at most
     # 1024 keys (one row per kv head)
     v64 = base_problem(batch=64, num_q_heads=8, num_kv_heads=8, head_dim=128, max_pages_per_seq=128,

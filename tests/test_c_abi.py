@@ -71,7 +71,7 @@ def _decode_problem(**kw):
 
 def _plan_tuple(pl):
     return [pl.splits, pl.heads_per_block, pl.rows_per_block, pl.matrix_core, pl.units, pl.workgroups,
-            pl.merge_in_kernel, pl.kernels, pl.kernel]
+            pl.merge_in_kernel, pl.kernels, pl.kernel, pl.paired_heads]
 
 
 def test_host_entry_points_answer_c_as_they_answer_python(probe):

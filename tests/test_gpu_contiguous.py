@@ -10,7 +10,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, note, run, run_contiguous, sub_batch  # noqa: E402
+from gpu_util import check, note, paired, run, run_contiguous, sub_batch  # noqa: E402
 from test_gpu_parity import SMALL  # noqa: E402
 
 
@@ -25,7 +25,9 @@ def compare_contiguous(w, layout, num_splits=0, heads_per_block=0, capacity=None
         sw = sub_batch(w, seqs)
         ref = oracle.decode_contiguous(sw, k[seqs], v[seqs], layout)
         check(o16[seqs], o32[seqs], ref, f"contiguous {layout} {w.name}")
-    if paged_too:
+    if paged_too and not (layout == "bhld" and paired(w, heads_per_block)):
+        # the same plan as the paged call, the same bits (head pairing, at D = 32, applies to the
+        # paged and blhd layouts only: bhld then runs another plan, checked against the oracle above)
         p16, p32 = run(w, num_splits=num_splits, heads_per_block=heads_per_block)
         assert np.array_equal(o16, p16)
         assert np.array_equal(o32.view(np.uint32), p32.view(np.uint32))

@@ -347,6 +347,9 @@ def _partials_then_combine(w, d, S):
     dict(B=2, q_len=2, Hq=16, Hkv=2, D=64, page_size=16, kv_lens=[900, 77], causal="last"),      # MFMA, R=16
     dict(B=2, q_len=1, Hq=48, Hkv=1, D=256, page_size=64, kv_lens=[700, 1000], mask="2d"),        # MFMA, R=48
     dict(B=2, q_len=160, Hq=32, Hkv=8, D=64, page_size=32, kv_lens=[800, 300], causal="last"),   # prefill, R=640
+    dict(B=3, q_len=1, Hq=8, Hkv=8, D=32, page_size=32, kv_lens=[1500, 0, 333]),                 # paired VALU
+    dict(B=2, q_len=2, Hq=32, Hkv=8, D=32, page_size=16, kv_lens=[900, 77], causal="last",
+         mask="2d"),                                                                              # paired MFMA
 ])
 @pytest.mark.parametrize("S", [2, 7, 64])
 def test_in_kernel_merge_equals_separate_combine(shape, S):
@@ -364,18 +367,21 @@ def test_in_kernel_merge_equals_separate_combine(shape, S):
     check(a16, a32, oracle.decode(w), "fused")
 
 
-def test_many_units_use_the_combine_kernel():
+@pytest.mark.parametrize("hpb", [1, 0])
+def test_many_units_use_the_combine_kernel(hpb):
     """More than PKV_MAX_FUSED_UNITS units with several splits: split kernel +
     combine kernel, with the (m, l) data after the counter head."""
-    B = pkv.PKV_MAX_FUSED_UNITS // 8 + 9
+    # matrix-core rows at D = 32: forced one kv head per workgroup, B * Hkv units; or head
+    # pairing (automatic grouping), two pairs of kv heads per workgroup at three splits, 2 B units
+    B = pkv.PKV_MAX_FUSED_UNITS // (8 if hpb else 2) + 9
     rng = np.random.default_rng(11)
     lens = rng.integers(0, 150, B)
-    # matrix-core rows at D = 32: one kv head per workgroup, B * Hkv units
     w = workloads.build("manyunits", B=B, q_len=1, Hq=64, Hkv=8, D=32, page_size=16,
                         kv_lens=lens, seed=3300)
-    info = pkv.plan(problem(w, num_splits=3))
+    info = pkv.plan(problem(w, num_splits=3, heads_per_block=hpb))
+    assert info.paired_heads == (hpb == 0)
     assert info.units > pkv.PKV_MAX_FUSED_UNITS and not info.merge_in_kernel and info.kernels == 2
-    out16, out32 = run(w, num_splits=3)
+    out16, out32 = run(w, num_splits=3, heads_per_block=hpb)
     seqs = [0, 1, int(np.argmax(lens)), B // 2, B - 1]
     ref = oracle.decode(sub_batch(w, seqs))
     check(out16[seqs], out32[seqs], ref, "manyunits")
@@ -387,7 +393,7 @@ def test_one_workspace_serves_calls_of_any_shape():
     counter head is zero after every call."""
     shapes = [
         dict(B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[800, 20, 0, 1400]),
-        dict(B=600, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 600),  # 4800 units
+        dict(B=2400, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 2400),  # 4800 units (paired)
         dict(B=2, q_len=3, Hq=16, Hkv=2, D=64, page_size=8, kv_lens=[300, 41], causal="last"),
         dict(B=1, q_len=1, Hq=8, Hkv=1, D=32, page_size=64, kv_lens=[5000]),
     ]
@@ -424,7 +430,7 @@ def test_both_merge_paths_are_exercised():
     PKV_MAX_FUSED_UNITS units, the combine kernel beyond."""
     shapes = [(dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 7),
               (dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=32, kv_lens=[1500, 0, 333]), 64),
-              (dict(B=600, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 600), 2)]
+              (dict(B=2400, q_len=1, Hq=64, Hkv=8, D=32, page_size=16, kv_lens=[70] * 2400), 2)]
     flags = [pkv.merges_in_kernel(problem(workloads.build("paths", seed=1, **kw), S), S) for kw, S in shapes]
     assert flags == [True, True, False]
 
@@ -440,6 +446,8 @@ FAR_CASES = [
                                                    kv_lens=[700, 33, 1500], seed=3101, mask="2d")),
     ("split_decode_mfma", lambda: workloads.build("far_mfma", B=3, q_len=1, Hq=32, Hkv=8, D=128, page_size=16,
                                                    kv_lens=[1200, 5, 640], seed=3102)),
+    ("split_decode_mfma", lambda: workloads.build("far_paired", B=3, q_len=1, Hq=32, Hkv=8, D=32, page_size=16,
+                                                   kv_lens=[1200, 5, 640], seed=3104, mask="2d")),   # head pairing
     ("split_prefill_mfma", lambda: workloads.build("far_prefill", B=2, q_len=128, Hq=16, Hkv=4, D=64, page_size=32,
                                                     kv_lens=[900, 300], seed=3103).replace(
                                                         causal_offset=workloads.CAUSAL_LAST)),

@@ -43,15 +43,23 @@ def _check_plan(p, pl):
         assert pl.heads_per_block == p.heads_per_block
     assert pl.rows_per_block in (1, 2, 16, 32, 128)
     rows = (p.num_q_heads // p.num_kv_heads) * p.q_len
+    hd, hpb = p.head_dim, pl.heads_per_block
+    # head pairing: only at D = 32, an even kv head count, automatic grouping and at most 8 rows
+    # per kv head; the launch is that of Hkv / 2 heads of 64 columns with twice the rows
+    assert pl.paired_heads == (p.head_dim == 32 and p.num_kv_heads % 2 == 0 and p.heads_per_block == 0
+                               and 2 * rows <= 16)
+    if pl.paired_heads:
+        assert hpb % 2 == 0
+        rows, hd, hpb = 2 * rows, 64, hpb // 2
     assert pl.matrix_core == (1 if pl.rows_per_block >= 16 else 0)
     if pl.rows_per_block == 128:
-        assert rows >= 128 and p.head_dim <= 128 and pl.heads_per_block == 1
+        assert rows >= 128 and hd <= 128 and hpb == 1
     # the kernel follows from the rows, head dim and grouping
     if pl.rows_per_block == 128:
         assert pl.kernel == pkv.PKV_KERNEL_PREFILL
-    elif pl.heads_per_block == 8 or (pl.heads_per_block == 4 and rows > 2 and p.head_dim <= 128):
+    elif hpb == 8 or (hpb == 4 and rows > 2 and hd <= 128):
         assert pl.kernel == pkv.PKV_KERNEL_SHARED_TILE and pl.rows_per_block in (16, 32)
-        assert pl.heads_per_block < 8 or p.head_dim <= 64
+        assert hpb < 8 or hd <= 64
     else:
         assert pl.kernel == (pkv.PKV_KERNEL_MATRIX if rows > 2 else pkv.PKV_KERNEL_VECTOR)
     assert pl.workgroups == pl.units * pl.splits
