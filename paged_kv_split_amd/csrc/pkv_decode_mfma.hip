@@ -516,9 +516,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, (MASK && D == 128) ? 1 : 2) vo
       for (int sub = 0; sub < P::SUB; sub += 2) {
         const int base = tb + KT * sub;
         if (base < wkmax)  // wave-uniform: some row of this wave sees a key of the subtile pair
-          mcompute2<D, NRB, CAUSAL, MASK>(a, c, base, mw + sub * P::MASK_SUB, mw + (sub + 1) * P::MASK_SUB, qb, lim,
-                                          ktile(buf, sub), vtile(buf, sub), ktile(buf, sub + 1),
-                                          vtile(buf, sub + 1), lane, st);
+          mcompute2<D, NRB, CAUSAL, MASK, true>(a, c, base, mw + sub * P::MASK_SUB, mw + (sub + 1) * P::MASK_SUB,
+                                                qb, lim, ktile(buf, sub), vtile(buf, sub), ktile(buf, sub + 1),
+                                                vtile(buf, sub + 1), lane, st);
       }
       mstore<D, NRB, false>(tr, ktile(buf ^ 1, w), vtile(buf ^ 1, w), nullptr, lane);
       if constexpr (MASK) pmask_store<NRB>(pm, mw, lane);
