@@ -146,10 +146,11 @@ def test_repeated_calls_are_deterministic():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
 
 
-def test_graph_capture_replay_matches_eager():
+@pytest.mark.parametrize("D", [128, 32])   # D = 32: a head-paired plan
+def test_graph_capture_replay_matches_eager(D):
     """Capture one call into a hipGraph with preallocated buffers, then replay
     after changing q and kv_lens in place; every replay must equal eager."""
-    w = workloads.build("graph", B=4, q_len=1, Hq=32, Hkv=8, D=128, page_size=32,
+    w = workloads.build("graph", B=4, q_len=1, Hq=32, Hkv=8, D=D, page_size=32,
                         kv_lens=[1500, 900, 64, 1000], seed=3080, mask="2d")
     d = dev_tensors(w)
     p = problem(w, num_splits=4)
