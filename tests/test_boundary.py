@@ -426,3 +426,37 @@ def test_noalloc_argument_checks():
     # one split needs no workspace: no limit applies
     big.num_splits = 1
     assert call_noalloc(big, q=0) == pkv.PKV_ERR_NULL
+
+
+def test_head_pairing_rule_and_workspace():
+    """Head pairing (pkv_plan_info.paired_heads): only at head_dim 32 with an even
+    kv head count, automatic grouping and at most 8 packed rows per kv head; the
+    paired plan's split count is what pkv_num_splits reports; the workspace keeps
+    the real 32 columns per output row."""
+    cases = [
+        (dict(head_dim=32, num_q_heads=8, num_kv_heads=8), True),                 # 1 row -> 2 paired rows
+        (dict(head_dim=32, num_q_heads=64, num_kv_heads=8), True),                # 8 rows -> 16
+        (dict(head_dim=32, num_q_heads=32, num_kv_heads=8, q_len=2), True),       # 8 rows
+        (dict(head_dim=32, num_q_heads=32, num_kv_heads=8, q_len=3), False),      # 12 rows
+        (dict(head_dim=32, num_q_heads=128, num_kv_heads=8), False),              # 16 rows
+        (dict(head_dim=32, num_q_heads=6, num_kv_heads=3), False),                # odd kv heads
+        (dict(head_dim=32, num_q_heads=8, num_kv_heads=8, heads_per_block=2), False),  # forced grouping
+        (dict(head_dim=64, num_q_heads=8, num_kv_heads=8), False),
+        (dict(head_dim=128, num_q_heads=32, num_kv_heads=8), False),
+    ]
+    for kw, want in cases:
+        p = base_problem(batch=16, max_pages_per_seq=128, max_kv_len=4096, num_pages=2048, **kw)
+        info = pkv.plan(p, 256)
+        assert info.paired_heads == want, kw
+        assert pkv.num_splits(p, 256) == info.splits
+        if want:
+            # heads_per_block counts real kv heads, two per pair; units count pairs
+            assert info.heads_per_block % 2 == 0
+            rows_per_pair = 2 * (kw["num_q_heads"] // kw["num_kv_heads"]) * kw.get("q_len", 1)
+            assert info.rows_per_block == (2 if rows_per_pair == 2 else 16)
+            assert info.units == 16 * (kw["num_kv_heads"] // info.heads_per_block)
+        S = max(info.splits, 2)
+        o, ml = pkv.workspace_bytes(p, S)
+        rows = 16 * kw.get("q_len", 1) * kw["num_q_heads"]
+        assert o == rows * S * kw["head_dim"] * 4
+        assert ml == pkv.PKV_COUNTER_BYTES + rows * S * 2 * 4
