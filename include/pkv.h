@@ -127,7 +127,8 @@ typedef struct pkv_plan_info {
   int32_t splits;           /* key splits per sequence */
   int32_t heads_per_block;  /* kv heads per split workgroup (1, 2, 4 or 8) */
   int32_t rows_per_block;   /* packed query rows (G * q_len) per kv head per workgroup:
-                               1 or 2 (vector kernel), 16 or 32 (matrix-core kernel),
+                               1 or 2 (vector kernel; 4 at head_dim 256 with 3 or 4
+                               rows), 16 or 32 (matrix-core kernel),
                                128 (prefill-shaped matrix-core kernel: from 128 rows on at
                                D <= 128 with one kv head per workgroup, four waves of 32
                                rows sharing each K/V tile) */
@@ -153,7 +154,8 @@ typedef struct pkv_plan_info {
                                count and workspace of a problem never depend on its layout. */
 } pkv_plan_info;
 
-/* pkv_plan_info.kernel: the vector kernel (1 or 2 rows per kv head); the
+/* pkv_plan_info.kernel: the vector kernel (1 or 2 rows per kv head, up to 4
+ * at head_dim 256); the
  * one-head matrix-core kernel (16 or 32 rows of one kv head per wave, each
  * wave its own key tiles); the shared-tile matrix-core kernel (a workgroup
  * of 4 or 8 kv heads whose waves share each K/V tile of the whole head group,

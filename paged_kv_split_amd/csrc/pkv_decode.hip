@@ -49,7 +49,7 @@ namespace pkv {
 int rows_per_block(int R, int head_dim, int hpb) {
   switch (kernel_kind(R, head_dim, hpb)) {
     case kKernelPrefill: return kPrefillRows;
-    case kKernelValu: return R <= 1 ? 1 : 2;
+    case kKernelValu: return R <= 1 ? 1 : R <= 2 ? 2 : 4;   // 4: head_dim 256 only (use_mfma)
     default: return R <= 16 ? 16 : 32;
   }
 }
@@ -656,6 +656,9 @@ hipError_t launch_rp(const DecodeArgs &a, bool causal, bool mask, hipStream_t s)
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, int rp, bool causal, bool mask, hipStream_t s) {
+  if constexpr (D == 256) {   // three or four rows per kv head (use_mfma)
+    if (rp == 4) return launch_rp<D, 4>(a, causal, mask, s);
+  }
   switch (rp) {
     case 1: return launch_rp<D, 1>(a, causal, mask, s);
     default: return launch_rp<D, 2>(a, causal, mask, s);

@@ -265,7 +265,7 @@ constexpr int64_t kMaxGroupedChunk = 2048;
 int max_heads_per_block(const pkv_problem *p) {
   const int R = (p->num_q_heads / p->num_kv_heads) * p->q_len;
   if (pkv::use_prefill(R, p->head_dim, 1)) return 1;
-  if (pkv::use_mfma(R)) return (p->head_dim == 64 || p->head_dim == 128) ? 2 : 1;
+  if (pkv::use_mfma(R, p->head_dim)) return (p->head_dim == 64 || p->head_dim == 128) ? 2 : 1;
   return p->head_dim <= 128 ? pkv::kMaxHeadsPerBlock : 1;
 }
 

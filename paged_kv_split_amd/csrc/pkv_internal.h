@@ -65,8 +65,15 @@ struct CombineArgs {
 // Up to 2 rows run on the VALU kernel (rows padded to RP in {1, 2}); from 3
 // rows on, the matrix-core kernel (16-row tiles, one or two per workgroup)
 // was measured as fast or faster on gfx950 even with most of a tile padded
-// (R = 3, 4, 6, 8), so it takes over there.
-inline bool use_mfma(int R) { return R > 2; }
+// (R = 3, 4, 6, 8), so it takes over there -- except at head_dim 256, where
+// the matrix-core kernel keeps one register tile per wave and one workgroup
+// per CU (more spill) and the VALU kernel (RP = 4) stays ahead up to 4 rows.
+// Measured on MI355X, Hkv = 8, bench protocol, matrix-core -> VALU: B = 16 x
+// 4096 keys with 32 query heads 93.8 -> 92.5 us, with 24 query heads
+// 93.5 -> 91.4 us, 16 query heads x 2 tokens 94.3 -> 92.1 us; B = 16 x 8192
+// keys 176.8 -> 172.2 us, x 1024 keys 31.5 -> 30.3 us (at 8 rows the VALU
+// kernel is slower everywhere).
+inline bool use_mfma(int R, int head_dim) { return head_dim == 256 ? R > 4 : R > 2; }
 // The prefill-shaped matrix-core kernel: four waves of 32 rows each share
 // every K/V tile (128 rows per workgroup), so a key is read once per 128 rows
 // rather than once per 32.  Taken at D <= 128 with one kv head per workgroup
@@ -94,9 +101,9 @@ enum { kKernelValu = 0, kKernelMfma = 1, kKernelGroup = 2, kKernelPrefill = 3 };
 inline int kernel_kind(int R, int head_dim, int hpb) {
   if (use_prefill(R, head_dim, hpb)) return kKernelPrefill;
   if (hpb == 8 || (hpb == 4 && R > 2 && head_dim <= 128)) return kKernelGroup;
-  return R > 2 ? kKernelMfma : kKernelValu;
+  return use_mfma(R, head_dim) ? kKernelMfma : kKernelValu;
 }
-// rows per workgroup and kv head: RP (vector kernel, 1 or 2), 16/32
+// rows per workgroup and kv head: RP (vector kernel, 1, 2 or 4), 16/32
 // (matrix-core kernels) or 128 (prefill-shaped)
 int rows_per_block(int R, int head_dim, int hpb);
 int tile_keys(int head_dim);       // keys per VALU wave tile T (a multiple of 16)

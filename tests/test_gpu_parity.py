@@ -88,6 +88,11 @@ SMALL = [
     dict(B=3, q_len=1, Hq=16, Hkv=8, D=32, page_size=16, kv_lens=[70, 513, 1]),                # R=2
     dict(B=2, q_len=2, Hq=4, Hkv=4, D=256, page_size=32, kv_lens=[300, 9], causal="last"),     # R=2
     dict(B=2, q_len=1, Hq=12, Hkv=4, D=64, page_size=64, kv_lens=[1000, 257], mask="2d"),      # R=3
+    # three and four rows per kv head at D = 256 (VALU kernel, four rows per workgroup)
+    dict(B=3, q_len=1, Hq=32, Hkv=8, D=256, page_size=32, kv_lens=[700, 1, 2049], mask="2d"),  # R=4
+    dict(B=2, q_len=3, Hq=2, Hkv=2, D=256, page_size=16, kv_lens=[300, 4], causal="last",
+         mask="3d"),                                                                           # R=3
+    dict(B=2, q_len=2, Hq=16, Hkv=8, D=256, page_size=1, kv_lens=[130, 77], causal=60),        # R=4
 ]
 
 

@@ -30,6 +30,8 @@ CASES = [
     ([4, 1, 12], [500, 100, 2000], dict(Hq=32, Hkv=8, D=128, page_size=32, causal=20)),
     ([16, 16, 1, 16], [4000, 16, 2500, 700], dict(Hq=8, Hkv=1, D=128, page_size=32, causal="lastv",
                                                    mask="2d", mask_p=0.3)),
+    ([2, 1, 0, 2], [900, 33, 5, 2], dict(Hq=16, Hkv=8, D=256, page_size=32, causal="lastv",
+                                         mask="3d")),                                  # VALU, 4 rows
 ]
 
 

@@ -41,7 +41,7 @@ def _check_plan(p, pl):
     assert pl.heads_per_block in (1, 2, 4, 8) and p.num_kv_heads % pl.heads_per_block == 0
     if p.heads_per_block:
         assert pl.heads_per_block == p.heads_per_block
-    assert pl.rows_per_block in (1, 2, 16, 32, 128)
+    assert pl.rows_per_block in (1, 2, 4, 16, 32, 128)
     rows = (p.num_q_heads // p.num_kv_heads) * p.q_len
     hd, hpb = p.head_dim, pl.heads_per_block
     # head pairing: only at D = 32, an even kv head count, automatic grouping and at most 8 rows
@@ -61,7 +61,11 @@ def _check_plan(p, pl):
         assert pl.kernel == pkv.PKV_KERNEL_SHARED_TILE and pl.rows_per_block in (16, 32)
         assert hpb < 8 or hd <= 64
     else:
-        assert pl.kernel == (pkv.PKV_KERNEL_MATRIX if rows > 2 else pkv.PKV_KERNEL_VECTOR)
+        # the vector kernel up to 2 rows, at head_dim 256 up to 4 (four rows per workgroup)
+        vector = rows <= 2 or (hd == 256 and rows <= 4)
+        assert pl.kernel == (pkv.PKV_KERNEL_VECTOR if vector else pkv.PKV_KERNEL_MATRIX)
+        if vector:
+            assert pl.rows_per_block == (1 if rows <= 1 else 2 if rows <= 2 else 4)
     assert pl.workgroups == pl.units * pl.splits
     assert pl.merge_in_kernel in (0, 1) and pl.kernels in (1, 2)
     if pl.merge_in_kernel:
